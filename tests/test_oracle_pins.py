@@ -1,0 +1,421 @@
+"""Pins of the fp64 oracle to facts fixed by the pages and by mathematics.
+
+None of these re-types the oracle's formula.  Each pins the oracle against
+something else: hand-worked examples (tests/golden), a scalar brute-force
+twin written separately (tests/brute_force.py), a library routine
+(torch's scaled_dot_product_attention on CPU fp64) for the special cases it
+covers, closed forms, and invariants the pages state (paged layout equals the
+contiguous one, GQA equals repeated KV heads, empty-tensor rules, the lse
+decomposition used by ring attention).
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import MASK_ALIBI, MASK_CAUSAL, MASK_NONE
+from tests.brute_force import brute_attention
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+TIGHT = 1e-12
+
+
+# ----------------------------------------------------------------- helpers
+
+def _val(x):
+    if x is None:
+        return math.nan
+    if isinstance(x, (int, float)):
+        return float(x)
+    x = x.strip()
+    if x == "inf":
+        return math.inf
+    if x.startswith("ln "):
+        arg = x[3:].strip()
+        return math.log(float(Fraction(arg)))
+    return float(Fraction(x))
+
+
+def _arr(nested):
+    if isinstance(nested, list):
+        return [_arr(v) for v in nested]
+    return _val(nested)
+
+
+def _random_case(rng, *, B, H, Hkv, D, bs, mask, int8=False, max_kv=12, allow_empty=True):
+    q_lens, kv_lens = [], []
+    for _ in range(B):
+        kv = int(rng.integers(0 if allow_empty else 1, max_kv + 1))
+        if mask == "decode":
+            ql = 1
+        else:
+            ql = int(rng.integers(0, 4))
+        q_lens.append(ql)
+        kv_lens.append(kv)
+    need = [-(-k // bs) for k in kv_lens]
+    nb = sum(need) + 2
+    perm = rng.permutation(nb)
+    width = max(need + [1]) + 1
+    table = np.full((B, width), -1, dtype=np.int64)
+    pos = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[pos:pos + need[b]]
+        pos += need[b]
+    T = sum(q_lens)
+    q = rng.standard_normal((T, H, D))
+    if int8:
+        k = rng.integers(-127, 128, size=(nb, bs, Hkv, D)).astype(np.float64)
+        v = rng.integers(-127, 128, size=(nb, bs, Hkv, D)).astype(np.float64)
+        ks = rng.uniform(0.005, 0.02, size=(Hkv, D))
+        vs = rng.uniform(0.005, 0.02, size=(Hkv, D))
+    else:
+        k = rng.standard_normal((nb, bs, Hkv, D))
+        v = rng.standard_normal((nb, bs, Hkv, D))
+        ks = vs = None
+    slopes = rng.uniform(0.0, 1.0, size=H)
+    return dict(q=q, k=k, v=v, table=table, q_lens=q_lens, kv_lens=kv_lens,
+                slopes=slopes, ks=ks, vs=vs)
+
+
+def _oracle(c, mask_type, H, Hkv, scale):
+    return oracle.paged_attention(
+        c["q"], c["k"], c["v"], c["table"], c["q_lens"], c["kv_lens"], mask_type,
+        H, Hkv, scale, slopes=c["slopes"], key_antiquant_scale=c["ks"],
+        value_antiquant_scale=c["vs"])
+
+
+def _same(a, b, tol=TIGHT):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin), "inf pattern differs"
+    assert np.array_equal(a[~fin], b[~fin])
+    if fin.any():
+        assert np.max(np.abs(a[fin] - b[fin])) <= tol * max(1.0, np.max(np.abs(b[fin])))
+
+
+# ------------------------------------------------------- golden examples
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+def _pool(blocks, kv_heads, head_size):
+    """Nested [block][slot][kvHead][d]; a null slot is one never to be read (NaN)."""
+    nan_slot = [[math.nan] * head_size for _ in range(kv_heads)]
+    return np.array([[nan_slot if slot in (None, [None]) else _arr(slot) for slot in blk]
+                     for blk in blocks], dtype=np.float64)
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_golden_worked_examples(case):
+    D = len(case["query"][0][0])
+    Hkv = case["kv_head_num"]
+    key = _pool(case["key"], Hkv, D)
+    value = _pool(case["value"], Hkv, D)
+    query = np.array(_arr(case["query"]), dtype=np.float64)
+    slopes = np.array(_arr(case["slopes"])) if "slopes" in case else None
+    ks = np.array(_arr(case["key_scale"])) if "key_scale" in case else None
+    vs = np.array(_arr(case["value_scale"])) if "value_scale" in case else None
+    out, lse = oracle.paged_attention(
+        query, key, value, np.array(case["block_tables"]), case["seq_len"],
+        case["kv_seq_len"], case["mask_type"], case["head_num"], case["kv_head_num"],
+        _val(case["qk_scale"]), slopes=slopes, key_antiquant_scale=ks,
+        value_antiquant_scale=vs)
+    _same(out, np.array(_arr(case["out"])), 1e-14)
+    _same(lse, np.array(_arr(case["lse"])), 1e-14)
+
+
+# ------------------------------------------------------------ brute force
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_agrees(seed):
+    rng = np.random.default_rng([314, 77, seed])
+    H, Hkv = [(1, 1), (2, 1), (4, 2), (4, 4)][seed % 4]
+    mask = [MASK_NONE, MASK_CAUSAL, MASK_ALIBI][seed % 3]
+    int8 = seed % 5 == 4
+    bs = [1, 2, 4][seed % 3]
+    D = [1, 3, 8][seed % 3]
+    c = _random_case(rng, B=2, H=H, Hkv=Hkv, D=D, bs=bs,
+                     mask="decode" if seed % 6 == 0 else mask, int8=int8)
+    scale = float(rng.uniform(0.1, 1.5))
+    out, lse = _oracle(c, mask, H, Hkv, scale)
+    bo, bl = brute_attention(
+        c["q"].tolist(), c["k"].tolist(), c["v"].tolist(), c["table"].tolist(),
+        c["q_lens"], c["kv_lens"], mask, H, Hkv, scale, slopes=c["slopes"].tolist(),
+        key_scale=None if c["ks"] is None else c["ks"].tolist(),
+        value_scale=None if c["vs"] is None else c["vs"].tolist())
+    _same(out, np.array(bo).reshape(out.shape))
+    _same(lse, np.array(bl).reshape(lse.shape))
+
+
+# ---------------------------------------------------- library special case
+
+def _sdpa_reference(q, k, v, positions, mask, scale, slopes, H, Hkv):
+    """torch SDPA in fp64 with an explicit bottom-right additive mask."""
+    g = H // Hkv
+    kk = torch.from_numpy(np.repeat(k, g, axis=1)).permute(1, 0, 2)   # [H, kv, D]
+    vv = torch.from_numpy(np.repeat(v, g, axis=1)).permute(1, 0, 2)
+    qq = torch.from_numpy(q).permute(1, 0, 2)                         # [H, nq, D]
+    j = torch.arange(k.shape[0], dtype=torch.float64)
+    p = torch.from_numpy(positions.astype(np.float64))
+    bias = torch.zeros((H, q.shape[0], k.shape[0]), dtype=torch.float64)
+    if mask == MASK_ALIBI:
+        bias += torch.from_numpy(slopes)[:, None, None] * (j[None, None, :] - p[None, :, None])
+    if mask in (MASK_ALIBI, MASK_CAUSAL):
+        bias = bias.masked_fill(j[None, None, :] > p[None, :, None], -math.inf)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qq, kk, vv, attn_mask=bias, scale=scale)
+    return out.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL, MASK_ALIBI])
+@pytest.mark.parametrize("heads", [(4, 4), (8, 2)])
+def test_matches_torch_sdpa(mask, heads):
+    H, Hkv = heads
+    rng = np.random.default_rng([314, 78, mask, H])
+    kv, nq, D = 37, 9, 16
+    q = rng.standard_normal((nq, H, D))
+    k = rng.standard_normal((kv, Hkv, D))
+    v = rng.standard_normal((kv, Hkv, D))
+    slopes = rng.uniform(0, 1, H)
+    positions = oracle.query_positions(nq, kv)
+    out, _ = oracle.attention_contiguous(q, k, v, positions, mask, 0.37, H, Hkv, slopes)
+    ref = _sdpa_reference(q, k, v, positions, mask, 0.37, slopes, H, Hkv)
+    _same(out, ref)
+
+
+# ----------------------------------------------------------- closed forms
+
+def test_causal_zero_query_closed_form():
+    """Q = 0: every visible score is 0, so out_i = mean(V[0..p_i]), lse = ln(p_i+1)."""
+    rng = np.random.default_rng([314, 79])
+    kv, nq, D = 20, 6, 4
+    q = np.zeros((nq, 1, D))
+    k = rng.standard_normal((kv, 1, D))
+    v = rng.standard_normal((kv, 1, D))
+    pos = oracle.query_positions(nq, kv)
+    out, lse = oracle.attention_contiguous(q, k, v, pos, MASK_CAUSAL, 0.5, 1, 1)
+    for i, p in enumerate(pos):
+        np.testing.assert_allclose(out[i, 0], v[:p + 1, 0].mean(axis=0), rtol=0, atol=1e-14)
+        assert abs(lse[i, 0] - math.log(p + 1)) < 1e-14
+
+
+def test_alibi_zero_query_closed_form():
+    """Q = 0 with slope s: weights e^{-s k} for distance k = p - j, a geometric series."""
+    rng = np.random.default_rng([314, 80])
+    kv, nq, D, s = 15, 4, 3, 0.7
+    q = np.zeros((nq, 1, D))
+    k = rng.standard_normal((kv, 1, D))
+    v = rng.standard_normal((kv, 1, D))
+    pos = oracle.query_positions(nq, kv)
+    out, lse = oracle.attention_contiguous(q, k, v, pos, MASK_ALIBI, 1.3, 1, 1, [s])
+    for i, p in enumerate(pos):
+        total = (1 - math.exp(-s * (p + 1))) / (1 - math.exp(-s))
+        assert abs(lse[i, 0] - math.log(total)) < 1e-13
+        want = sum(math.exp(-s * d) * v[p - d, 0] for d in range(p + 1)) / total
+        np.testing.assert_allclose(out[i, 0], want, rtol=0, atol=1e-13)
+
+
+def test_one_hot_values_expose_softmax_row():
+    """V[t] = e_t turns out into the probability row: it sums to 1 and
+    equals exp(s_j - lse) (lse definition of the softmaxLse restriction)."""
+    rng = np.random.default_rng([314, 81])
+    kv, D = 11, 16
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((kv, 1, D))
+    v = np.zeros((kv, 1, D))
+    v[np.arange(kv), 0, np.arange(kv)] = 1.0
+    out, lse = oracle.attention_contiguous(q, k, v, [kv - 1], MASK_NONE, 0.9, 1, 1)
+    prob = out[0, 0, :kv]
+    assert abs(prob.sum() - 1.0) < 1e-12
+    assert np.all(out[0, 0, kv:] == 0)
+    s = 0.9 * (k[:, 0, :] @ q[0, 0])
+    np.testing.assert_allclose(prob, np.exp(s - lse[0, 0]), rtol=1e-12, atol=0)
+
+
+def test_constant_values_give_constant_output():
+    rng = np.random.default_rng([314, 82])
+    c = _random_case(rng, B=3, H=4, Hkv=2, D=5, bs=4, mask=MASK_CAUSAL, allow_empty=False)
+    c["v"][:] = 2.75
+    out, lse = _oracle(c, MASK_CAUSAL, 4, 2, 0.6)
+    seen = np.isfinite(lse)
+    assert seen.any()
+    np.testing.assert_allclose(out[seen], 2.75, rtol=0, atol=1e-13)
+
+
+def test_single_key_returns_its_value_row():
+    rng = np.random.default_rng([314, 83])
+    D = 6
+    q = rng.standard_normal((1, 2, D))
+    k = rng.standard_normal((1, 1, D))
+    v = rng.standard_normal((1, 1, D))
+    out, lse = oracle.attention_contiguous(q, k, v, [0], MASK_NONE, 0.25, 2, 1)
+    for h in range(2):
+        np.testing.assert_array_equal(out[0, h], v[0, 0])
+        assert abs(lse[0, h] - 0.25 * float(q[0, h] @ k[0, 0])) < 1e-15
+
+
+# ------------------------------------------------------------- invariants
+
+def test_paged_equals_contiguous_and_ignores_unused_slots():
+    """Paged layout = the blocks of blockTables laid end to end; unused
+    blocks, tail slots and -1 table padding are never read."""
+    rng = np.random.default_rng([314, 84])
+    B, H, Hkv, D, bs = 3, 4, 2, 8, 4
+    c = _random_case(rng, B=B, H=H, Hkv=Hkv, D=D, bs=bs, mask=MASK_ALIBI, allow_empty=False)
+    out, lse = _oracle(c, MASK_ALIBI, H, Hkv, 0.4)
+    # poison every slot no sequence owns
+    used = np.zeros(c["k"].shape[:2], dtype=bool)
+    for b in range(B):
+        for t in range(c["kv_lens"][b]):
+            used[c["table"][b, t // bs], t % bs] = True
+    pk, pv = c["k"].copy(), c["v"].copy()
+    pk[~used] = np.nan
+    pv[~used] = np.nan
+    p_out, p_lse = oracle.paged_attention(
+        c["q"], pk, pv, c["table"], c["q_lens"], c["kv_lens"], MASK_ALIBI, H, Hkv, 0.4,
+        slopes=c["slopes"])
+    assert np.array_equal(p_out, out) and np.array_equal(p_lse, lse)
+    # per-sequence contiguous computation
+    q0 = 0
+    for b in range(B):
+        rows = []
+        for t in range(c["kv_lens"][b]):
+            rows.append(c["k"][c["table"][b, t // bs], t % bs])
+        kc = np.array(rows).reshape(-1, Hkv, D)
+        vc = np.array([c["v"][c["table"][b, t // bs], t % bs]
+                       for t in range(c["kv_lens"][b])]).reshape(-1, Hkv, D)
+        ql = c["q_lens"][b]
+        o_b, l_b = oracle.attention_contiguous(
+            c["q"][q0:q0 + ql], kc, vc, oracle.query_positions(ql, c["kv_lens"][b]),
+            MASK_ALIBI, 0.4, H, Hkv, c["slopes"])
+        assert np.array_equal(o_b, out[q0:q0 + ql])
+        q0 += ql
+    # permuting the physical blocks together with the table changes nothing
+    perm = rng.permutation(c["k"].shape[0])
+    inv = np.argsort(perm)
+    tab = np.where(c["table"] >= 0, inv[np.maximum(c["table"], 0)], -1)
+    r_out, r_lse = oracle.paged_attention(
+        c["q"], c["k"][perm], c["v"][perm], tab, c["q_lens"], c["kv_lens"], MASK_ALIBI,
+        H, Hkv, 0.4, slopes=c["slopes"])
+    _same(r_out, out)
+    _same(r_lse, lse)
+
+
+def test_alibi_with_zero_slopes_is_causal():
+    rng = np.random.default_rng([314, 85])
+    c = _random_case(rng, B=3, H=2, Hkv=1, D=4, bs=2, mask=MASK_CAUSAL)
+    c["slopes"] = np.zeros(2)
+    a = _oracle(c, MASK_ALIBI, 2, 1, 0.8)
+    b = _oracle(c, MASK_CAUSAL, 2, 1, 0.8)
+    _same(a[0], b[0])
+    _same(a[1], b[1])
+
+
+def test_alibi_row_shift_changes_lse_only():
+    """Adding the same constant to a row's bias leaves out unchanged: the
+    out of maskType 3 does not depend on where the bias is anchored."""
+    rng = np.random.default_rng([314, 86])
+    kv, nq, D = 13, 5, 4
+    q = rng.standard_normal((nq, 1, D))
+    k = rng.standard_normal((kv, 1, D))
+    v = rng.standard_normal((kv, 1, D))
+    pos = oracle.query_positions(nq, kv)
+    o1, l1 = oracle.attention_contiguous(q, k, v, pos, MASK_ALIBI, 0.5, 1, 1, [0.3])
+    # the same causal pattern with a bias anchored at key 0 instead of p_i
+    out2 = np.zeros_like(o1)
+    for i, p in enumerate(pos):
+        s = 0.5 * (k[:p + 1, 0] @ q[i, 0]) + 0.3 * np.arange(p + 1)
+        e = np.exp(s - s.max())
+        out2[i, 0] = e @ v[:p + 1, 0] / e.sum()
+    np.testing.assert_allclose(o1, out2, rtol=0, atol=1e-13)
+
+
+def test_scale_invariance():
+    rng = np.random.default_rng([314, 87])
+    c = _random_case(rng, B=2, H=4, Hkv=4, D=6, bs=3, mask=MASK_ALIBI)
+    a = _oracle(c, MASK_ALIBI, 4, 4, 0.5)
+    c2 = dict(c, q=c["q"] * 4.0)
+    b = _oracle(c2, MASK_ALIBI, 4, 4, 0.125)
+    _same(a[0], b[0], 1e-12)
+    _same(a[1], b[1], 1e-12)
+
+
+def test_gqa_equals_repeated_kv_heads():
+    rng = np.random.default_rng([314, 88])
+    H, Hkv = 8, 2
+    c = _random_case(rng, B=3, H=H, Hkv=Hkv, D=5, bs=2, mask=MASK_CAUSAL)
+    a = _oracle(c, MASK_CAUSAL, H, Hkv, 0.7)
+    c2 = dict(c, k=np.repeat(c["k"], H // Hkv, axis=2), v=np.repeat(c["v"], H // Hkv, axis=2))
+    b = _oracle(c2, MASK_CAUSAL, H, H, 0.7)
+    _same(a[0], b[0])
+    _same(a[1], b[1])
+    # kvHeadNum = 0 means kvHeadNum = headNum
+    d0 = _oracle(c2, MASK_CAUSAL, H, 0, 0.7)
+    _same(d0[0], b[0])
+
+
+def test_int8_equals_float_on_dequantised_pool():
+    rng = np.random.default_rng([314, 89])
+    c = _random_case(rng, B=2, H=4, Hkv=2, D=6, bs=4, mask=MASK_NONE, int8=True)
+    a = _oracle(c, MASK_NONE, 4, 2, 0.3)
+    kf = c["k"] * c["ks"][None, None]
+    vf = c["v"] * c["vs"][None, None]
+    b = oracle.paged_attention(c["q"], kf, vf, c["table"], c["q_lens"], c["kv_lens"],
+                               MASK_NONE, 4, 2, 0.3)
+    _same(a[0], b[0])
+    _same(a[1], b[1])
+    # dequant multiplies per (kv head, channel), not per token or transposed
+    x = np.arange(2 * 3, dtype=np.int64).reshape(1, 2, 3) - 3
+    sc = np.array([[1.0, 2.0, 4.0], [8.0, 16.0, 32.0]])
+    np.testing.assert_array_equal(oracle.dequantize_per_channel(x, sc),
+                                  [[[-3.0, -4.0, -4.0], [0.0, 16.0, 64.0]]])
+
+
+def test_empty_tensor_rules():
+    """aclnnFusedInferAttentionScoreV4, Constraints, empty input: empty
+    query/out returns empty; empty key/value gives out 0 and lse inf."""
+    q = np.zeros((0, 2, 4))
+    k = np.ones((3, 2, 1, 4))
+    out, lse = oracle.paged_attention(q, k, k, np.zeros((1, 2), int), [0], [3], 0, 2, 1, 1.0)
+    assert out.shape == (0, 2, 4) and lse.shape == (0, 2)
+    q = np.ones((2, 2, 4))
+    ek = np.zeros((0, 2, 1, 4))
+    out, lse = oracle.paged_attention(q, ek, ek, np.zeros((2, 1), int), [1, 1], [5, 5],
+                                      0, 2, 1, 1.0)
+    assert np.all(out == 0) and np.all(np.isinf(lse)) and np.all(lse > 0)
+    out, lse = oracle.paged_attention(q, k, k, np.zeros((2, 1), int), [1, 1], [0, 0],
+                                      0, 2, 1, 1.0)
+    assert np.all(out == 0) and np.all(lse == np.inf)
+
+
+def test_merge_partials_equals_unsplit():
+    """The max/sum/log decomposition of the softmaxLse restriction merges
+    results over disjoint key ranges into the full result."""
+    rng = np.random.default_rng([314, 90])
+    kv, nq, H, D = 29, 4, 2, 5
+    q = rng.standard_normal((nq, H, D))
+    k = rng.standard_normal((kv, H, D))
+    v = rng.standard_normal((kv, H, D))
+    pos = oracle.query_positions(nq, kv)
+    full = oracle.attention_contiguous(q, k, v, pos, MASK_CAUSAL, 0.6, H, H)
+    cuts = [0, 7, 8, 20, kv]
+    outs, lses = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        # the chunk's keys keep their absolute index: shift the positions
+        o, l = oracle.attention_contiguous(q, k[a:b], v[a:b], pos - a, MASK_CAUSAL,
+                                           0.6, H, H)
+        outs.append(o)
+        lses.append(l)
+    out, lse = oracle.merge_partials(outs, lses)
+    _same(out, full[0])
+    _same(lse, full[1])
