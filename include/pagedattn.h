@@ -1,0 +1,197 @@
+/*
+ * pagedattn.h -- paged-KV fused inference attention for AMD MI355X (gfx950).
+ *
+ * Computes, per query row i of sequence b and query head h,
+ *
+ *     out[i,h,:] = sum_j softmax_j( qkScale * <q[i,h,:], K[j,kvh,:]> + bias(i,j) ) * V[j,kvh,:]
+ *     lse[i,h]   = log( sum_j exp( qkScale * <q, K_j> + bias(i,j) ) )        (natural log)
+ *
+ * with K/V read through a paged cache (blockTables), kvh = h / (headNum / kvHeadNum) (GQA),
+ * and bias from maskType.  Formula: aclnnFusedInferAttentionScoreV4, "Function"
+ * (Attention = Softmax(QK^T/sqrt(d) + mask) V, softmax per row); qkScale generalises
+ * 1/sqrt(d) and the mask/bias is added after the scaling (PrefixEncoder, Members:
+ * qkScale, maskType).  lse definition: aclnnFusedInferAttentionScoreV3, Constraints,
+ * softmaxLse (max + log of the sum of exponentials, the ring-attention decomposition).
+ *
+ * Two-phase call, as the pages' operator APIs (PrefixEncoder, Definition; the
+ * "GetWorkspaceSize then execute" pattern of aclnnFusedInferAttentionScoreV3/V4):
+ *   1. pa_paged_attention_get_workspace_size(...) validates every argument, plans the
+ *      work and returns the device workspace size plus an operator handle.  It makes no
+ *      HIP call and touches no device memory.
+ *   2. pa_paged_attention(workspace, size, op, stream) enqueues the kernels on `stream`.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are described by pa_tensor (data pointer, dtype, shape, strides in
+ *     elements).  The innermost dimension must be contiguous; see each argument.
+ *   - "device" = HIP device memory (e.g. a torch CUDA tensor on ROCm);
+ *     "host" = ordinary CPU memory.
+ *   - The caller owns every tensor and the workspace.  The library never allocates
+ *     device memory.  It owns the pa_op (host memory), released by pa_op_destroy.
+ *   - Tensors and the workspace must stay alive, and must not be written by others,
+ *     until the work enqueued by pa_paged_attention has completed on the stream.
+ *   - Block ids in blockTables are not validated (aclnnFusedInferAttentionScoreV3,
+ *     Constraints, paged attention scenario: the validity of block ids is not
+ *     verified).  An id outside [0, numBlocks) for a token t < kvSeqLen[b] is an
+ *     out-of-bounds device read: the caller must not pass one.  Entries past
+ *     ceil(kvSeqLen[b] / blockSize) are never read (they may hold -1).
+ *   - Results are deterministic: the same call on the same inputs gives bitwise equal
+ *     outputs (aclnnFusedInferAttentionScoreV3, Constraints: deterministic computation).
+ *     No atomics; split-KV partials are merged in a fixed order.
+ *   - Errors: every check happens in phase 1, which returns a pa_status and leaves
+ *     *op = NULL on failure; pa_last_error() gives a message naming the failed check.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  The pages' own error-code table is not recoverable, so these are
+ * this library's codes for the same classes of failure (null pointer, invalid
+ * parameter, unsupported feature) plus the run-time ones. */
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULLPTR = 1,              /* a required pointer argument is NULL */
+    PA_ERR_PARAM_INVALID = 2,        /* shape / dtype / value check failed */
+    PA_ERR_UNSUPPORTED = 3,          /* valid per the pages, not implemented here */
+    PA_ERR_WORKSPACE_TOO_SMALL = 4,  /* phase 2 got less workspace than phase 1 asked */
+    PA_ERR_HIP = 5,                  /* a HIP runtime call failed in phase 2 */
+    PA_ERR_HOST_ALLOC = 6            /* host memory for the operator could not be had */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F16 = 1,
+    PA_BF16 = 2,
+    PA_I8 = 3,
+    PA_F32 = 4,
+    PA_I32 = 5
+} pa_dtype;
+
+/* Tensor descriptor.  shape[0..ndim-1] and stride[0..ndim-1] (in elements, not bytes)
+ * are read; entries past ndim are ignored.  A NULL pa_tensor* means "not passed". */
+typedef struct pa_tensor {
+    void* data;
+    int32_t dtype;        /* pa_dtype */
+    int32_t ndim;         /* 1..4 */
+    int64_t shape[4];
+    int64_t stride[4];
+} pa_tensor;
+
+/* maskType values (PrefixEncoder, Members: maskType). */
+enum {
+    PA_MASK_NONE = 0,               /* every key j < kvSeqLen[b] visible */
+    PA_MASK_ALIBI = 3,              /* MASK_TYPE_ALIBI_COMPRESS: bias slopes[h]*(j - p_i), causal */
+    PA_MASK_ALIBI_SQRT = 4,         /* MASK_TYPE_ALIBI_COMPRESS_SQRT: PA_ERR_UNSUPPORTED */
+    PA_MASK_ALIBI_LEFT_ALIGN = 5,   /* MASK_TYPE_ALIBI_COMPRESS_LEFT_ALIGN: PA_ERR_UNSUPPORTED */
+    PA_MASK_CAUSAL = 9              /* MASK_TYPE_CAUSAL_MASK: keys j > p_i hidden */
+};
+
+typedef struct pa_op pa_op;
+
+/*
+ * Phase 1: validate, plan, size the workspace.  (PrefixEncoder, Definition:
+ * AtbSelfAttentionPrefixEncoderGetWorkspaceSize and its Members table; lse and the
+ * antiquant scales are added from aclnnFusedInferAttentionScoreV3.)
+ *
+ * query        device, [nTokens, headNum, headSize] or [nTokens, headNum*headSize],
+ *              f16 or bf16.  Rows of all sequences packed back to back: sequence b owns
+ *              rows q0[b] .. q0[b]+seqLen[b]-1, q0[b] = seqLen[0] + ... + seqLen[b-1].
+ *              The d stride must be 1; token and head strides are free (multiples of
+ *              16 bytes; attnOut rows and heads must not overlap).  Data 16-byte aligned.
+ * key, value   device, [numBlocks, blockSize, kvHeadNum, headSize] or
+ *              [numBlocks, blockSize, kvHeadNum*headSize] (layout BnBsH), dtype = query
+ *              dtype, or int8 with both antiquant scales given.  Same shape and dtype.
+ *              d stride 1; block, slot and head strides are free (multiples of 16
+ *              bytes), so a (numBlocks, kvHeadNum, blockSize, headSize) cache can be
+ *              passed as its permuted view.  Data 16-byte aligned.
+ *              Token t of sequence b is at block blockTables[b][t / blockSize],
+ *              slot t % blockSize.
+ * blockTables  device, [batch, maxBlockNum] int32, row stride free, column stride 1.
+ *              maxBlockNum >= ceil(max_b kvSeqLen[b] / blockSize).
+ * mask         must be NULL (compressed mask tensors are not supported; maskType 3
+ *              generates the ALiBi bias from slopes).
+ * seqLen       HOST, [batch] int32: new query tokens per sequence, >= 0, summing to
+ *              nTokens.  If every seqLen is <= 1 the decode kernels run (one query per
+ *              sequence), otherwise the prefill kernels.
+ * kvSeqLen     HOST, [batch] int32: tokens in the cache per sequence (cached prefix plus
+ *              the new tokens), >= 0.  Query i of sequence b sits at absolute position
+ *              p_i = kvSeqLen[b] - seqLen[b] + i (the new tokens are the last ones).
+ * slopes       device, [headNum] f32; required iff maskType == PA_MASK_ALIBI, else NULL.
+ * maskType     PA_MASK_NONE, PA_MASK_CAUSAL (key j visible iff j <= p_i) or
+ *              PA_MASK_ALIBI (causal plus bias slopes[h] * (j - p_i), added after the
+ *              qkScale product).  4 and 5 return PA_ERR_UNSUPPORTED.
+ * headNum      > 0.   kvHeadNum: 0 means headNum; headNum % kvHeadNum == 0
+ *              (aclnnFusedInferAttentionScoreV3, Constraints: numHeads divisible by
+ *              numKeyValueHeads).  Query head h reads kv head h / (headNum/kvHeadNum).
+ * qkScale      finite float multiplying Q*K^T (default on the pages: 1).
+ * keyAntiquantScale, valueAntiquantScale
+ *              device, kvHeadNum*headSize elements (shapes [kvHeadNum, headSize],
+ *              [1, kvHeadNum, headSize], [kvHeadNum*headSize] ... all accepted),
+ *              contiguous, f32 or the query dtype.  Required iff key/value are int8:
+ *              per-channel symmetric dequant K_hat[t,c,d] = scale[c,d] * K[t,c,d]
+ *              (aclnnFusedInferAttentionScoreV3, Constraints on antiquantScale,
+ *              per-channel mode; no offset).
+ * attnOut      device, same shape form and dtype as query; written in full.
+ * lse          device, [nTokens, headNum] f32, or NULL when not wanted.
+ * workspaceSize  out: bytes of device workspace phase 2 needs (may be 0).
+ * op           out: operator handle; NULL on failure.
+ *
+ * Empty tensors (aclnnFusedInferAttentionScoreV4, Constraints, processing when the
+ * input parameter is empty): nTokens*headNum*headSize == 0 -> nothing is computed and
+ * the remaining checks are skipped; key or value with 0 elements -> out is all 0 and
+ * lse all +inf.  A query row that sees no key (kvSeqLen[b] == 0, or causal rows with
+ * p_i < 0) also gets out 0 and lse +inf.
+ */
+pa_status pa_paged_attention_get_workspace_size(
+    const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
+    const pa_tensor* blockTables, const pa_tensor* mask,
+    const pa_tensor* seqLen, const pa_tensor* kvSeqLen, const pa_tensor* slopes,
+    int maskType, int32_t headNum, int32_t kvHeadNum, float qkScale,
+    const pa_tensor* keyAntiquantScale, const pa_tensor* valueAntiquantScale,
+    const pa_tensor* attnOut, const pa_tensor* lse,
+    uint64_t* workspaceSize, pa_op** op);
+
+/*
+ * Phase 2: enqueue the computation on `stream` (a hipStream_t; NULL = the null
+ * stream).  (PrefixEncoder, Definition: AtbSelfAttentionPrefixEncoder; the pages'
+ * context argument becomes a HIP stream.)  workspace: device memory of at least the
+ * phase-1 size, 256-byte aligned, or NULL if that size is 0; its contents on entry do
+ * not matter and are scratch afterwards.  The call returns once the work is enqueued.
+ * An op may be executed any number of times, on any stream of its device; two
+ * executions must not share a workspace while both are in flight.
+ * Returns PA_ERR_NULLPTR (op, or a needed workspace, is NULL), PA_ERR_WORKSPACE_TOO_SMALL,
+ * PA_ERR_PARAM_INVALID (workspace not 256-byte aligned) or PA_ERR_HIP on failure.
+ */
+pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
+                             void* stream);
+
+/* Release an operator handle (NULL is ignored).  Work already enqueued is unaffected: the
+ * call waits until the last upload of the op's work lists has left host memory. */
+void pa_op_destroy(pa_op* op);
+
+/* Write a JSON description of the operator's plan into buf (NUL-terminated, cut at
+ * cap - 1 bytes; buf may be NULL when cap is 0) and return the full length without the
+ * NUL.  Keys: "mode" ("noop", "fill", "decode", "prefill"), "workspace_bytes",
+ * "chunk_tiles", "partial_slots", and the work lists "decode_items"
+ * [b, kvh, hg, t0, t1, slot, qrow, kvlen], "combine_items" [kvh, hg, slot0, nsplit, qrow],
+ * "prefill_items" [b, h, qbeg, qlen, kvlen, qrow0, ktiles].  Host only, no HIP call.
+ * For inspection and tests: not a stable interface.  op == NULL returns 0. */
+uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap);
+
+/* Static text for a status code. */
+const char* pa_status_string(int status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

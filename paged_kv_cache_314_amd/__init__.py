@@ -1,0 +1,40 @@
+"""Paged-KV fused inference attention for AMD MI355X (gfx950).
+
+The compute lives in libpagedattn.so (HIP kernels behind the C ABI declared in
+include/pagedattn.h).  This package is its thin Python binding plus the
+seeded synthetic-input generators (``workloads``) used by tests and benchmarks.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    Op,
+    PA_BF16,
+    PA_ERR_HIP,
+    PA_ERR_HOST_ALLOC,
+    PA_ERR_NULLPTR,
+    PA_ERR_PARAM_INVALID,
+    PA_ERR_UNSUPPORTED,
+    PA_ERR_WORKSPACE_TOO_SMALL,
+    PA_F16,
+    PA_F32,
+    PA_I8,
+    PA_I32,
+    PA_MASK_ALIBI,
+    PA_MASK_CAUSAL,
+    PA_MASK_NONE,
+    PA_OK,
+    PagedAttentionError,
+    PaTensor,
+    alloc_workspace,
+    describe,
+    load,
+    pa_last_error,
+    pa_op_describe,
+    pa_op_destroy,
+    pa_paged_attention,
+    pa_paged_attention_get_workspace_size,
+    pa_status_string,
+    pa_version,
+    paged_attention,
+)

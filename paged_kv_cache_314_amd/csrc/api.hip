@@ -1,0 +1,289 @@
+// C ABI of libpagedattn: two-phase get-workspace-size / execute (PrefixEncoder,
+// Definition: GetWorkspaceSize then execute with workspace, size, op and context).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "pa_internal.h"
+#include "pa_kernels.h"
+#include "pagedattn.h"
+
+struct pa_op {
+    pa::Plan plan;
+    void* staging = nullptr;        // pinned copy of the work lists (allocated on first run)
+    hipEvent_t copied = nullptr;    // recorded after each upload from `staging`
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+    std::string msg = std::string(what) + ": " + hipGetErrorString(e);
+    return fail(PA_ERR_HIP, msg);
+}
+
+// Copy the host work lists into one pinned buffer that phase 2 uploads each run.
+pa_status ensure_staging(pa_op* op) {
+    const pa::Plan& p = op->plan;
+    if (op->staging != nullptr || p.items_bytes == 0) return PA_OK;
+    hipError_t e = hipHostMalloc(&op->staging, p.items_bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        op->staging = nullptr;
+        return hip_fail(e, "hipHostMalloc(work list staging)");
+    }
+    auto* base = static_cast<unsigned char*>(op->staging);
+    std::memset(base, 0, p.items_bytes);
+    if (p.mode == pa::Mode::kDecode) {
+        std::memcpy(base + p.off_items, p.decode_items.data(),
+                    p.decode_items.size() * sizeof(pa::DecodeItem));
+        std::memcpy(base + p.off_combine, p.combine_items.data(),
+                    p.combine_items.size() * sizeof(pa::CombineItem));
+    } else if (p.mode == pa::Mode::kPrefill) {
+        std::memcpy(base + p.off_items, p.prefill_items.data(),
+                    p.prefill_items.size() * sizeof(pa::PrefillItem));
+    }
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_paged_attention_get_workspace_size(
+    const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
+    const pa_tensor* blockTables, const pa_tensor* mask, const pa_tensor* seqLen,
+    const pa_tensor* kvSeqLen, const pa_tensor* slopes, int maskType, int32_t headNum,
+    int32_t kvHeadNum, float qkScale, const pa_tensor* keyAntiquantScale,
+    const pa_tensor* valueAntiquantScale, const pa_tensor* attnOut, const pa_tensor* lse,
+    uint64_t* workspaceSize, pa_op** op) {
+    if (op != nullptr) *op = nullptr;
+    if (workspaceSize == nullptr || op == nullptr)
+        return fail(PA_ERR_NULLPTR, "workspaceSize and op must not be NULL");
+    *workspaceSize = 0;
+    pa_op* h = new (std::nothrow) pa_op();
+    if (h == nullptr) return fail(PA_ERR_HOST_ALLOC, "cannot allocate the operator");
+    std::string err;
+    const pa_status st = pa::plan(query, key, value, blockTables, mask, seqLen, kvSeqLen, slopes,
+                                  maskType, headNum, kvHeadNum, qkScale, keyAntiquantScale,
+                                  valueAntiquantScale, attnOut, lse, h->plan, err);
+    if (st != PA_OK) {
+        delete h;
+        return fail(st, err);
+    }
+    *workspaceSize = h->plan.workspace_bytes;
+    *op = h;
+    g_last_error.clear();
+    return PA_OK;
+}
+
+pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op, void* stream) {
+    if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
+    const pa::Plan& p = op->plan;
+    if (p.mode == pa::Mode::kNoop) return PA_OK;
+    if (workspaceSize < p.workspace_bytes)
+        return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace of " + std::to_string(workspaceSize) + " bytes, need " +
+                        std::to_string(p.workspace_bytes));
+    if (p.workspace_bytes > 0 && workspace == nullptr)
+        return fail(PA_ERR_NULLPTR, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(PA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = p.qtype == PA_BF16;
+    const bool i8 = p.kvtype == PA_I8;
+    hipError_t e;
+
+    if (p.mode == pa::Mode::kFill) {
+        pa::FillArgs f{};
+        f.out = p.out;
+        f.lse = p.lse;
+        f.n_tokens = p.n_tokens;
+        f.head_num = p.head_num;
+        f.head_size = p.head_size;
+        f.out_tok_stride = p.out_tok_stride;
+        f.out_head_stride = p.out_head_stride;
+        f.lse_tok_stride = p.lse_tok_stride;
+        e = pa::launch_fill(f, s);
+        return e == hipSuccess ? PA_OK : hip_fail(e, "fill kernel launch");
+    }
+
+    pa_status st = ensure_staging(op);
+    if (st != PA_OK) return st;
+    auto* ws = static_cast<unsigned char*>(workspace);
+    if (op->copied == nullptr) {
+        e = hipEventCreateWithFlags(&op->copied, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            op->copied = nullptr;
+            return hip_fail(e, "hipEventCreateWithFlags");
+        }
+    }
+    e = hipMemcpyAsync(ws, op->staging, p.items_bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work lists)");
+    e = hipEventRecord(op->copied, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    const float scale_log2 = p.qk_scale * 1.4426950408889634f;
+
+    if (p.mode == pa::Mode::kDecode) {
+        pa::DecodeArgs a{};
+        a.items = reinterpret_cast<const pa::DecodeItem*>(ws + p.off_items);
+        a.q = p.q;
+        a.k = p.k;
+        a.v = p.v;
+        a.table = p.table;
+        a.out = p.out;
+        a.lse = p.lse;
+        a.slopes = p.slopes;
+        a.kscale = p.kscale;
+        a.vscale = p.vscale;
+        a.part_o = reinterpret_cast<float*>(ws + p.off_part_o);
+        a.part_ml = reinterpret_cast<float*>(ws + p.off_part_ml);
+        a.q_tok_stride = p.q_tok_stride;
+        a.q_head_stride = p.q_head_stride;
+        a.out_tok_stride = p.out_tok_stride;
+        a.out_head_stride = p.out_head_stride;
+        a.lse_tok_stride = p.lse_tok_stride;
+        a.k_blk_stride = p.k_blk_stride;
+        a.k_slot_stride = p.k_slot_stride;
+        a.k_head_stride = p.k_head_stride;
+        a.v_blk_stride = p.v_blk_stride;
+        a.v_slot_stride = p.v_slot_stride;
+        a.v_head_stride = p.v_head_stride;
+        a.table_stride = p.table_stride;
+        a.group = p.group;
+        a.block_size = p.block_size;
+        a.mask_type = p.mask_type;
+        a.scale_is_f32 = p.scale_type == PA_F32;
+        a.scale_log2 = scale_log2;
+        e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, s);
+        if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+        if (!p.combine_items.empty()) {
+            pa::CombineArgs c{};
+            c.items = reinterpret_cast<const pa::CombineItem*>(ws + p.off_combine);
+            c.part_o = a.part_o;
+            c.part_ml = a.part_ml;
+            c.out = p.out;
+            c.lse = p.lse;
+            c.out_tok_stride = p.out_tok_stride;
+            c.out_head_stride = p.out_head_stride;
+            c.lse_tok_stride = p.lse_tok_stride;
+            c.group = p.group;
+            e = pa::launch_combine(c, static_cast<int>(p.combine_items.size()), p.head_size, bf16, s);
+            if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+        }
+        return PA_OK;
+    }
+
+    pa::PrefillArgs a{};
+    a.items = reinterpret_cast<const pa::PrefillItem*>(ws + p.off_items);
+    a.q = p.q;
+    a.k = p.k;
+    a.v = p.v;
+    a.table = p.table;
+    a.out = p.out;
+    a.lse = p.lse;
+    a.slopes = p.slopes;
+    a.kscale = p.kscale;
+    a.vscale = p.vscale;
+    a.q_tok_stride = p.q_tok_stride;
+    a.q_head_stride = p.q_head_stride;
+    a.out_tok_stride = p.out_tok_stride;
+    a.out_head_stride = p.out_head_stride;
+    a.lse_tok_stride = p.lse_tok_stride;
+    a.k_blk_stride = p.k_blk_stride;
+    a.k_slot_stride = p.k_slot_stride;
+    a.k_head_stride = p.k_head_stride;
+    a.v_blk_stride = p.v_blk_stride;
+    a.v_slot_stride = p.v_slot_stride;
+    a.v_head_stride = p.v_head_stride;
+    a.table_stride = p.table_stride;
+    a.group = p.group;
+    a.block_size = p.block_size;
+    a.mask_type = p.mask_type;
+    a.scale_is_f32 = p.scale_type == PA_F32;
+    a.scale_log2 = scale_log2;
+    e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e, "prefill kernel launch");
+}
+
+void pa_op_destroy(pa_op* op) {
+    if (op == nullptr) return;
+    // an enqueued upload may still read the pinned staging buffer: wait for the last one
+    if (op->copied != nullptr) {
+        (void)hipEventSynchronize(op->copied);
+        (void)hipEventDestroy(op->copied);
+    }
+    if (op->staging != nullptr) (void)hipHostFree(op->staging);
+    delete op;
+}
+
+uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
+    if (op == nullptr) return 0;
+    const pa::Plan& p = op->plan;
+    static const char* modes[] = {"noop", "fill", "decode", "prefill"};
+    std::string s = "{\"mode\": \"";
+    s += modes[static_cast<int>(p.mode)];
+    s += "\", \"workspace_bytes\": " + std::to_string(p.workspace_bytes);
+    s += ", \"chunk_tiles\": " + std::to_string(p.decode_chunk_tiles);
+    s += ", \"partial_slots\": " + std::to_string(p.partial_slots);
+    s += ", \"decode_items\": [";
+    for (size_t i = 0; i < p.decode_items.size(); ++i) {
+        const pa::DecodeItem& d = p.decode_items[i];
+        if (i) s += ", ";
+        s += "[" + std::to_string(d.b) + ", " + std::to_string(d.kvh) + ", " + std::to_string(d.hg) +
+             ", " + std::to_string(d.t0) + ", " + std::to_string(d.t1) + ", " +
+             std::to_string(d.slot) + ", " + std::to_string(d.qrow) + ", " +
+             std::to_string(d.kvlen) + "]";
+    }
+    s += "], \"combine_items\": [";
+    for (size_t i = 0; i < p.combine_items.size(); ++i) {
+        const pa::CombineItem& c = p.combine_items[i];
+        if (i) s += ", ";
+        s += "[" + std::to_string(c.kvh) + ", " + std::to_string(c.hg) + ", " +
+             std::to_string(c.slot0) + ", " + std::to_string(c.nsplit) + ", " +
+             std::to_string(c.qrow) + "]";
+    }
+    s += "], \"prefill_items\": [";
+    for (size_t i = 0; i < p.prefill_items.size(); ++i) {
+        const pa::PrefillItem& q = p.prefill_items[i];
+        if (i) s += ", ";
+        s += "[" + std::to_string(q.b) + ", " + std::to_string(q.h) + ", " + std::to_string(q.qbeg) +
+             ", " + std::to_string(q.qlen) + ", " + std::to_string(q.kvlen) + ", " +
+             std::to_string(q.qrow0) + ", " + std::to_string(q.ktiles) + "]";
+    }
+    s += "]}";
+    if (buf != nullptr && cap > 0) {
+        const uint64_t n = std::min<uint64_t>(cap - 1, s.size());
+        std::memcpy(buf, s.data(), n);
+        buf[n] = 0;
+    }
+    return s.size();
+}
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_NULLPTR: return "PA_ERR_NULLPTR: a required pointer is NULL";
+        case PA_ERR_PARAM_INVALID: return "PA_ERR_PARAM_INVALID: invalid argument";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: not implemented";
+        case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL: workspace too small or misaligned";
+        case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
+        case PA_ERR_HOST_ALLOC: return "PA_ERR_HOST_ALLOC: host allocation failed";
+        default: return "unknown pa_status";
+    }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pa_version(void) { return 100; }
+
+}  // extern "C"

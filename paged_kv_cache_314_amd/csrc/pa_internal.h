@@ -1,0 +1,109 @@
+// Internal types shared by the host planner (plan.cpp) and the HIP launchers.
+// Plain C++17: no HIP types, so the planner builds and runs without a GPU.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+// Token tile one wave consumes per step in the decode kernel.
+constexpr int kDecodeTile = 32;
+// Heads packed into one decode MFMA column block (the N dimension of 16x16x32).
+constexpr int kHeadPack = 16;
+// Waves per decode workgroup.
+constexpr int kDecodeWaves = 4;
+// Prefill: query rows per workgroup and keys per step.
+constexpr int kPrefillBM = 128;
+constexpr int kPrefillBN = 64;
+
+enum class Mode : int32_t { kNoop = 0, kFill = 1, kDecode = 2, kPrefill = 3 };
+
+// One decode workgroup: a range of 32-token tiles of one (sequence, kv head, head group).
+struct DecodeItem {
+    int32_t b;        // sequence
+    int32_t kvh;      // kv head
+    int32_t hg;       // group of up to 16 query heads sharing kvh
+    int32_t t0, t1;   // tile range [t0, t1)
+    int32_t slot;     // -1: write out/lse directly; >= 0: partial slot in the workspace
+    int32_t qrow;     // query/out row of this sequence's decode token
+    int32_t kvlen;    // kvSeqLen[b]
+};
+static_assert(sizeof(DecodeItem) == 32, "DecodeItem layout");
+
+// One combine workgroup: merge nsplit consecutive partial slots into out/lse.
+struct CombineItem {
+    int32_t kvh, hg;
+    int32_t slot0, nsplit;
+    int32_t qrow;
+    int32_t pad[3];
+};
+static_assert(sizeof(CombineItem) == 32, "CombineItem layout");
+
+// One prefill workgroup: kPrefillBM query rows of one (sequence, head).
+struct PrefillItem {
+    int32_t b;
+    int32_t h;
+    int32_t qbeg;     // first local query row of the tile
+    int32_t qlen;     // seqLen[b]
+    int32_t kvlen;    // kvSeqLen[b]
+    int32_t qrow0;    // packed row of local query 0 of this sequence
+    int32_t ktiles;   // key tiles (kPrefillBN) the tile must visit
+    int32_t pad;
+};
+static_assert(sizeof(PrefillItem) == 32, "PrefillItem layout");
+
+// Everything phase 2 needs; produced by plan().
+struct Plan {
+    Mode mode = Mode::kNoop;
+    pa_dtype qtype = PA_F16;     // query / out dtype
+    pa_dtype kvtype = PA_F16;    // key / value dtype
+    pa_dtype scale_type = PA_F32;
+    int32_t batch = 0, head_num = 0, kv_head_num = 0, group = 1, head_groups = 1;
+    int32_t head_size = 0, block_size = 0, num_blocks = 0, n_tokens = 0;
+    int32_t mask_type = 0;
+    float qk_scale = 1.0f;
+
+    // device pointers captured in phase 1
+    const void* q = nullptr;
+    const void* k = nullptr;
+    const void* v = nullptr;
+    const int32_t* table = nullptr;
+    void* out = nullptr;
+    float* lse = nullptr;
+    const float* slopes = nullptr;
+    const void* kscale = nullptr;
+    const void* vscale = nullptr;
+
+    // strides in elements
+    int64_t q_tok_stride = 0, q_head_stride = 0, out_tok_stride = 0, out_head_stride = 0;
+    int64_t lse_tok_stride = 0;
+    int64_t k_blk_stride = 0, k_slot_stride = 0, k_head_stride = 0;
+    int64_t v_blk_stride = 0, v_slot_stride = 0, v_head_stride = 0;
+    int64_t table_stride = 0;
+
+    // work lists (copied into the workspace by phase 2)
+    std::vector<DecodeItem> decode_items;
+    std::vector<CombineItem> combine_items;
+    std::vector<PrefillItem> prefill_items;
+    int32_t decode_chunk_tiles = 0;
+    int32_t partial_slots = 0;
+
+    // workspace layout (bytes, 256-aligned offsets)
+    uint64_t off_items = 0, off_combine = 0, off_part_o = 0, off_part_ml = 0;
+    uint64_t items_bytes = 0;        // bytes of the work lists (one host->device copy)
+    uint64_t workspace_bytes = 0;
+};
+
+// Validation + planning.  On failure returns a status and sets `err`.
+pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
+               const pa_tensor* blockTables, const pa_tensor* mask,
+               const pa_tensor* seqLen, const pa_tensor* kvSeqLen, const pa_tensor* slopes,
+               int maskType, int32_t headNum, int32_t kvHeadNum, float qkScale,
+               const pa_tensor* keyAntiquantScale, const pa_tensor* valueAntiquantScale,
+               const pa_tensor* attnOut, const pa_tensor* lse, Plan& p, std::string& err);
+
+}  // namespace pa

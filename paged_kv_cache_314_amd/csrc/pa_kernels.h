@@ -1,0 +1,80 @@
+// Kernel argument blocks and launchers (host side of the HIP kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+struct DecodeArgs {
+    const DecodeItem* items;
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* table;
+    void* out;
+    float* lse;
+    const float* slopes;
+    const void* kscale;
+    const void* vscale;
+    float* part_o;          // [slots][min(group,16)][D] un-normalised partial outputs
+    float* part_ml;         // [slots][min(group,16)][2] partial (max, sum), log2 units
+    int64_t q_tok_stride, q_head_stride, out_tok_stride, out_head_stride, lse_tok_stride;
+    int64_t k_blk_stride, k_slot_stride, k_head_stride;
+    int64_t v_blk_stride, v_slot_stride, v_head_stride, table_stride;
+    int32_t group;          // headNum / kvHeadNum
+    int32_t block_size;
+    int32_t mask_type;
+    int32_t scale_is_f32;   // antiquant scales are f32 (else the query dtype)
+    float scale_log2;       // qkScale * log2(e)
+};
+
+struct CombineArgs {
+    const CombineItem* items;
+    const float* part_o;
+    const float* part_ml;
+    void* out;
+    float* lse;
+    int64_t out_tok_stride, out_head_stride, lse_tok_stride;
+    int32_t group;
+};
+
+struct PrefillArgs {
+    const PrefillItem* items;
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* table;
+    void* out;
+    float* lse;
+    const float* slopes;
+    const void* kscale;
+    const void* vscale;
+    int64_t q_tok_stride, q_head_stride, out_tok_stride, out_head_stride, lse_tok_stride;
+    int64_t k_blk_stride, k_slot_stride, k_head_stride;
+    int64_t v_blk_stride, v_slot_stride, v_head_stride, table_stride;
+    int32_t group;
+    int32_t block_size;
+    int32_t mask_type;
+    int32_t scale_is_f32;
+    float scale_log2;
+};
+
+struct FillArgs {
+    void* out;
+    float* lse;
+    int64_t n_tokens, head_num, head_size;
+    int64_t out_tok_stride, out_head_stride, lse_tok_stride;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int n_items, int head_size, bool bf16, bool i8,
+                         hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int n_items, int head_size, bool bf16,
+                          hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int n_items, int head_size, bool bf16, bool i8,
+                          hipStream_t stream);
+hipError_t launch_fill(const FillArgs& a, hipStream_t stream);
+
+}  // namespace pa

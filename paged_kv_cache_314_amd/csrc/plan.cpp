@@ -1,0 +1,522 @@
+// Phase 1: argument validation and work planning.  No HIP calls, no device memory:
+// runs (and is unit-tested) on a machine without a GPU.
+//
+// Checks follow the pages where they state one (PrefixEncoder, Members; the constraint
+// sections of aclnnFusedInferAttentionScoreV3/V4); each message names the argument.
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <sstream>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+struct Fail {
+    pa_status status;
+    std::string msg;
+};
+
+int64_t numel(const pa_tensor* t) {
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+    return n;
+}
+
+int elem_bytes(int32_t dt) {
+    switch (dt) {
+        case PA_F16:
+        case PA_BF16: return 2;
+        case PA_I8: return 1;
+        case PA_F32:
+        case PA_I32: return 4;
+        default: return 0;
+    }
+}
+
+const char* dtype_name(int32_t dt) {
+    switch (dt) {
+        case PA_F16: return "f16";
+        case PA_BF16: return "bf16";
+        case PA_I8: return "i8";
+        case PA_F32: return "f32";
+        case PA_I32: return "i32";
+        default: return "?";
+    }
+}
+
+#define REQUIRE(cond, st, text)                     \
+    do {                                            \
+        if (!(cond)) {                              \
+            std::ostringstream os_;                 \
+            os_ << text;                            \
+            throw Fail{st, os_.str()};              \
+        }                                           \
+    } while (0)
+
+void check_desc(const pa_tensor* t, const char* name) {
+    REQUIRE(t->ndim >= 1 && t->ndim <= 4, PA_ERR_PARAM_INVALID,
+            name << ": ndim " << t->ndim << " not in [1, 4]");
+    for (int i = 0; i < t->ndim; ++i)
+        REQUIRE(t->shape[i] >= 0, PA_ERR_PARAM_INVALID, name << ": negative shape[" << i << "]");
+    REQUIRE(elem_bytes(t->dtype) > 0, PA_ERR_PARAM_INVALID, name << ": unknown dtype " << t->dtype);
+}
+
+// Contiguous in the C sense (strides of a dense row-major array), ignoring size-1 dims.
+bool is_contiguous(const pa_tensor* t) {
+    int64_t expect = 1;
+    for (int i = t->ndim - 1; i >= 0; --i) {
+        if (t->shape[i] != 1 && t->stride[i] != expect) return false;
+        expect *= t->shape[i];
+    }
+    return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [rows, heads, headSize] view of a query/out-like tensor (3-D, or 2-D with heads folded).
+struct RowView {
+    int64_t rows = 0, heads = 0, d = 0;
+    int64_t row_stride = 0, head_stride = 0;
+};
+
+RowView row_view(const pa_tensor* t, const char* name, int64_t heads) {
+    RowView v;
+    if (t->ndim == 3) {
+        REQUIRE(t->shape[1] == heads, PA_ERR_PARAM_INVALID,
+                name << ": shape[1] = " << t->shape[1] << " but headNum = " << heads);
+        REQUIRE(t->stride[2] == 1 || t->shape[2] == 1, PA_ERR_PARAM_INVALID,
+                name << ": last dimension must be contiguous");
+        v.rows = t->shape[0];
+        v.heads = heads;
+        v.d = t->shape[2];
+        v.row_stride = t->stride[0];
+        v.head_stride = t->stride[1];
+    } else if (t->ndim == 2) {
+        REQUIRE(heads > 0 && t->shape[1] % heads == 0, PA_ERR_PARAM_INVALID,
+                name << ": hidden size " << t->shape[1] << " not divisible by headNum " << heads);
+        REQUIRE(t->stride[1] == 1 || t->shape[1] == 1, PA_ERR_PARAM_INVALID,
+                name << ": last dimension must be contiguous");
+        v.rows = t->shape[0];
+        v.heads = heads;
+        v.d = t->shape[1] / heads;
+        v.row_stride = t->stride[0];
+        v.head_stride = v.d;
+    } else {
+        REQUIRE(false, PA_ERR_PARAM_INVALID,
+                name << ": expected [nTokens, headNum, headSize] or [nTokens, headNum*headSize]");
+    }
+    return v;
+}
+
+// [blocks, slots, kvHeads, headSize] view of the paged key/value pool.
+struct PoolView {
+    int64_t blocks = 0, slots = 0, heads = 0, d = 0;
+    int64_t blk_stride = 0, slot_stride = 0, head_stride = 0;
+};
+
+PoolView pool_view(const pa_tensor* t, const char* name, int64_t kv_heads) {
+    PoolView v;
+    if (t->ndim == 4) {
+        REQUIRE(t->shape[2] == kv_heads, PA_ERR_PARAM_INVALID,
+                name << ": shape[2] = " << t->shape[2] << " but kvHeadNum = " << kv_heads);
+        REQUIRE(t->stride[3] == 1 || t->shape[3] == 1, PA_ERR_PARAM_INVALID,
+                name << ": last dimension must be contiguous");
+        v.blocks = t->shape[0];
+        v.slots = t->shape[1];
+        v.heads = kv_heads;
+        v.d = t->shape[3];
+        v.blk_stride = t->stride[0];
+        v.slot_stride = t->stride[1];
+        v.head_stride = t->stride[2];
+    } else if (t->ndim == 3) {
+        REQUIRE(kv_heads > 0 && t->shape[2] % kv_heads == 0, PA_ERR_PARAM_INVALID,
+                name << ": kv hidden " << t->shape[2] << " not divisible by kvHeadNum " << kv_heads);
+        REQUIRE(t->stride[2] == 1 || t->shape[2] == 1, PA_ERR_PARAM_INVALID,
+                name << ": last dimension must be contiguous");
+        v.blocks = t->shape[0];
+        v.slots = t->shape[1];
+        v.heads = kv_heads;
+        v.d = t->shape[2] / kv_heads;
+        v.blk_stride = t->stride[0];
+        v.slot_stride = t->stride[1];
+        v.head_stride = v.d;
+    } else {
+        REQUIRE(false, PA_ERR_PARAM_INVALID,
+                name << ": expected [numBlocks, blockSize, kvHeadNum, headSize] or "
+                        "[numBlocks, blockSize, kvHeadNum*headSize]");
+    }
+    return v;
+}
+
+int env_int(const char* name, int fallback) {
+    const char* s = std::getenv(name);
+    if (s == nullptr || *s == 0) return fallback;
+    char* end = nullptr;
+    long v = std::strtol(s, &end, 10);
+    if (end == s || v <= 0 || v > (1 << 20)) return fallback;
+    return static_cast<int>(v);
+}
+
+uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
+void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
+               const pa_tensor* blockTables, const pa_tensor* mask, const pa_tensor* seqLen,
+               const pa_tensor* kvSeqLen, const pa_tensor* slopes, int maskType,
+               int32_t headNum, int32_t kvHeadNum, float qkScale,
+               const pa_tensor* keyScale, const pa_tensor* valueScale,
+               const pa_tensor* attnOut, const pa_tensor* lse, Plan& p) {
+    // -- required descriptors (aclnnFusedInferAttentionScoreV3, Constraints: null inputs)
+    REQUIRE(query, PA_ERR_NULLPTR, "query is NULL");
+    REQUIRE(key, PA_ERR_NULLPTR, "key is NULL");
+    REQUIRE(value, PA_ERR_NULLPTR, "value is NULL");
+    REQUIRE(blockTables, PA_ERR_NULLPTR, "blockTables is NULL");
+    REQUIRE(seqLen, PA_ERR_NULLPTR, "seqLen is NULL");
+    REQUIRE(kvSeqLen, PA_ERR_NULLPTR, "kvSeqLen is NULL");
+    REQUIRE(attnOut, PA_ERR_NULLPTR, "attnOut is NULL");
+    check_desc(query, "query");
+    check_desc(attnOut, "attnOut");
+    REQUIRE(headNum > 0, PA_ERR_PARAM_INVALID, "headNum must be > 0, got " << headNum);
+    REQUIRE(kvHeadNum >= 0, PA_ERR_PARAM_INVALID, "kvHeadNum must be >= 0, got " << kvHeadNum);
+    const int32_t kvh_num = kvHeadNum == 0 ? headNum : kvHeadNum;
+
+    // -- empty query/out: nothing to do, verification skipped
+    //    (aclnnFusedInferAttentionScoreV4, Constraints, processing when empty)
+    if (numel(query) == 0 && numel(attnOut) == 0) {
+        p.mode = Mode::kNoop;
+        return;
+    }
+
+    REQUIRE(query->dtype == PA_F16 || query->dtype == PA_BF16, PA_ERR_PARAM_INVALID,
+            "query dtype must be f16 or bf16, got " << dtype_name(query->dtype));
+    REQUIRE(attnOut->dtype == query->dtype, PA_ERR_PARAM_INVALID,
+            "attnOut dtype " << dtype_name(attnOut->dtype) << " differs from query "
+                             << dtype_name(query->dtype));
+    const RowView qv = row_view(query, "query", headNum);
+    const RowView ov = row_view(attnOut, "attnOut", headNum);
+    REQUIRE(qv.rows == ov.rows && qv.d == ov.d, PA_ERR_PARAM_INVALID,
+            "attnOut shape differs from query shape");
+    REQUIRE(qv.rows > 0 && qv.d > 0, PA_ERR_PARAM_INVALID,
+            "query has zero elements but attnOut does not (or the reverse)");
+    REQUIRE(ov.row_stride >= ov.heads * ov.d || ov.rows == 1, PA_ERR_PARAM_INVALID,
+            "attnOut rows overlap (token stride " << ov.row_stride << ")");
+    REQUIRE(std::llabs(ov.head_stride) >= ov.d || ov.heads == 1, PA_ERR_PARAM_INVALID,
+            "attnOut heads overlap (head stride " << ov.head_stride << ")");
+
+    p.qtype = static_cast<pa_dtype>(query->dtype);
+    p.head_num = headNum;
+    p.kv_head_num = kvh_num;
+    p.head_size = static_cast<int32_t>(qv.d);
+    p.n_tokens = static_cast<int32_t>(qv.rows);
+    p.q = query->data;
+    p.out = attnOut->data;
+    p.q_tok_stride = qv.row_stride;
+    p.q_head_stride = qv.head_stride;
+    p.out_tok_stride = ov.row_stride;
+    p.out_head_stride = ov.head_stride;
+    REQUIRE(qv.rows < (int64_t(1) << 31), PA_ERR_UNSUPPORTED, "nTokens >= 2^31");
+    REQUIRE(query->data != nullptr, PA_ERR_NULLPTR, "query->data is NULL");
+    REQUIRE(attnOut->data != nullptr, PA_ERR_NULLPTR, "attnOut->data is NULL");
+
+    if (lse) {
+        check_desc(lse, "lse");
+        REQUIRE(lse->dtype == PA_F32, PA_ERR_PARAM_INVALID,
+                "lse dtype must be f32, got " << dtype_name(lse->dtype));
+        const bool shape_ok = (lse->ndim == 2 || (lse->ndim == 3 && lse->shape[2] == 1)) &&
+                              lse->shape[0] == qv.rows && lse->shape[1] == headNum;
+        REQUIRE(shape_ok, PA_ERR_PARAM_INVALID, "lse must be [nTokens, headNum] (or [.., .., 1])");
+        REQUIRE(lse->stride[1] == 1 || headNum == 1, PA_ERR_PARAM_INVALID,
+                "lse head dimension must be contiguous");
+        REQUIRE(lse->stride[0] >= headNum || qv.rows == 1, PA_ERR_PARAM_INVALID,
+                "lse rows overlap");
+        REQUIRE(lse->data != nullptr, PA_ERR_NULLPTR, "lse->data is NULL");
+        p.lse = static_cast<float*>(lse->data);
+        p.lse_tok_stride = lse->stride[0];
+    }
+
+    // -- empty key/value: out = 0, lse = +inf, verification skipped
+    check_desc(key, "key");
+    check_desc(value, "value");
+    if (numel(key) == 0 || numel(value) == 0) {
+        p.mode = Mode::kFill;
+        return;
+    }
+
+    // ------------------------------------------------------------ full checks
+    REQUIRE(mask == nullptr, PA_ERR_UNSUPPORTED,
+            "mask tensors are not supported; maskType 3 builds the ALiBi bias from slopes");
+    REQUIRE(maskType == PA_MASK_NONE || maskType == PA_MASK_CAUSAL || maskType == PA_MASK_ALIBI ||
+                maskType == PA_MASK_ALIBI_SQRT || maskType == PA_MASK_ALIBI_LEFT_ALIGN,
+            PA_ERR_PARAM_INVALID, "maskType " << maskType << " is not 0, 3, 4, 5 or 9");
+    REQUIRE(maskType != PA_MASK_ALIBI_SQRT && maskType != PA_MASK_ALIBI_LEFT_ALIGN,
+            PA_ERR_UNSUPPORTED, "maskType " << maskType << " (ALiBi sqrt / left-align) is not implemented");
+    REQUIRE(std::isfinite(qkScale), PA_ERR_PARAM_INVALID, "qkScale must be finite");
+    REQUIRE(headNum % kvh_num == 0, PA_ERR_PARAM_INVALID,
+            "headNum " << headNum << " is not a multiple of kvHeadNum " << kvh_num);
+    REQUIRE(qv.d == 64 || qv.d == 128, PA_ERR_UNSUPPORTED,
+            "headSize " << qv.d << " not supported (64 or 128)");
+
+    // key / value
+    const bool kv_i8 = key->dtype == PA_I8;
+    REQUIRE(key->dtype == query->dtype || kv_i8, PA_ERR_PARAM_INVALID,
+            "key dtype " << dtype_name(key->dtype) << " must equal the query dtype or be i8");
+    REQUIRE(value->dtype == key->dtype, PA_ERR_PARAM_INVALID, "value dtype differs from key dtype");
+    const PoolView kv = pool_view(key, "key", kvh_num);
+    const PoolView vv = pool_view(value, "value", kvh_num);
+    REQUIRE(key->ndim == value->ndim, PA_ERR_PARAM_INVALID, "key and value shapes differ");
+    for (int i = 0; i < key->ndim; ++i)
+        REQUIRE(key->shape[i] == value->shape[i], PA_ERR_PARAM_INVALID, "key and value shapes differ");
+    REQUIRE(kv.d == qv.d, PA_ERR_PARAM_INVALID,
+            "key headSize " << kv.d << " differs from query headSize " << qv.d);
+    const int64_t bs = kv.slots;
+    const int64_t bs_align = kv_i8 ? 32 : 16;   // aclnnFusedInferAttentionScoreV3: 16 (f16/bf16), 32 (int8)
+    REQUIRE(bs > 0 && bs % bs_align == 0, PA_ERR_PARAM_INVALID,
+            "blockSize " << bs << " must be a positive multiple of " << bs_align);
+    REQUIRE(bs <= 4096, PA_ERR_UNSUPPORTED, "blockSize " << bs << " > 4096");
+    REQUIRE(key->data != nullptr && value->data != nullptr, PA_ERR_NULLPTR, "key/value data is NULL");
+
+    // scales (int8 only)
+    if (kv_i8) {
+        REQUIRE(keyScale != nullptr && valueScale != nullptr, PA_ERR_NULLPTR,
+                "int8 key/value need keyAntiquantScale and valueAntiquantScale");
+        check_desc(keyScale, "keyAntiquantScale");
+        check_desc(valueScale, "valueAntiquantScale");
+        for (const pa_tensor* s : {keyScale, valueScale}) {
+            REQUIRE(numel(s) == kvh_num * qv.d, PA_ERR_PARAM_INVALID,
+                    "antiquant scale must hold kvHeadNum*headSize = " << kvh_num * qv.d
+                                                                     << " elements, got " << numel(s));
+            REQUIRE(is_contiguous(s), PA_ERR_PARAM_INVALID, "antiquant scale must be contiguous");
+            REQUIRE(s->dtype == PA_F32 || s->dtype == query->dtype, PA_ERR_PARAM_INVALID,
+                    "antiquant scale dtype must be f32 or the query dtype");
+            REQUIRE(s->data != nullptr, PA_ERR_NULLPTR, "antiquant scale data is NULL");
+        }
+        REQUIRE(keyScale->dtype == valueScale->dtype, PA_ERR_PARAM_INVALID,
+                "key and value antiquant scales differ in dtype");
+        p.kscale = keyScale->data;
+        p.vscale = valueScale->data;
+        p.scale_type = static_cast<pa_dtype>(keyScale->dtype);
+    } else {
+        REQUIRE(keyScale == nullptr && valueScale == nullptr, PA_ERR_PARAM_INVALID,
+                "antiquant scales given for non-int8 key/value");
+    }
+
+    // alignment of every vector access: 16-byte rows
+    const int eb_q = 2, eb_kv = kv_i8 ? 1 : 2;
+    REQUIRE(aligned16(query->data) && aligned16(attnOut->data) && aligned16(key->data) &&
+                aligned16(value->data),
+            PA_ERR_PARAM_INVALID, "query/attnOut/key/value data must be 16-byte aligned");
+    auto mult16 = [](int64_t stride, int eb) { return (stride * eb) % 16 == 0; };
+    REQUIRE(mult16(qv.row_stride, eb_q) && mult16(qv.head_stride, eb_q) &&
+                mult16(ov.row_stride, eb_q) && mult16(ov.head_stride, eb_q),
+            PA_ERR_PARAM_INVALID, "query/attnOut strides must be multiples of 16 bytes");
+    REQUIRE(mult16(kv.blk_stride, eb_kv) && mult16(kv.slot_stride, eb_kv) &&
+                mult16(kv.head_stride, eb_kv) && mult16(vv.blk_stride, eb_kv) &&
+                mult16(vv.slot_stride, eb_kv) && mult16(vv.head_stride, eb_kv),
+            PA_ERR_PARAM_INVALID, "key/value strides must be multiples of 16 bytes");
+
+    // lengths (host)
+    check_desc(seqLen, "seqLen");
+    check_desc(kvSeqLen, "kvSeqLen");
+    REQUIRE(seqLen->dtype == PA_I32 && kvSeqLen->dtype == PA_I32, PA_ERR_PARAM_INVALID,
+            "seqLen and kvSeqLen must be int32");
+    REQUIRE(seqLen->ndim == 1 && kvSeqLen->ndim == 1, PA_ERR_PARAM_INVALID,
+            "seqLen and kvSeqLen must be 1-D");
+    const int64_t B = seqLen->shape[0];
+    REQUIRE(kvSeqLen->shape[0] == B, PA_ERR_PARAM_INVALID,
+            "seqLen has " << B << " entries, kvSeqLen " << kvSeqLen->shape[0]);
+    REQUIRE(B > 0, PA_ERR_PARAM_INVALID, "batch must be > 0");
+    REQUIRE(seqLen->data != nullptr && kvSeqLen->data != nullptr, PA_ERR_NULLPTR,
+            "seqLen/kvSeqLen data is NULL");
+    const int32_t* ql = static_cast<const int32_t*>(seqLen->data);
+    const int32_t* kl = static_cast<const int32_t*>(kvSeqLen->data);
+    const int64_t qls = seqLen->stride[0], kls = kvSeqLen->stride[0];
+    int64_t qsum = 0, need_blocks = 0, max_blocks = 0;
+    int32_t max_q = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t q = ql[b * qls], k = kl[b * kls];
+        REQUIRE(q >= 0, PA_ERR_PARAM_INVALID, "seqLen[" << b << "] = " << q << " < 0");
+        REQUIRE(k >= 0, PA_ERR_PARAM_INVALID, "kvSeqLen[" << b << "] = " << k << " < 0");
+        qsum += q;
+        max_q = std::max(max_q, q);
+        const int64_t nb = (k + bs - 1) / bs;
+        need_blocks += nb;
+        max_blocks = std::max(max_blocks, nb);
+    }
+    REQUIRE(qsum == qv.rows, PA_ERR_PARAM_INVALID,
+            "sum(seqLen) = " << qsum << " but query has " << qv.rows << " rows");
+
+    // block table (aclnnFusedInferAttentionScoreV3, Constraints, paged attention scenario)
+    check_desc(blockTables, "blockTables");
+    REQUIRE(blockTables->dtype == PA_I32, PA_ERR_PARAM_INVALID, "blockTables must be int32");
+    REQUIRE(blockTables->ndim == 2, PA_ERR_PARAM_INVALID, "blockTables must be 2-D");
+    REQUIRE(blockTables->shape[0] == B, PA_ERR_PARAM_INVALID,
+            "blockTables has " << blockTables->shape[0] << " rows, batch is " << B);
+    REQUIRE(blockTables->shape[1] >= max_blocks, PA_ERR_PARAM_INVALID,
+            "blockTables has " << blockTables->shape[1] << " columns, a sequence needs " << max_blocks);
+    REQUIRE(blockTables->stride[1] == 1 || blockTables->shape[1] <= 1, PA_ERR_PARAM_INVALID,
+            "blockTables columns must be contiguous");
+    REQUIRE(kv.blocks >= need_blocks, PA_ERR_PARAM_INVALID,
+            "numBlocks " << kv.blocks << " < blocks the sequences need (" << need_blocks << ")");
+    REQUIRE(blockTables->data != nullptr || max_blocks == 0, PA_ERR_NULLPTR, "blockTables data is NULL");
+
+    // slopes
+    if (maskType == PA_MASK_ALIBI) {
+        REQUIRE(slopes != nullptr, PA_ERR_NULLPTR, "maskType 3 (ALiBi) needs slopes");
+        check_desc(slopes, "slopes");
+        REQUIRE(slopes->dtype == PA_F32, PA_ERR_PARAM_INVALID, "slopes must be f32");
+        REQUIRE(numel(slopes) == headNum && is_contiguous(slopes), PA_ERR_PARAM_INVALID,
+                "slopes must be a contiguous [headNum] tensor");
+        REQUIRE(slopes->data != nullptr, PA_ERR_NULLPTR, "slopes data is NULL");
+        p.slopes = static_cast<const float*>(slopes->data);
+    } else {
+        REQUIRE(slopes == nullptr, PA_ERR_PARAM_INVALID, "slopes given but maskType is not 3");
+    }
+
+    // ------------------------------------------------------------------ plan
+    p.kvtype = static_cast<pa_dtype>(key->dtype);
+    p.batch = static_cast<int32_t>(B);
+    p.group = headNum / kvh_num;
+    p.head_groups = (p.group + kHeadPack - 1) / kHeadPack;
+    p.block_size = static_cast<int32_t>(bs);
+    p.num_blocks = static_cast<int32_t>(std::min<int64_t>(kv.blocks, INT32_MAX));
+    p.mask_type = maskType;
+    p.qk_scale = qkScale;
+    p.k = key->data;
+    p.v = value->data;
+    p.table = static_cast<const int32_t*>(blockTables->data);
+    p.table_stride = blockTables->stride[0];
+    p.k_blk_stride = kv.blk_stride;
+    p.k_slot_stride = kv.slot_stride;
+    p.k_head_stride = kv.head_stride;
+    p.v_blk_stride = vv.blk_stride;
+    p.v_slot_stride = vv.slot_stride;
+    p.v_head_stride = vv.head_stride;
+
+    std::vector<int32_t> q0(B + 1, 0);
+    for (int64_t b = 0; b < B; ++b) q0[b + 1] = q0[b] + ql[b * qls];
+
+    uint64_t off = 0;
+    if (max_q <= 1) {
+        // ---- decode: split each (sequence, kv head, head group) into tile ranges
+        p.mode = Mode::kDecode;
+        int64_t total_tiles = 0;
+        for (int64_t b = 0; b < B; ++b)
+            if (ql[b * qls] == 1) total_tiles += (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
+        total_tiles *= static_cast<int64_t>(kvh_num) * p.head_groups;
+        const int target = env_int("PA_DECODE_TARGET_ITEMS", 2048);
+        int chunk = static_cast<int>(std::min<int64_t>((total_tiles + target - 1) / target, 1 << 20));
+        chunk = std::max(chunk, 8);
+        chunk = (chunk + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
+        chunk = env_int("PA_DECODE_CHUNK_TILES", chunk);
+        p.decode_chunk_tiles = chunk;
+        int32_t slots = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            if (ql[b * qls] != 1) continue;
+            const int32_t klen = kl[b * kls];
+            const int32_t tiles = (klen + kDecodeTile - 1) / kDecodeTile;
+            const int32_t nsplit = std::max<int32_t>(1, (tiles + chunk - 1) / chunk);
+            for (int32_t h = 0; h < kvh_num; ++h) {
+                for (int32_t hg = 0; hg < p.head_groups; ++hg) {
+                    const int32_t slot0 = nsplit > 1 ? slots : -1;
+                    for (int32_t s = 0; s < nsplit; ++s) {
+                        DecodeItem it{};
+                        it.b = static_cast<int32_t>(b);
+                        it.kvh = h;
+                        it.hg = hg;
+                        it.t0 = static_cast<int32_t>(int64_t(tiles) * s / nsplit);
+                        it.t1 = static_cast<int32_t>(int64_t(tiles) * (s + 1) / nsplit);
+                        it.slot = nsplit > 1 ? slot0 + s : -1;
+                        it.qrow = q0[b];
+                        it.kvlen = klen;
+                        p.decode_items.push_back(it);
+                    }
+                    if (nsplit > 1) {
+                        CombineItem c{};
+                        c.kvh = h;
+                        c.hg = hg;
+                        c.slot0 = slot0;
+                        c.nsplit = nsplit;
+                        c.qrow = q0[b];
+                        p.combine_items.push_back(c);
+                        slots += nsplit;
+                    }
+                }
+            }
+        }
+        p.partial_slots = slots;
+        const int64_t geff = std::min<int32_t>(p.group, kHeadPack);
+        p.off_items = 0;
+        off = align256(p.decode_items.size() * sizeof(DecodeItem));
+        p.off_combine = off;
+        off = align256(off + p.combine_items.size() * sizeof(CombineItem));
+        p.items_bytes = off;
+        p.off_part_o = off;
+        off = align256(off + uint64_t(slots) * geff * qv.d * sizeof(float));
+        p.off_part_ml = off;
+        off = align256(off + uint64_t(slots) * geff * 2 * sizeof(float));
+        p.workspace_bytes = off;
+    } else {
+        // ---- prefill: (sequence, head, 128-row query tile) items, heaviest first
+        p.mode = Mode::kPrefill;
+        const bool causal = maskType == PA_MASK_CAUSAL || maskType == PA_MASK_ALIBI;
+        for (int64_t b = 0; b < B; ++b) {
+            const int32_t qlen = ql[b * qls], klen = kl[b * kls];
+            for (int32_t qb = 0; qb < qlen; qb += kPrefillBM) {
+                int64_t last_key;   // last key index any row of the tile can see
+                if (causal) {
+                    const int64_t last_row = std::min<int64_t>(qb + kPrefillBM, qlen) - 1;
+                    last_key = std::min<int64_t>(int64_t(klen) - qlen + last_row, int64_t(klen) - 1);
+                } else {
+                    last_key = int64_t(klen) - 1;
+                }
+                const int32_t ktiles =
+                    last_key < 0 ? 0 : static_cast<int32_t>((last_key + kPrefillBN) / kPrefillBN);
+                for (int32_t h = 0; h < headNum; ++h) {
+                    PrefillItem it{};
+                    it.b = static_cast<int32_t>(b);
+                    it.h = h;
+                    it.qbeg = qb;
+                    it.qlen = qlen;
+                    it.kvlen = klen;
+                    it.qrow0 = q0[b];
+                    it.ktiles = ktiles;
+                    p.prefill_items.push_back(it);
+                }
+            }
+        }
+        std::stable_sort(p.prefill_items.begin(), p.prefill_items.end(),
+                         [](const PrefillItem& x, const PrefillItem& y) { return x.ktiles > y.ktiles; });
+        p.off_items = 0;
+        off = align256(p.prefill_items.size() * sizeof(PrefillItem));
+        p.items_bytes = off;
+        p.workspace_bytes = off;
+    }
+}
+
+}  // namespace
+
+pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
+               const pa_tensor* blockTables, const pa_tensor* mask, const pa_tensor* seqLen,
+               const pa_tensor* kvSeqLen, const pa_tensor* slopes, int maskType,
+               int32_t headNum, int32_t kvHeadNum, float qkScale,
+               const pa_tensor* keyAntiquantScale, const pa_tensor* valueAntiquantScale,
+               const pa_tensor* attnOut, const pa_tensor* lse, Plan& p, std::string& err) {
+    try {
+        plan_impl(query, key, value, blockTables, mask, seqLen, kvSeqLen, slopes, maskType,
+                  headNum, kvHeadNum, qkScale, keyAntiquantScale, valueAntiquantScale, attnOut,
+                  lse, p);
+    } catch (const Fail& f) {
+        err = f.msg;
+        return f.status;
+    } catch (const std::bad_alloc&) {
+        err = "host allocation failed while planning";
+        return PA_ERR_HOST_ALLOC;
+    }
+    err.clear();
+    return PA_OK;
+}
+
+}  // namespace pa

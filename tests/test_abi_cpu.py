@@ -1,0 +1,400 @@
+"""CPU tests of the C ABI: symbols, phase-1 validation and planning.
+
+Phase 1 (pa_paged_attention_get_workspace_size) makes no HIP call and never
+dereferences device pointers, so these tests hand it descriptors with fake,
+aligned device addresses and real host length arrays.  Phase 2 is only called
+on paths that return before any HIP call (NULL op, short workspace, no-op op).
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_314_amd as pa
+from paged_kv_cache_314_amd import workloads as wl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "pagedattn.h")
+FAKE = 0x7f0000000000          # 256-aligned fake device address (never dereferenced)
+ESZ = {pa.PA_F16: 2, pa.PA_BF16: 2, pa.PA_I8: 1, pa.PA_F32: 4, pa.PA_I32: 4}
+
+
+def desc(shape, dtype, ptr=FAKE, strides=None):
+    d = pa.PaTensor()
+    d.data = ptr
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+def host_i32(values):
+    arr = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    d = desc([arr.shape[0]], pa.PA_I32, ptr=arr.ctypes.data)
+    return d, arr
+
+
+class Case:
+    """Descriptor set for one phase-1 call; fields can be overridden per test."""
+
+    def __init__(self, *, q_lens, kv_lens, H, Hkv, D, bs, dtype=pa.PA_BF16, kv_dtype=None,
+                 mask=pa.PA_MASK_NONE, lse=True, num_blocks=None, width=None):
+        kv_dtype = kv_dtype or dtype
+        T = int(sum(q_lens))
+        need = sum(-(-k // bs) for k in kv_lens)
+        nb = need if num_blocks is None else num_blocks
+        W = max([-(-k // bs) for k in kv_lens] + [1]) if width is None else width
+        self.query = desc([T, H, D], dtype)
+        self.key = desc([nb, bs, Hkv, D], kv_dtype)
+        self.value = desc([nb, bs, Hkv, D], kv_dtype)
+        self.table = desc([len(q_lens), W], pa.PA_I32)
+        self.mask = None
+        self.seq_len, self._ql = host_i32(q_lens)
+        self.kv_seq_len, self._kl = host_i32(kv_lens)
+        self.slopes = desc([H], pa.PA_F32) if mask == pa.PA_MASK_ALIBI else None
+        self.mask_type = mask
+        self.H, self.Hkv, self.scale = H, Hkv, 1.0 / math.sqrt(D)
+        self.kscale = desc([Hkv, D], pa.PA_F32) if kv_dtype == pa.PA_I8 else None
+        self.vscale = desc([Hkv, D], pa.PA_F32) if kv_dtype == pa.PA_I8 else None
+        self.out = desc([T, H, D], dtype)
+        self.lse = desc([T, H], pa.PA_F32) if lse else None
+
+    def call(self):
+        lib = pa.load()
+        ws = ctypes.c_uint64(123)
+        op = ctypes.c_void_p(None)
+        r = lambda d: ctypes.byref(d) if d is not None else None
+        st = lib.pa_paged_attention_get_workspace_size(
+            r(self.query), r(self.key), r(self.value), r(self.table), r(self.mask),
+            r(self.seq_len), r(self.kv_seq_len), r(self.slopes), self.mask_type, self.H,
+            self.Hkv, self.scale, r(self.kscale), r(self.vscale), r(self.out), r(self.lse),
+            ctypes.byref(ws), ctypes.byref(op))
+        return st, int(ws.value), op.value
+
+    def plan(self):
+        st, ws, op = self.call()
+        assert st == pa.PA_OK, pa.pa_last_error()
+        info = pa.pa_op_describe(op)
+        assert info["workspace_bytes"] == ws
+        pa.pa_op_destroy(op)
+        return info
+
+
+# --------------------------------------------------------------- symbols
+
+def test_library_exports_every_header_symbol():
+    with open(HEADER) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\S.*?\b(pa_\w+)\s*\(", text, flags=re.M))
+    assert declared == set(pa.EXPORTED)
+    lib = pa.load()
+    for name in declared:
+        assert getattr(lib, name) is not None
+    assert pa.pa_version() >= 100
+    for st in range(7):
+        assert pa.pa_status_string(st)
+
+
+# ---------------------------------------------------------------- planning
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_plan_for_named_workloads(name):
+    w = wl.WORKLOADS[name]
+    rng = np.random.default_rng([314, w.index, 1])
+    if isinstance(w.kv_seq_len, tuple):
+        kv = rng.integers(w.kv_seq_len[1], w.kv_seq_len[2] + 1, size=w.batch).tolist()
+    elif isinstance(w.kv_seq_len, list):
+        kv = w.kv_seq_len
+    else:
+        kv = [w.kv_seq_len] * w.batch
+    ql = [1] * w.batch if w.seq_len == "decode" else [w.seq_len] * w.batch
+    dt = {"f16": pa.PA_F16, "bf16": pa.PA_BF16, "i8": pa.PA_I8}
+    c = Case(q_lens=ql, kv_lens=kv, H=w.head_num, Hkv=w.kv_head_num, D=w.head_size,
+             bs=w.block_size, dtype=dt[w.dtype], kv_dtype=dt[w.kv_dtype], mask=w.mask_type,
+             width=w.table_width)
+    info = c.plan()
+    assert info["mode"] == ("decode" if w.seq_len == "decode" else "prefill")
+    if info["mode"] == "decode":
+        _check_decode_plan(info, ql, kv, w.kv_head_num, w.head_num // w.kv_head_num)
+    else:
+        _check_prefill_plan(info, ql, kv, w.head_num, w.mask_type)
+
+
+def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
+    """Every (sequence, kv head, head group) is covered by tile ranges that partition
+    [0, ceil(kvlen/32)) exactly once; split items own consecutive slots merged by one
+    combine item; single-split items write directly (slot -1)."""
+    n_hg = -(-group // 16)
+    items = info["decode_items"]
+    by_key = {}
+    for b, kvh, hg, t0, t1, slot, qrow, kvlen in items:
+        by_key.setdefault((b, kvh, hg), []).append((t0, t1, slot, qrow, kvlen))
+    q0 = np.concatenate([[0], np.cumsum(q_lens)])
+    combines = {(c[0], c[1], c[4]): c for c in info["combine_items"]}
+    slots_seen = set()
+    for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
+        for kvh in range(Hkv):
+            for hg in range(n_hg):
+                parts = by_key.pop((b, kvh, hg), None) if ql == 1 else None
+                if ql != 1:
+                    assert (b, kvh, hg) not in by_key
+                    continue
+                assert parts, (b, kvh, hg)
+                tiles = -(-kl // 32)
+                cur = 0
+                for t0, t1, slot, qrow, kvlen in parts:
+                    assert t0 == cur and t1 >= t0 and qrow == q0[b] and kvlen == kl
+                    cur = t1
+                assert cur == tiles
+                if len(parts) == 1:
+                    assert parts[0][2] == -1
+                else:
+                    slots = [p[2] for p in parts]
+                    assert slots == list(range(slots[0], slots[0] + len(parts)))
+                    assert not (set(slots) & slots_seen)
+                    slots_seen |= set(slots)
+                    c = combines.pop((kvh, hg, int(q0[b])))
+                    assert c[2] == slots[0] and c[3] == len(parts)
+    assert not by_key and not combines
+    assert info["partial_slots"] == len(slots_seen)
+
+
+def _check_prefill_plan(info, q_lens, kv_lens, H, mask):
+    items = info["prefill_items"]
+    ks = [it[6] for it in items]
+    assert ks == sorted(ks, reverse=True), "heaviest items first"
+    seen = set()
+    q0 = np.concatenate([[0], np.cumsum(q_lens)])
+    for b, h, qbeg, qlen, kvlen, qrow0, ktiles in items:
+        assert (b, h, qbeg) not in seen
+        seen.add((b, h, qbeg))
+        assert qlen == q_lens[b] and kvlen == kv_lens[b] and qrow0 == q0[b]
+        # keys that the tile's rows can see, counted independently
+        rows = range(qbeg, min(qbeg + 128, qlen))
+        if mask in (pa.PA_MASK_CAUSAL, pa.PA_MASK_ALIBI):
+            last = max(kvlen - qlen + i for i in rows)
+        else:
+            last = kvlen - 1
+        want = 0 if last < 0 else last // 64 + 1
+        assert ktiles == want
+    expect = {(b, h, qb) for b, ql in enumerate(q_lens) for h in range(H)
+              for qb in range(0, ql, 128)}
+    assert seen == expect
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_decode_plans(seed):
+    rng = np.random.default_rng([314, 500, seed])
+    B = int(rng.integers(1, 40))
+    kv = rng.integers(0, 20000, size=B).tolist()
+    ql = rng.integers(0, 2, size=B).tolist()
+    if sum(ql) == 0:
+        ql[0] = 1
+    Hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 4, 8, 24]))
+    c = Case(q_lens=ql, kv_lens=kv, H=Hkv * g, Hkv=Hkv, D=128, bs=int(rng.choice([16, 32, 128])))
+    info = c.plan()
+    assert info["mode"] == "decode"
+    _check_decode_plan(info, ql, kv, Hkv, g)
+
+
+@pytest.mark.parametrize("mask", [pa.PA_MASK_NONE, pa.PA_MASK_CAUSAL, pa.PA_MASK_ALIBI])
+def test_random_prefill_plans(mask):
+    rng = np.random.default_rng([314, 501, mask])
+    B = 5
+    ql = [0, 1, 130, 700, 64]
+    kv = [10, 0, 100, 3000, 64]
+    c = Case(q_lens=ql, kv_lens=kv, H=4, Hkv=2, D=64, bs=16, dtype=pa.PA_F16, mask=mask)
+    info = c.plan()
+    assert info["mode"] == "prefill"
+    _check_prefill_plan(info, ql, kv, 4, mask)
+    assert B == len(ql) and rng is not None
+
+
+# -------------------------------------------------------- empty tensors
+
+def test_empty_query_is_noop_and_skips_checks():
+    c = Case(q_lens=[0, 0], kv_lens=[5, 9], H=4, Hkv=4, D=64, bs=16)
+    c.H = 4
+    c.Hkv = 3             # would be invalid, but empty tensors skip verification
+    c.mask_type = 77
+    info = c.plan()
+    assert info["mode"] == "noop" and info["workspace_bytes"] == 0
+
+
+def test_empty_key_value_plans_a_fill():
+    c = Case(q_lens=[1, 1], kv_lens=[5, 9], H=4, Hkv=4, D=64, bs=16)
+    c.key = desc([0, 16, 4, 64], pa.PA_F16)
+    c.value = desc([0, 16, 4, 64], pa.PA_F16)
+    info = c.plan()
+    assert info["mode"] == "fill" and info["workspace_bytes"] == 0
+
+
+# ---------------------------------------------------------- validation
+
+def _expect(c, status, text=None):
+    st, _, op = c.call()
+    assert st == status, (st, pa.pa_last_error())
+    assert op is None
+    if text:
+        assert text in pa.pa_last_error()
+
+
+def base(**kw):
+    args = dict(q_lens=[1, 1], kv_lens=[100, 37], H=8, Hkv=2, D=128, bs=16)
+    args.update(kw)
+    return Case(**args)
+
+
+def test_null_arguments():
+    c = base()
+    c.query = None
+    _expect(c, pa.PA_ERR_NULLPTR, "query")
+    c = base()
+    c.kv_seq_len = None
+    _expect(c, pa.PA_ERR_NULLPTR, "kvSeqLen")
+    lib = pa.load()
+    assert lib.pa_paged_attention_get_workspace_size(
+        *([None] * 8), 0, 1, 1, 1.0, None, None, None, None, None, None) == pa.PA_ERR_NULLPTR
+
+
+def test_head_checks():
+    c = base()
+    c.H = 0
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "headNum")
+    c = base(H=6, Hkv=4)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "multiple")
+    c = base(D=96)
+    _expect(c, pa.PA_ERR_UNSUPPORTED, "headSize")
+
+
+def test_kv_head_num_zero_means_head_num():
+    c = base(H=4, Hkv=4)
+    c.Hkv = 0
+    info = c.plan()
+    assert info["mode"] == "decode"
+    assert {it[1] for it in info["decode_items"]} == {0, 1, 2, 3}
+
+
+def test_mask_checks():
+    for m in (4, 5):
+        c = base()
+        c.mask_type = m
+        _expect(c, pa.PA_ERR_UNSUPPORTED, "maskType")
+    c = base()
+    c.mask_type = 7
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "maskType")
+    c = base()
+    c.mask_type = pa.PA_MASK_ALIBI
+    _expect(c, pa.PA_ERR_NULLPTR, "slopes")
+    c = base()
+    c.slopes = desc([8], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "slopes")
+    c = base(mask=pa.PA_MASK_ALIBI)
+    c.slopes = desc([7], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "slopes")
+    c = base()
+    c.mask = desc([256, 256], pa.PA_F16)
+    _expect(c, pa.PA_ERR_UNSUPPORTED, "mask")
+
+
+def test_length_and_table_checks():
+    c = base()
+    c.seq_len, c._ql = host_i32([1, 2])
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "sum(seqLen)")
+    c = base()
+    c.kv_seq_len, c._kl = host_i32([100, -1])
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "kvSeqLen[1]")
+    c = base(width=6)                       # 100 tokens need 7 blocks of 16
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "columns")
+    c = base(num_blocks=9)                  # need 7 + 3 = 10 blocks
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "numBlocks")
+    c = base(bs=24)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "blockSize")
+    c = base(kv_dtype=pa.PA_I8, bs=16)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "blockSize")   # int8 needs a multiple of 32
+    c = base()
+    c.table = desc([2, 7], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "int32")
+
+
+def test_dtype_and_layout_checks():
+    c = base()
+    c.out = desc([2, 8, 128], pa.PA_F16)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "attnOut dtype")
+    c = base()
+    c.key = desc([10, 16, 2, 128], pa.PA_F16)
+    c.value = desc([10, 16, 2, 128], pa.PA_F16)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "key dtype")
+    c = base(kv_dtype=pa.PA_I8, bs=32)
+    c.kscale = None
+    _expect(c, pa.PA_ERR_NULLPTR, "AntiquantScale")
+    c = base(kv_dtype=pa.PA_I8, bs=32)
+    c.vscale = desc([2, 64], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "elements")
+    c = base()
+    c.kscale = desc([2, 128], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "non-int8")
+    c = base()
+    c.lse = desc([2, 7], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "lse")
+    c = base()
+    c.query = desc([2, 8, 128], pa.PA_BF16, ptr=FAKE + 8)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "aligned")
+    c = base()
+    c.scale = float("nan")
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "qkScale")
+
+
+def test_strided_views_are_accepted():
+    # query as a slice of a fused [T, H + 2*Hkv, D] projection; out heads padded;
+    # key/value as a permuted (numBlocks, kvHeadNum, blockSize, headSize) cache
+    c = base()
+    c.query = desc([2, 8, 128], pa.PA_BF16, strides=[12 * 128, 128, 1])
+    c.out = desc([2, 8, 128], pa.PA_BF16, strides=[8 * 136, 136, 1])
+    c.key = desc([10, 16, 2, 128], pa.PA_BF16, strides=[2 * 16 * 128, 128, 16 * 128, 1])
+    c.value = desc([10, 16, 2, 128], pa.PA_BF16, strides=[2 * 16 * 128, 128, 16 * 128, 1])
+    assert c.plan()["mode"] == "decode"
+    c2 = base()
+    c2.out = desc([2, 8, 128], pa.PA_BF16, strides=[64, 128, 1])
+    _expect(c2, pa.PA_ERR_PARAM_INVALID, "overlap")
+
+
+def test_two_dimensional_forms():
+    c = base()
+    c.query = desc([2, 8 * 128], pa.PA_BF16)
+    c.out = desc([2, 8 * 128], pa.PA_BF16)
+    c.key = desc([10, 16, 2 * 128], pa.PA_BF16)
+    c.value = desc([10, 16, 2 * 128], pa.PA_BF16)
+    assert c.plan()["mode"] == "decode"
+
+
+# ----------------------------------------------- phase 2 without a GPU call
+
+def test_execute_argument_errors():
+    lib = pa.load()
+    assert lib.pa_paged_attention(None, 0, None, None) == pa.PA_ERR_NULLPTR
+    c = base()
+    st, ws, op = c.call()
+    assert st == pa.PA_OK and ws > 0
+    assert lib.pa_paged_attention(FAKE, ws - 1, op, None) == pa.PA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.pa_paged_attention(None, ws, op, None) == pa.PA_ERR_NULLPTR
+    assert lib.pa_paged_attention(FAKE + 16, ws, op, None) == pa.PA_ERR_PARAM_INVALID
+    lib.pa_op_destroy(op)
+    lib.pa_op_destroy(None)
+    c = Case(q_lens=[0], kv_lens=[3], H=2, Hkv=2, D=64, bs=16)
+    st, ws, op = c.call()
+    assert st == pa.PA_OK and ws == 0
+    assert lib.pa_paged_attention(None, 0, op, None) == pa.PA_OK     # no-op, no HIP call
+    lib.pa_op_destroy(op)
