@@ -1,0 +1,292 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-probe MiB]
+
+A step is one execute of the planned operator (pa_paged_attention): the upload of
+the work lists plus every kernel of the path, over one batch of seeded synthetic
+inputs already resident in HBM.  The plan (phase 1) is made once before timing;
+its host time is reported as ``plan_us``.  Prints ONE JSON line.
+
+Default workload: causal prefill, bf16, B=4, seqLen=kvSeqLen=512, H=32, Hkv=8,
+D=128, blockSize=128 ("prefill_causal_bf16").  --workload picks another of the
+named workloads in paged_kv_cache_314_amd.workloads.
+
+Throughput: prefill workloads report algorithmic TFLOP/s (4*D flops per visible
+(query, key) pair, exact causal count); decode workloads report algorithmic GB/s
+(K/V bytes of the valid tokens + Q + out + lse + used block-table entries +
+antiquant scales).  ``roofline`` covers the main kernel alone, timed with HIP
+events recorded on its launch stream around each launch.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense MFMA, published
+KERNEL_SOURCES = {"decode": "decode.hip", "prefill": "prefill.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_causal_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU budget of the oracle baseline sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ counts
+
+def algorithmic_counts(inp):
+    """(bytes, flops) of one step, from the definition of the operation."""
+    import numpy as np
+    q, k = inp["query"], inp["key"]
+    T, H, D = q.shape
+    Hkv = inp["kv_head_num"]
+    bs = k.shape[1]
+    ql = inp["seq_len"].numpy().astype(np.int64)
+    kl = inp["kv_seq_len"].numpy().astype(np.int64)
+    kv_elt = k.element_size()
+    q_elt = q.element_size()
+    causal = inp["mask_type"] in (3, 9)
+    pairs = 0
+    for a, b in zip(ql, kl):
+        if causal:
+            p = b - a + np.arange(a)            # absolute positions
+            pairs += int(np.sum(np.clip(np.minimum(p, b - 1) + 1, 0, None)))
+        else:
+            pairs += int(a * b)
+    flops = 4 * D * H * pairs
+    kv_bytes = int(np.sum(kl)) * Hkv * D * kv_elt * 2
+    qo_bytes = 2 * T * H * D * q_elt
+    lse_bytes = T * H * 4 if inp["want_lse"] else 0
+    table_bytes = int(np.sum((kl + bs - 1) // bs)) * 4
+    scale_bytes = 2 * Hkv * D * 4 if inp.get("key_scale") is not None else 0
+    nbytes = kv_bytes + qo_bytes + lse_bytes + table_bytes + scale_bytes
+    return nbytes, flops
+
+
+def source_hash(kind):
+    path = os.path.join(ROOT, "paged_kv_cache_314_amd", "csrc", KERNEL_SOURCES[kind])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, kind):
+    """HBM bytes per launch measured with rocprofv3 counters, if a summary for this
+    workload exists and was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256_16") != source_hash(kind):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------ cpu baseline
+
+def cpu_baseline(inp, nbytes, flops, decode, budget_s):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
+    whole sequences, one after another, until the time budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    q = inp["query"].double().numpy()
+    if inp["key"].dtype.is_floating_point:
+        k = inp["key"].double().numpy()
+        v = inp["value"].double().numpy()
+        ks = vs = None
+    else:
+        k = inp["key"].numpy()
+        v = inp["value"].numpy()
+        ks = inp["key_scale"].double().numpy()
+        vs = inp["value_scale"].double().numpy()
+    sl = inp["slopes"].double().numpy() if inp["slopes"] is not None else None
+    table = inp["block_tables"].numpy()
+    ql = inp["seq_len"].numpy().astype(np.int64)
+    kl = inp["kv_seq_len"].numpy().astype(np.int64)
+    q0 = np.concatenate([[0], np.cumsum(ql)])
+    H, Hkv = inp["head_num"], inp["kv_head_num"]
+    bs = k.shape[1]
+    done_units = 0.0
+    total_units = 0.0
+    for b in range(len(ql)):
+        total_units += ql[b] * kl[b] if not decode else kl[b]
+    t0 = time.perf_counter()
+    nseq = 0
+    for b in range(len(ql)):
+        kb = oracle.gather_sequence(k, table[b], kl[b], bs)
+        vb = oracle.gather_sequence(v, table[b], kl[b], bs)
+        if ks is not None:
+            kb = oracle.dequantize_per_channel(kb, ks)
+            vb = oracle.dequantize_per_channel(vb, vs)
+        oracle.attention_contiguous(q[q0[b]:q0[b + 1]], kb, vb,
+                                    oracle.query_positions(ql[b], kl[b]), inp["mask_type"],
+                                    inp["qk_scale"], H, Hkv, sl)
+        nseq += 1
+        done_units += ql[b] * kl[b] if not decode else kl[b]
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    frac = done_units / total_units if total_units else 1.0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    if decode:
+        value, unit = nbytes * frac / dt / 1e9, "GB/s"
+    else:
+        value, unit = flops * frac / dt / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{nseq} of {len(ql)} sequences (all heads), {frac:.3f} of the "
+                      f"step's work, {dt:.1f} s, fp64 NumPy, BLAS threads {threads}"}
+
+
+# -------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the hot path is a "
+              "single-GPU kernel and no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_314_amd as pa
+    from paged_kv_cache_314_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": max(args.steps, 1)}))
+        return
+
+    w = wl.WORKLOADS[args.workload]
+    decode = w.seq_len == "decode"
+    kind = "decode" if decode else "prefill"
+    inp = wl.make_inputs(w, poison=False)
+    nbytes, flops = algorithmic_counts(inp)
+    g = {key: (val.to(dev) if isinstance(val, torch.Tensor) and key not in ("seq_len", "kv_seq_len")
+               else val) for key, val in inp.items()}
+    out = torch.empty_like(g["query"])
+    lse = (torch.empty((out.shape[0], w.head_num), dtype=torch.float32, device=dev)
+           if w.lse else None)
+
+    t_plan = time.perf_counter()
+    op = pa.pa_paged_attention_get_workspace_size(
+        g["query"], g["key"], g["value"], g["block_tables"], None, g["seq_len"],
+        g["kv_seq_len"], g["slopes"], g["mask_type"], g["head_num"], g["kv_head_num"],
+        g["qk_scale"], g["key_scale"], g["value_scale"], out, lse)
+    plan_us = (time.perf_counter() - t_plan) * 1e6
+    ws = pa.alloc_workspace(op.workspace_size, dev)
+    info = pa.pa_op_describe(op)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # main-kernel duration: HIP events recorded around each launch on its stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + stops:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for s_ev, e_ev in zip(starts, stops):
+        pa.pa_op_set_timing_events(op, s_ev, e_ev)
+        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+    pa.pa_op_set_timing_events(op, None, None)
+    torch.cuda.synchronize()
+    kms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
+    kernel_ms = sum(kms) / len(kms)
+
+    if decode:
+        value = nbytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+        dtype = "f16" if w.kv_dtype == "i8" else w.dtype
+    else:
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        peak = PEAK_MFMA_TFLOPS[w.dtype]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+        dtype = w.dtype
+    roof["traffic"] = traffic_from_profiles(args.workload, kind)
+    roof["kernel"] = f"{kind}_kernel"
+    roof["kernel_us"] = kernel_ms * 1e3
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, nbytes, flops, decode, args.cpu_seconds)
+
+    result = {
+        "metric": "decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), paged attention",
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "mode": kind, "batch": w.batch,
+            "head_num": w.head_num, "kv_head_num": w.kv_head_num, "head_size": w.head_size,
+            "block_size": w.block_size, "q_dtype": w.dtype, "kv_dtype": w.kv_dtype,
+            "mask_type": w.mask_type, "lse": w.lse, "parallelism": "single GPU",
+            "work_items": len(info["decode_items"]) + len(info["prefill_items"]),
+            "combine_items": len(info["combine_items"]),
+        },
+        "plan_us": plan_us,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    op.destroy()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

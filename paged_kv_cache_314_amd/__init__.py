@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     pa_last_error,
     pa_op_describe,
     pa_op_destroy,
+    pa_op_set_timing_events,
     pa_paged_attention,
     pa_paged_attention_get_workspace_size,
     pa_status_string,

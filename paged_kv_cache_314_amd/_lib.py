@@ -38,6 +38,7 @@ EXPORTED = (
     "pa_paged_attention",
     "pa_op_destroy",
     "pa_op_describe",
+    "pa_op_set_timing_events",
     "pa_status_string",
     "pa_last_error",
     "pa_version",
@@ -87,6 +88,8 @@ def load():
                                        ctypes.c_void_p]
     lib.pa_op_destroy.restype = None
     lib.pa_op_destroy.argtypes = [ctypes.c_void_p]
+    lib.pa_op_set_timing_events.restype = ctypes.c_int
+    lib.pa_op_set_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.pa_op_describe.restype = ctypes.c_uint64
     lib.pa_op_describe.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_uint64]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -201,6 +204,15 @@ def pa_op_destroy(op):
         op.destroy()
     elif op:
         load().pa_op_destroy(op)
+
+
+def pa_op_set_timing_events(op, start, stop):
+    """Record torch.cuda.Event ``start``/``stop`` around the op's main kernel (None clears).
+    Events must have been recorded once (torch creates them lazily)."""
+    handle = op.handle if isinstance(op, Op) else op
+    s = start.cuda_event if start is not None else None
+    e = stop.cuda_event if stop is not None else None
+    _check(load().pa_op_set_timing_events(handle, s, e))
 
 
 def pa_op_describe(op):

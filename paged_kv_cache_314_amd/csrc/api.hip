@@ -16,6 +16,8 @@ struct pa_op {
     pa::Plan plan;
     void* staging = nullptr;        // pinned copy of the work lists (allocated on first run)
     hipEvent_t copied = nullptr;    // recorded after each upload from `staging`
+    hipEvent_t t_start = nullptr;   // caller's timing events around the main kernel
+    hipEvent_t t_stop = nullptr;
 };
 
 namespace {
@@ -164,8 +166,12 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.mask_type = p.mask_type;
         a.scale_is_f32 = p.scale_type == PA_F32;
         a.scale_log2 = scale_log2;
+        if (op->t_start != nullptr && (e = hipEventRecord(op->t_start, s)) != hipSuccess)
+            return hip_fail(e, "hipEventRecord(start)");
         e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, s);
         if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+        if (op->t_stop != nullptr && (e = hipEventRecord(op->t_stop, s)) != hipSuccess)
+            return hip_fail(e, "hipEventRecord(stop)");
         if (!p.combine_items.empty()) {
             pa::CombineArgs c{};
             c.items = reinterpret_cast<const pa::CombineItem*>(ws + p.off_combine);
@@ -211,8 +217,13 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
     a.mask_type = p.mask_type;
     a.scale_is_f32 = p.scale_type == PA_F32;
     a.scale_log2 = scale_log2;
+    if (op->t_start != nullptr && (e = hipEventRecord(op->t_start, s)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord(start)");
     e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, s);
-    return e == hipSuccess ? PA_OK : hip_fail(e, "prefill kernel launch");
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    if (op->t_stop != nullptr && (e = hipEventRecord(op->t_stop, s)) != hipSuccess)
+        return hip_fail(e, "hipEventRecord(stop)");
+    return PA_OK;
 }
 
 void pa_op_destroy(pa_op* op) {
@@ -224,6 +235,13 @@ void pa_op_destroy(pa_op* op) {
     }
     if (op->staging != nullptr) (void)hipHostFree(op->staging);
     delete op;
+}
+
+pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop) {
+    if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
+    op->t_start = static_cast<hipEvent_t>(start);
+    op->t_stop = static_cast<hipEvent_t>(stop);
+    return PA_OK;
 }
 
 uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
