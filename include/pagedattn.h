@@ -159,7 +159,10 @@ pa_status pa_paged_attention_get_workspace_size(
  * stream).  (PrefixEncoder, Definition: AtbSelfAttentionPrefixEncoder; the pages'
  * context argument becomes a HIP stream.)  workspace: device memory of at least the
  * phase-1 size, 256-byte aligned, or NULL if that size is 0; its contents on entry do
- * not matter and are scratch afterwards.  The call returns once the work is enqueued.
+ * not matter and are scratch afterwards (it holds split-KV partial results; the size is
+ * 0 when no sequence is split).  The call returns once the work is enqueued; the first
+ * call on an op allocates a small pinned, device-mapped host buffer for the op's work
+ * lists, which the kernels read in place (no host-to-device copy per run).
  * An op may be executed any number of times, on any stream of its device; two
  * executions must not share a workspace while both are in flight.
  * Returns PA_ERR_NULLPTR (op, or a needed workspace, is NULL), PA_ERR_WORKSPACE_TOO_SMALL,
@@ -169,7 +172,8 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
                              void* stream);
 
 /* Release an operator handle (NULL is ignored).  Work already enqueued is unaffected: the
- * call waits until the last upload of the op's work lists has left host memory. */
+ * call blocks until the kernels of the op's last run have finished (they read the op's
+ * work lists from its host buffer). */
 void pa_op_destroy(pa_op* op);
 
 /* Instrumentation: start and stop are hipEvent_t handles (or NULL to clear).  While set,

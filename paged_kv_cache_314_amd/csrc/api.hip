@@ -14,8 +14,9 @@
 
 struct pa_op {
     pa::Plan plan;
-    void* staging = nullptr;        // pinned copy of the work lists (allocated on first run)
-    hipEvent_t copied = nullptr;    // recorded after each upload from `staging`
+    void* staging = nullptr;        // pinned, device-mapped work lists (made on first run)
+    unsigned char* staging_dev = nullptr;   // the same memory as seen by the GPU
+    hipEvent_t done = nullptr;      // recorded after the last kernel of each run
     hipEvent_t t_start = nullptr;   // caller's timing events around the main kernel
     hipEvent_t t_stop = nullptr;
 };
@@ -34,15 +35,24 @@ pa_status hip_fail(hipError_t e, const char* what) {
     return fail(PA_ERR_HIP, msg);
 }
 
-// Copy the host work lists into one pinned buffer that phase 2 uploads each run.
+// Copy the host work lists into one pinned, device-mapped buffer.  Each workgroup reads
+// its own 32-byte item from it at start-up, so a run needs no host-to-device copy.
 pa_status ensure_staging(pa_op* op) {
     const pa::Plan& p = op->plan;
     if (op->staging != nullptr || p.items_bytes == 0) return PA_OK;
-    hipError_t e = hipHostMalloc(&op->staging, p.items_bytes, hipHostMallocDefault);
+    hipError_t e = hipHostMalloc(&op->staging, p.items_bytes, hipHostMallocMapped);
     if (e != hipSuccess) {
         op->staging = nullptr;
-        return hip_fail(e, "hipHostMalloc(work list staging)");
+        return hip_fail(e, "hipHostMalloc(work lists)");
     }
+    void* dev = nullptr;
+    e = hipHostGetDevicePointer(&dev, op->staging, 0);
+    if (e != hipSuccess) {
+        (void)hipHostFree(op->staging);
+        op->staging = nullptr;
+        return hip_fail(e, "hipHostGetDevicePointer(work lists)");
+    }
+    op->staging_dev = static_cast<unsigned char*>(dev);
     auto* base = static_cast<unsigned char*>(op->staging);
     std::memset(base, 0, p.items_bytes);
     if (p.mode == pa::Mode::kDecode) {
@@ -121,23 +131,20 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
 
     pa_status st = ensure_staging(op);
     if (st != PA_OK) return st;
-    auto* ws = static_cast<unsigned char*>(workspace);
-    if (op->copied == nullptr) {
-        e = hipEventCreateWithFlags(&op->copied, hipEventDisableTiming);
+    if (op->done == nullptr) {
+        e = hipEventCreateWithFlags(&op->done, hipEventDisableTiming);
         if (e != hipSuccess) {
-            op->copied = nullptr;
+            op->done = nullptr;
             return hip_fail(e, "hipEventCreateWithFlags");
         }
     }
-    e = hipMemcpyAsync(ws, op->staging, p.items_bytes, hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work lists)");
-    e = hipEventRecord(op->copied, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    auto* ws = static_cast<unsigned char*>(workspace);
+    const unsigned char* lists = op->staging_dev;
     const float scale_log2 = p.qk_scale * 1.4426950408889634f;
 
     if (p.mode == pa::Mode::kDecode) {
         pa::DecodeArgs a{};
-        a.items = reinterpret_cast<const pa::DecodeItem*>(ws + p.off_items);
+        a.items = reinterpret_cast<const pa::DecodeItem*>(lists + p.off_items);
         a.q = p.q;
         a.k = p.k;
         a.v = p.v;
@@ -147,8 +154,8 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.slopes = p.slopes;
         a.kscale = p.kscale;
         a.vscale = p.vscale;
-        a.part_o = reinterpret_cast<float*>(ws + p.off_part_o);
-        a.part_ml = reinterpret_cast<float*>(ws + p.off_part_ml);
+        a.part_o = p.workspace_bytes ? reinterpret_cast<float*>(ws + p.off_part_o) : nullptr;
+        a.part_ml = p.workspace_bytes ? reinterpret_cast<float*>(ws + p.off_part_ml) : nullptr;
         a.q_tok_stride = p.q_tok_stride;
         a.q_head_stride = p.q_head_stride;
         a.out_tok_stride = p.out_tok_stride;
@@ -174,7 +181,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
             return hip_fail(e, "hipEventRecord(stop)");
         if (!p.combine_items.empty()) {
             pa::CombineArgs c{};
-            c.items = reinterpret_cast<const pa::CombineItem*>(ws + p.off_combine);
+            c.items = reinterpret_cast<const pa::CombineItem*>(lists + p.off_combine);
             c.part_o = a.part_o;
             c.part_ml = a.part_ml;
             c.out = p.out;
@@ -186,52 +193,53 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
             e = pa::launch_combine(c, static_cast<int>(p.combine_items.size()), p.head_size, bf16, s);
             if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
         }
-        return PA_OK;
+    } else {
+        pa::PrefillArgs a{};
+        a.items = reinterpret_cast<const pa::PrefillItem*>(lists + p.off_items);
+        a.q = p.q;
+        a.k = p.k;
+        a.v = p.v;
+        a.table = p.table;
+        a.out = p.out;
+        a.lse = p.lse;
+        a.slopes = p.slopes;
+        a.kscale = p.kscale;
+        a.vscale = p.vscale;
+        a.q_tok_stride = p.q_tok_stride;
+        a.q_head_stride = p.q_head_stride;
+        a.out_tok_stride = p.out_tok_stride;
+        a.out_head_stride = p.out_head_stride;
+        a.lse_tok_stride = p.lse_tok_stride;
+        a.k_blk_stride = p.k_blk_stride;
+        a.k_slot_stride = p.k_slot_stride;
+        a.k_head_stride = p.k_head_stride;
+        a.v_blk_stride = p.v_blk_stride;
+        a.v_slot_stride = p.v_slot_stride;
+        a.v_head_stride = p.v_head_stride;
+        a.table_stride = p.table_stride;
+        a.group = p.group;
+        a.block_size = p.block_size;
+        a.mask_type = p.mask_type;
+        a.scale_is_f32 = p.scale_type == PA_F32;
+        a.scale_log2 = scale_log2;
+        if (op->t_start != nullptr && (e = hipEventRecord(op->t_start, s)) != hipSuccess)
+            return hip_fail(e, "hipEventRecord(start)");
+        e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, s);
+        if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+        if (op->t_stop != nullptr && (e = hipEventRecord(op->t_stop, s)) != hipSuccess)
+            return hip_fail(e, "hipEventRecord(stop)");
     }
-
-    pa::PrefillArgs a{};
-    a.items = reinterpret_cast<const pa::PrefillItem*>(ws + p.off_items);
-    a.q = p.q;
-    a.k = p.k;
-    a.v = p.v;
-    a.table = p.table;
-    a.out = p.out;
-    a.lse = p.lse;
-    a.slopes = p.slopes;
-    a.kscale = p.kscale;
-    a.vscale = p.vscale;
-    a.q_tok_stride = p.q_tok_stride;
-    a.q_head_stride = p.q_head_stride;
-    a.out_tok_stride = p.out_tok_stride;
-    a.out_head_stride = p.out_head_stride;
-    a.lse_tok_stride = p.lse_tok_stride;
-    a.k_blk_stride = p.k_blk_stride;
-    a.k_slot_stride = p.k_slot_stride;
-    a.k_head_stride = p.k_head_stride;
-    a.v_blk_stride = p.v_blk_stride;
-    a.v_slot_stride = p.v_slot_stride;
-    a.v_head_stride = p.v_head_stride;
-    a.table_stride = p.table_stride;
-    a.group = p.group;
-    a.block_size = p.block_size;
-    a.mask_type = p.mask_type;
-    a.scale_is_f32 = p.scale_type == PA_F32;
-    a.scale_log2 = scale_log2;
-    if (op->t_start != nullptr && (e = hipEventRecord(op->t_start, s)) != hipSuccess)
-        return hip_fail(e, "hipEventRecord(start)");
-    e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, s);
-    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
-    if (op->t_stop != nullptr && (e = hipEventRecord(op->t_stop, s)) != hipSuccess)
-        return hip_fail(e, "hipEventRecord(stop)");
-    return PA_OK;
+    // the kernels read the op's work lists from host memory until they finish
+    e = hipEventRecord(op->done, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e, "hipEventRecord(done)");
 }
 
 void pa_op_destroy(pa_op* op) {
     if (op == nullptr) return;
-    // an enqueued upload may still read the pinned staging buffer: wait for the last one
-    if (op->copied != nullptr) {
-        (void)hipEventSynchronize(op->copied);
-        (void)hipEventDestroy(op->copied);
+    // kernels enqueued with this op may still read its work lists: wait for the last run
+    if (op->done != nullptr) {
+        (void)hipEventSynchronize(op->done);
+        (void)hipEventDestroy(op->done);
     }
     if (op->staging != nullptr) (void)hipHostFree(op->staging);
     delete op;

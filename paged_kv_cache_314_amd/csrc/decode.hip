@@ -22,6 +22,14 @@
 // rows per load instruction, and transposed in registers (8x8 of 16-bit values), so no
 // LDS traffic is needed on the streaming path.  Tokens are visited in the permuted
 // order that makes the S accumulator layout equal the P^T operand layout.
+//
+// Streaming: every load of a tile is issued from one uniform (scalar) base plus a 32-bit
+// per-lane offset, without branches; rows past kvSeqLen are clamped to the last valid
+// row (their scores are masked, their V rows zeroed), and the next tile's loads are in
+// flight while the current tile is computed.  Block ids come from a lane-distributed
+// window of 64 table entries read with readlane, so the table costs no load per tile.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_kernels.h"
@@ -39,12 +47,22 @@ __device__ __forceinline__ int dchunk(int qg, int kk) {
     else return 4 * kk + qg;
 }
 
+template <int D, bool I8>
+struct DecodeTileRegs {
+    static constexpr int KN = I8 ? D / 64 : D / 32;   // 16-byte K loads per row
+    u32x4 k[2][KN];
+    std::conditional_t<I8, u32x2, u32x4> v[8];
+};
+
 template <int D, bool BF16, bool I8>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     constexpr int KK = D / 32;                 // QK k-steps
     constexpr int KP = D / 64;                 // int8 16-byte loads per K row
     constexpr bool MBF = BF16 && !I8;          // MFMA element type (int8 path runs in f16)
     constexpr int VCOLS = D / 8;               // lanes (per row) that hold V columns
+    constexpr int ESZ = I8 ? 1 : 2;            // bytes per K/V element
+    using Tile = DecodeTileRegs<D, I8>;
+    using VT = std::conditional_t<I8, u32x2, u32x4>;
 
     __shared__ float s_m[kDecodeWaves][kHeadPack];
     __shared__ float s_l[kDecodeWaves][kHeadPack];
@@ -52,7 +70,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 
     const DecodeItem it = a.items[blockIdx.x];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;                 // packed head (QK/PV column)
     const int qg = lane >> 4;                  // lane group: k-slots 8*qg .. 8*qg+7
     const int hl = it.hg * kHeadPack + col;    // head index within the kv group
@@ -144,83 +162,109 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const int w1 = it.t0 + (ntiles * (wave + 1)) / kDecodeWaves;
     const int32_t* trow = a.table + static_cast<int64_t>(it.b) * a.table_stride;
     const int bs = a.block_size;
-    const int64_t k_head_off = static_cast<int64_t>(it.kvh) * a.k_head_stride;
-    const int64_t v_head_off = static_cast<int64_t>(it.kvh) * a.v_head_stride;
+    const char* kpool = static_cast<const char*>(a.k) +
+                        static_cast<int64_t>(it.kvh) * a.k_head_stride * ESZ;
+    const char* vpool = static_cast<const char*>(a.v) +
+                        static_cast<int64_t>(it.kvh) * a.v_head_stride * ESZ;
+    const int64_t kblk_bytes = a.k_blk_stride * ESZ, vblk_bytes = a.v_blk_stride * ESZ;
+    const uint32_t kslot_bytes = static_cast<uint32_t>(a.k_slot_stride * ESZ);
+    const uint32_t vslot_bytes = static_cast<uint32_t>(a.v_slot_stride * ESZ);
 
-    for (int tile = w0; tile < w1; ++tile) {
-        const int T = tile * kDecodeTile;
-        // Blocks holding tokens T .. T+31: at most three (blockSize >= 16).
-        const int blk_a = T / bs;
-        const int r0 = T - blk_a * bs;
-        const int e0 = trow[blk_a];
-        const int e1 = ((blk_a + 1) * bs < kvlen) ? trow[blk_a + 1] : 0;
-        const int e2 = ((blk_a + 2) * bs < kvlen) ? trow[blk_a + 2] : 0;
-        auto token_addr = [&](int delta, int64_t blk_stride, int64_t slot_stride,
-                              int64_t head_off) -> int64_t {
-            int u = r0 + delta;
-            int nb = (u >= bs) + (u >= 2 * bs);
-            int phys = nb == 0 ? e0 : (nb == 1 ? e1 : e2);
-            return static_cast<int64_t>(phys) * blk_stride +
-                   static_cast<int64_t>(u - nb * bs) * slot_stride + head_off;
-        };
+    const uint32_t vcol = (I8 ? 8u : 16u) * static_cast<uint32_t>(col & (VCOLS - 1));
 
-        // ---- K tile (MFMA A operand: lane row = token T + 16m + col)
-        u32x4 kop[2][KK];
+    // Each 16-token half of a 32-token tile lies inside one block (blockSize is a
+    // multiple of 16 and tiles start at multiples of 32), so every load of a tile uses a
+    // uniform base: K row m and V rows r/4 == h read from half h.  Block ids are scalar
+    // loads (constant address space: they do not count against vector-load waits).
+    using ctab_t = const __attribute__((address_space(4))) int32_t*;
+    const ctab_t ctab = reinterpret_cast<ctab_t>(reinterpret_cast<uintptr_t>(trow));
+    struct TileBase {
+        int T;
+        int lim[2];                  // last valid row inside each half (clamp)
+        const char* kb[2];           // row 0 of each half
+        const char* vb[2];
+    };
+    auto tile_base = [&](int tile) -> TileBase {
+        TileBase b;
+        b.T = tile * kDecodeTile;
+        const int t0 = b.T, t1 = b.T + 16;
+        const int blk0 = t0 / bs, blk1 = t1 / bs;
+        const int e0 = ctab[blk0];
+        const bool h1 = t1 < kvlen;                   // second half has a valid row
+        const int e1 = (h1 && blk1 != blk0) ? ctab[blk1] : e0;
+        const int s0 = t0 - blk0 * bs;
+        b.kb[0] = kpool + static_cast<int64_t>(e0) * kblk_bytes + static_cast<int64_t>(s0) * kslot_bytes;
+        b.vb[0] = vpool + static_cast<int64_t>(e0) * vblk_bytes + static_cast<int64_t>(s0) * vslot_bytes;
+        b.lim[0] = min(15, kvlen - 1 - t0);
+        if (h1) {
+            const int s1 = t1 - blk1 * bs;
+            b.kb[1] = kpool + static_cast<int64_t>(e1) * kblk_bytes + static_cast<int64_t>(s1) * kslot_bytes;
+            b.vb[1] = vpool + static_cast<int64_t>(e1) * vblk_bytes + static_cast<int64_t>(s1) * vslot_bytes;
+            b.lim[1] = min(15, kvlen - 1 - t1);
+        } else {                                      // whole half past kvlen: re-read row kvlen-1
+            b.kb[1] = b.kb[0] + static_cast<int64_t>(b.lim[0]) * kslot_bytes;
+            b.vb[1] = b.vb[0] + static_cast<int64_t>(b.lim[0]) * vslot_bytes;
+            b.lim[1] = 0;
+        }
+        return b;
+    };
+    // per-lane byte offsets inside a half: K row `col`, lane group qg's 16-byte chunk(s);
+    // V rows 4*qg + (r&3), columns 8*col (in-bounds alias col&(VCOLS-1) when D = 64)
+    const uint32_t kqg = 16u * static_cast<uint32_t>(qg);
+    Tile t;
+    auto issue_k = [&](const TileBase& b) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int delta = 16 * m + col;
-            const bool ok = T + delta < kvlen;
-            const int64_t off = ok ? token_addr(delta, a.k_blk_stride, a.k_slot_stride, k_head_off) : 0;
-            if constexpr (!I8) {
-                const uint16_t* krow = static_cast<const uint16_t*>(a.k) + off;
+            const uint32_t ro = static_cast<uint32_t>(min(col, b.lim[m])) * kslot_bytes + kqg;
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    u32x4 z = {0u, 0u, 0u, 0u};
-                    kop[m][kk] = ok ? *reinterpret_cast<const u32x4*>(krow + 8 * dchunk<I8>(qg, kk)) : z;
-                }
-            } else {
-                const int8_t* krow = static_cast<const int8_t*>(a.k) + off;
-#pragma unroll
-                for (int kp = 0; kp < KP; ++kp) {
-                    u32x4 raw = {0u, 0u, 0u, 0u};
-                    if (ok) raw = *reinterpret_cast<const u32x4*>(krow + 16 * (qg + 4 * kp));
-                    // 16 int8 -> two k-steps of 8 f16 each
-                    const u32x2 c0 = i8x4_to_f16x4(raw.x), c1 = i8x4_to_f16x4(raw.y);
-                    const u32x2 c2 = i8x4_to_f16x4(raw.z), c3 = i8x4_to_f16x4(raw.w);
-                    kop[m][2 * kp] = u32x4{c0.x, c0.y, c1.x, c1.y};
-                    kop[m][2 * kp + 1] = u32x4{c2.x, c2.y, c3.x, c3.y};
-                }
-            }
+            for (int i = 0; i < Tile::KN; ++i)
+                t.k[m][i] = *reinterpret_cast<const u32x4*>(b.kb[m] + (ro + 64u * i));
         }
-        // ---- V tile rows: token T + 16*(r/4) + 4*qg + r%4, columns 8*col .. 8*col+7
-        u32x4 vrow[8];
+    };
+    auto issue_v = [&](const TileBase& b) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int delta = 16 * (r >> 2) + 4 * qg + (r & 3);
-            const bool ok = (T + delta < kvlen) && (col < VCOLS);
-            const int64_t off = ok ? token_addr(delta, a.v_blk_stride, a.v_slot_stride, v_head_off) : 0;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            if constexpr (!I8) {
-                const uint16_t* vp = static_cast<const uint16_t*>(a.v) + off + 8 * col;
-                vrow[r] = ok ? *reinterpret_cast<const u32x4*>(vp) : z;
-            } else {
-                const int8_t* vp = static_cast<const int8_t*>(a.v) + off + 8 * col;
-                u32x2 raw = {0u, 0u};
-                if (ok) raw = *reinterpret_cast<const u32x2*>(vp);
-                const u32x2 c0 = i8x4_to_f16x4(raw.x), c1 = i8x4_to_f16x4(raw.y);
-                vrow[r] = ok ? u32x4{c0.x, c0.y, c1.x, c1.y} : z;
-            }
+            const int h = r >> 2;
+            const uint32_t ro = static_cast<uint32_t>(min(4 * qg + (r & 3), b.lim[h])) * vslot_bytes + vcol;
+            t.v[r] = *reinterpret_cast<const VT*>(b.vb[h] + ro);
         }
+    };
 
+    // Loads of tile i+1 are issued as soon as tile i's registers are consumed: K right
+    // after the QK MFMAs, V right after the transpose that builds the PV operands.  The
+    // block ids of tile i+1 are fetched at the top of iteration i.
+    TileBase cur;
+    if (w0 < w1) {
+        cur = tile_base(w0);
+        issue_k(cur);
+        issue_v(cur);
+    }
+    for (int tile = w0; tile < w1; ++tile) {
+        const int T = cur.T;
+        // the last tile re-issues its own loads (L2 hits) so that the loop body has no
+        // branch around a load and each wait leaves the other operand's 8 loads in flight
+        const TileBase nxt = (tile + 1 < w1) ? tile_base(tile + 1) : cur;
         // ---- S = K Q^T, scaled to log2 units, bias + mask
         float s[8];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (!I8) {
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                c = mfma16x16x32<MBF>(kop[m][kk], qhi[kk], c);
-                if constexpr (I8) c = mfma16x16x32<false>(kop[m][kk], qlo[kk], c);
+                for (int kk = 0; kk < KK; ++kk) c = mfma16x16x32<MBF>(t.k[m][kk], qhi[kk], c);
+            } else {
+#pragma unroll
+                for (int kp = 0; kp < KP; ++kp) {
+                    const u32x4 raw = t.k[m][kp];
+                    const u32x2 c0 = i8x4_to_f16x4(raw.x), c1 = i8x4_to_f16x4(raw.y);
+                    const u32x2 c2 = i8x4_to_f16x4(raw.z), c3 = i8x4_to_f16x4(raw.w);
+                    const u32x4 k0 = {c0.x, c0.y, c1.x, c1.y};
+                    const u32x4 k1 = {c2.x, c2.y, c3.x, c3.y};
+                    c = mfma16x16x32<false>(k0, qhi[2 * kp], c);
+                    c = mfma16x16x32<false>(k0, qlo[2 * kp], c);
+                    c = mfma16x16x32<false>(k1, qhi[2 * kp + 1], c);
+                    c = mfma16x16x32<false>(k1, qlo[2 * kp + 1], c);
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -230,6 +274,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
                 s[4 * m + r] = (j < kvlen) ? x : -INFINITY;
             }
         }
+        issue_k(nxt);
         // ---- online softmax (head `col`; its 32 scores live in 4 lanes x 8)
         float tmax = s[0];
 #pragma unroll
@@ -256,17 +301,40 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         pop.z = pack2<MBF>(p[4], p[5]);
         pop.w = pack2<MBF>(p[6], p[7]);
 
-        // ---- O^T += V^T P^T: operand n holds column d = 8*col + n of the 8 rows
+        // ---- V rows as 16-bit values; rows past kvlen (tail tile only) are zeroed
+        u32x4 vrow[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (!I8) {
+                vrow[r] = t.v[r];
+            } else {
+                const u32x2 c0 = i8x4_to_f16x4(t.v[r].x), c1 = i8x4_to_f16x4(t.v[r].y);
+                vrow[r] = u32x4{c0.x, c0.y, c1.x, c1.y};
+            }
+        }
+        if (T + kDecodeTile > kvlen) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const bool ok = T + 16 * (r >> 2) + 4 * qg + (r & 3) < kvlen;
+                u32x4 z = {0u, 0u, 0u, 0u};
+                vrow[r] = ok ? vrow[r] : z;
+            }
+        }
+        // operand n holds column d = 8*col + n of the 8 rows
+        u32x4 vop[8];
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-            u32x4 vop;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t x = vrow[2 * i][n >> 1], y = vrow[2 * i + 1][n >> 1];
-                vop[i] = (n & 1) ? pack_hi(x, y) : pack_lo(x, y);
+                vop[n][i] = (n & 1) ? pack_hi(x, y) : pack_lo(x, y);
             }
-            acc[n] = mfma16x16x32<MBF>(vop, pop, acc[n]);
         }
+        issue_v(nxt);
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[n] = mfma16x16x32<MBF>(vop[n], pop, acc[n]);
+        cur = nxt;
     }
 
     // ------------------------------------------------ merge the 4 wave states

@@ -92,10 +92,10 @@ struct Plan {
     int32_t decode_chunk_tiles = 0;
     int32_t partial_slots = 0;
 
-    // workspace layout (bytes, 256-aligned offsets)
-    uint64_t off_items = 0, off_combine = 0, off_part_o = 0, off_part_ml = 0;
-    uint64_t items_bytes = 0;        // bytes of the work lists (one host->device copy)
-    uint64_t workspace_bytes = 0;
+    // work lists live in pinned host memory owned by the op (offsets into it); the
+    // device workspace holds only the split-KV partials (256-aligned offsets)
+    uint64_t off_items = 0, off_combine = 0, items_bytes = 0;
+    uint64_t off_part_o = 0, off_part_ml = 0, workspace_bytes = 0;
 };
 
 // Validation + planning.  On failure returns a status and sets `err`.

@@ -448,16 +448,15 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         }
         p.partial_slots = slots;
         const int64_t geff = std::min<int32_t>(p.group, kHeadPack);
+        // work lists: in the op's pinned host buffer; partials: in the device workspace
         p.off_items = 0;
-        off = align256(p.decode_items.size() * sizeof(DecodeItem));
-        p.off_combine = off;
-        off = align256(off + p.combine_items.size() * sizeof(CombineItem));
-        p.items_bytes = off;
-        p.off_part_o = off;
-        off = align256(off + uint64_t(slots) * geff * qv.d * sizeof(float));
+        p.off_combine = align256(p.decode_items.size() * sizeof(DecodeItem));
+        p.items_bytes = align256(p.off_combine + p.combine_items.size() * sizeof(CombineItem));
+        p.off_part_o = 0;
+        off = align256(uint64_t(slots) * geff * qv.d * sizeof(float));
         p.off_part_ml = off;
         off = align256(off + uint64_t(slots) * geff * 2 * sizeof(float));
-        p.workspace_bytes = off;
+        p.workspace_bytes = slots > 0 ? off : 0;
     } else {
         // ---- prefill: (sequence, head, 128-row query tile) items, heaviest first
         p.mode = Mode::kPrefill;
@@ -490,9 +489,8 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         std::stable_sort(p.prefill_items.begin(), p.prefill_items.end(),
                          [](const PrefillItem& x, const PrefillItem& y) { return x.ktiles > y.ktiles; });
         p.off_items = 0;
-        off = align256(p.prefill_items.size() * sizeof(PrefillItem));
-        p.items_bytes = off;
-        p.workspace_bytes = off;
+        p.items_bytes = align256(p.prefill_items.size() * sizeof(PrefillItem));
+        p.workspace_bytes = 0;
     }
 }
 

@@ -385,7 +385,7 @@ def test_two_dimensional_forms():
 def test_execute_argument_errors():
     lib = pa.load()
     assert lib.pa_paged_attention(None, 0, None, None) == pa.PA_ERR_NULLPTR
-    c = base()
+    c = base(kv_lens=[20000, 37])           # long enough to be split: needs partials
     st, ws, op = c.call()
     assert st == pa.PA_OK and ws > 0
     assert lib.pa_paged_attention(FAKE, ws - 1, op, None) == pa.PA_ERR_WORKSPACE_TOO_SMALL
