@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_causal_bf16")
+    ap.add_argument("--kv-layout", choices=["bnbsh", "bnnbsd"], default="bnbsh",
+                    help="K/V pool memory layout: (block, slot, kv head, d) as the workload "
+                         "defines it, or (block, kv head, slot, d) passed as a strided view")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU budget of the oracle baseline sample")
@@ -193,6 +196,9 @@ def main():
     nbytes, flops = algorithmic_counts(inp)
     g = {key: (val.to(dev) if isinstance(val, torch.Tensor) and key not in ("seq_len", "kv_seq_len")
                else val) for key, val in inp.items()}
+    if args.kv_layout == "bnnbsd":
+        for key in ("key", "value"):
+            g[key] = g[key].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     out = torch.empty_like(g["query"])
     lse = (torch.empty((out.shape[0], w.head_num), dtype=torch.float32, device=dev)
            if w.lse else None)
@@ -276,7 +282,8 @@ def main():
             "workload": args.workload, "mode": kind, "batch": w.batch,
             "head_num": w.head_num, "kv_head_num": w.kv_head_num, "head_size": w.head_size,
             "block_size": w.block_size, "q_dtype": w.dtype, "kv_dtype": w.kv_dtype,
-            "mask_type": w.mask_type, "lse": w.lse, "parallelism": "single GPU",
+            "mask_type": w.mask_type, "lse": w.lse, "kv_layout": args.kv_layout,
+            "parallelism": "single GPU",
             "work_items": len(info["decode_items"]) + len(info["prefill_items"]),
             "combine_items": len(info["combine_items"]),
         },

@@ -211,8 +211,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     // per-lane byte offsets inside a half: K row `col`, lane group qg's 16-byte chunk(s);
     // V rows 4*qg + (r&3), columns 8*col (in-bounds alias col&(VCOLS-1) when D = 64)
     const uint32_t kqg = 16u * static_cast<uint32_t>(qg);
-    Tile t;
-    auto issue_k = [&](const TileBase& b) {
+    auto issue_k = [&](Tile& t, const TileBase& b) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const uint32_t ro = static_cast<uint32_t>(min(col, b.lim[m])) * kslot_bytes + kqg;
@@ -221,7 +220,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
                 t.k[m][i] = *reinterpret_cast<const u32x4*>(b.kb[m] + (ro + 64u * i));
         }
     };
-    auto issue_v = [&](const TileBase& b) {
+    auto issue_v = [&](Tile& t, const TileBase& b) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int h = r >> 2;
@@ -230,20 +229,11 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
         }
     };
 
-    // Loads of tile i+1 are issued as soon as tile i's registers are consumed: K right
-    // after the QK MFMAs, V right after the transpose that builds the PV operands.  The
-    // block ids of tile i+1 are fetched at the top of iteration i.
-    TileBase cur;
-    if (w0 < w1) {
-        cur = tile_base(w0);
-        issue_k(cur);
-        issue_v(cur);
-    }
-    for (int tile = w0; tile < w1; ++tile) {
+    // Process the tile held in `t` (addressed by `cur`) and refill `t` with the tile two
+    // ahead (`next`): its K loads are issued right after the QK MFMAs consume K, its V
+    // loads right after the transpose consumes V, so two tiles are always in flight.
+    auto step = [&](Tile& t, const TileBase& cur, const TileBase& next) {
         const int T = cur.T;
-        // the last tile re-issues its own loads (L2 hits) so that the loop body has no
-        // branch around a load and each wait leaves the other operand's 8 loads in flight
-        const TileBase nxt = (tile + 1 < w1) ? tile_base(tile + 1) : cur;
         // ---- S = K Q^T, scaled to log2 units, bias + mask
         float s[8];
 #pragma unroll
@@ -274,7 +264,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
                 s[4 * m + r] = (j < kvlen) ? x : -INFINITY;
             }
         }
-        issue_k(nxt);
+        issue_k(t, next);
         // ---- online softmax (head `col`; its 32 scores live in 4 lanes x 8)
         float tmax = s[0];
 #pragma unroll
@@ -301,40 +291,69 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
         pop.z = pack2<MBF>(p[4], p[5]);
         pop.w = pack2<MBF>(p[6], p[7]);
 
-        // ---- V rows as 16-bit values; rows past kvlen (tail tile only) are zeroed
-        u32x4 vrow[8];
+        // ---- V rows (rows past kvlen, tail tile only, are zeroed) transposed into the
+        // PV operands: operand n holds column d = 8*col + n of the 8 rows
+        VT vrow[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if constexpr (!I8) {
-                vrow[r] = t.v[r];
-            } else {
-                const u32x2 c0 = i8x4_to_f16x4(t.v[r].x), c1 = i8x4_to_f16x4(t.v[r].y);
-                vrow[r] = u32x4{c0.x, c0.y, c1.x, c1.y};
-            }
-        }
+        for (int r = 0; r < 8; ++r) vrow[r] = t.v[r];
         if (T + kDecodeTile > kvlen) {
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const bool ok = T + 16 * (r >> 2) + 4 * qg + (r & 3) < kvlen;
-                u32x4 z = {0u, 0u, 0u, 0u};
-                vrow[r] = ok ? vrow[r] : z;
+                VT z = {};
+                vrow[r] = ok ? vrow[r] : z;      // an int8 0 converts to f16 0 exactly
             }
         }
-        // operand n holds column d = 8*col + n of the 8 rows
-        u32x4 vop[8];
+        if constexpr (I8) {
+            u32x4 vop[8];
+            i8_rows_to_f16_cols(vrow, vop);
+            issue_v(t, next);
+            // ---- O^T += V^T P^T
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
+            for (int n = 0; n < 8; ++n) acc[n] = mfma16x16x32<MBF>(vop[n], pop, acc[n]);
+        } else {
+            // each operand is built right before its MFMA (fewer live registers); the
+            // next V loads follow the last one
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t x = vrow[2 * i][n >> 1], y = vrow[2 * i + 1][n >> 1];
-                vop[n][i] = (n & 1) ? pack_hi(x, y) : pack_lo(x, y);
+            for (int n = 0; n < 8; ++n) {
+                u32x4 vop;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t x = vrow[2 * i][n >> 1], y = vrow[2 * i + 1][n >> 1];
+                    vop[i] = (n & 1) ? pack_hi(x, y) : pack_lo(x, y);
+                }
+                acc[n] = mfma16x16x32<MBF>(vop, pop, acc[n]);
             }
+            issue_v(t, next);
         }
-        issue_v(nxt);
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] = mfma16x16x32<MBF>(vop[n], pop, acc[n]);
-        cur = nxt;
+    };
+
+    // Two register buffers alternate between even and odd tiles.  Past the end of the
+    // range a buffer loads row 0 of block 0 instead (the same few cache lines for every
+    // wave, so L2 hits), so that no load sits behind a branch and each wait leaves the
+    // later tiles' loads in flight.
+    TileBase idle;
+    idle.T = 0;
+    idle.lim[0] = idle.lim[1] = 0;
+    idle.kb[0] = idle.kb[1] = kpool;
+    idle.vb[0] = idle.vb[1] = vpool;
+    if (w0 < w1) {
+        Tile ta, tb;
+        TileBase ca = tile_base(w0);
+        TileBase cb = (w0 + 1 < w1) ? tile_base(w0 + 1) : idle;
+        issue_k(ta, ca);
+        issue_v(ta, ca);
+        issue_k(tb, cb);
+        issue_v(tb, cb);
+        for (int tile = w0; tile < w1; tile += 2) {
+            const TileBase na = (tile + 2 < w1) ? tile_base(tile + 2) : idle;
+            step(ta, ca, na);
+            ca = na;
+            if (tile + 1 >= w1) break;
+            const TileBase nb = (tile + 3 < w1) ? tile_base(tile + 3) : idle;
+            step(tb, cb, nb);
+            cb = nb;
+        }
     }
 
     // ------------------------------------------------ merge the 4 wave states
@@ -410,18 +429,21 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
         const int h = e / D, d = e - (e / D) * D;
         const int hlocal = it.hg * kHeadPack + h;
         if (hlocal >= a.group) continue;
+        // unrolled so that the partials' loads of several splits are in flight together;
+        // the sums still run in ascending split order
+        const float* ml = a.part_ml + 2 * (static_cast<int64_t>(it.slot0) * geff + h);
+        const float* po = a.part_o + (static_cast<int64_t>(it.slot0) * geff + h) * D + d;
+        const int64_t ml_step = 2 * geff, o_step = static_cast<int64_t>(geff) * D;
         float M = -INFINITY;
-        for (int s = 0; s < it.nsplit; ++s) {
-            const int64_t sl = static_cast<int64_t>(it.slot0 + s) * geff + h;
-            M = fmaxf(M, a.part_ml[2 * sl]);
-        }
+#pragma unroll 8
+        for (int s = 0; s < it.nsplit; ++s) M = fmaxf(M, ml[s * ml_step]);
         float L = 0.0f, O = 0.0f;
         if (M != -INFINITY) {
+#pragma unroll 4
             for (int s = 0; s < it.nsplit; ++s) {
-                const int64_t sl = static_cast<int64_t>(it.slot0 + s) * geff + h;
-                const float f = fast_exp2(a.part_ml[2 * sl] - M);
-                L += a.part_ml[2 * sl + 1] * f;
-                O += a.part_o[sl * D + d] * f;
+                const float f = fast_exp2(ml[s * ml_step] - M);
+                L += ml[s * ml_step + 1] * f;
+                O += po[s * o_step] * f;
             }
         }
         const int out_head = it.kvh * a.group + hlocal;

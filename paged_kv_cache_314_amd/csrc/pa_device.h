@@ -49,17 +49,47 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // Four int8 (one dword) -> four exact f16 values in two dwords.  Offset-binary trick:
 // byte u = x + 128 placed under exponent byte 0x64 is the f16 number 1024 + u, and
 // subtracting 1152 leaves x exactly (every integer below 2048 is an f16).
+// v_perm_b32 (perm(s0, s1, sel)): result byte i = byte sel.byte[i] of the 8-byte value
+// whose bytes 0-3 are s1 and 4-7 are s0.  With s0 = 0x64646464 the selectors below put
+// byte values under the f16 exponent byte 0x64.
+constexpr uint32_t kF16Exp = 0x64646464u;
+constexpr uint32_t kSelLoPair = 0x04010400u;   // [s1.b0, 64, s1.b1, 64]
+constexpr uint32_t kSelHiPair = 0x04030402u;   // [s1.b2, 64, s1.b3, 64]
+
+__device__ __forceinline__ uint32_t f16_unbias(uint32_t biased_pair) {
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, biased_pair) - bias);
+}
+
 __device__ __forceinline__ u32x2 i8x4_to_f16x4(uint32_t w) {
     const uint32_t u = w ^ 0x80808080u;
-    const uint32_t lo = (u & 0xffu) | ((u & 0xff00u) << 8) | 0x64006400u;
-    const uint32_t hi = ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u) | 0x64006400u;
-    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
-    const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
     u32x2 r;
-    r.x = __builtin_bit_cast(uint32_t, a);
-    r.y = __builtin_bit_cast(uint32_t, b);
+    r.x = f16_unbias(__builtin_amdgcn_perm(kF16Exp, u, kSelLoPair));
+    r.y = f16_unbias(__builtin_amdgcn_perm(kF16Exp, u, kSelHiPair));
     return r;
+}
+
+// Transpose-and-convert for the PV operand of an int8 V tile.  rows[r] holds 8 int8 of
+// token row r (columns c = 0..7, little-endian in .x then .y).  Returns, for column n,
+// the 8 f16 values rows[0..7][n] packed as the 4 dwords (rows 2i, 2i+1) of an MFMA
+// operand: out[n][i].  Offset-binary bytes (x ^ 0x80) are paired across two rows by one
+// perm, then each pair is placed under the f16 exponent and unbiased.
+__device__ __forceinline__ void i8_rows_to_f16_cols(const u32x2 (&rows)[8], u32x4 (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const uint32_t a = rows[2 * i][w] ^ 0x80808080u;       // row 2i: bytes 0-3
+            const uint32_t b = rows[2 * i + 1][w] ^ 0x80808080u;   // row 2i+1: bytes 4-7
+            // [a.b0, b.b0, a.b1, b.b1] and [a.b2, b.b2, a.b3, b.b3]
+            const uint32_t t01 = __builtin_amdgcn_perm(b, a, 0x05010400u);
+            const uint32_t t23 = __builtin_amdgcn_perm(b, a, 0x07030602u);
+            out[4 * w + 0][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t01, kSelLoPair));
+            out[4 * w + 1][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t01, kSelHiPair));
+            out[4 * w + 2][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t23, kSelLoPair));
+            out[4 * w + 3][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t23, kSelHiPair));
+        }
+    }
 }
 
 // ----------------------------------------------------------------------- MFMA

@@ -418,35 +418,45 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
             const int32_t klen = kl[b * kls];
             const int32_t tiles = (klen + kDecodeTile - 1) / kDecodeTile;
             const int32_t nsplit = std::max<int32_t>(1, (tiles + chunk - 1) / chunk);
-            for (int32_t h = 0; h < kvh_num; ++h) {
-                for (int32_t hg = 0; hg < p.head_groups; ++hg) {
-                    const int32_t slot0 = nsplit > 1 ? slots : -1;
-                    for (int32_t s = 0; s < nsplit; ++s) {
-                        DecodeItem it{};
-                        it.b = static_cast<int32_t>(b);
-                        it.kvh = h;
-                        it.hg = hg;
-                        it.t0 = static_cast<int32_t>(int64_t(tiles) * s / nsplit);
-                        it.t1 = static_cast<int32_t>(int64_t(tiles) * (s + 1) / nsplit);
-                        it.slot = nsplit > 1 ? slot0 + s : -1;
-                        it.qrow = q0[b];
-                        it.kvlen = klen;
-                        p.decode_items.push_back(it);
-                    }
-                    if (nsplit > 1) {
-                        CombineItem c{};
-                        c.kvh = h;
-                        c.hg = hg;
-                        c.slot0 = slot0;
-                        c.nsplit = nsplit;
-                        c.qrow = q0[b];
-                        p.combine_items.push_back(c);
-                        slots += nsplit;
-                    }
+            const int32_t groups = kvh_num * p.head_groups;
+            // (kv head, head group) g owns partial slots slots + g*nsplit + s.  Items are
+            // emitted head-major: the splits of one kv head launch together.  (Launching
+            // the kv heads of one token range together measured slower in the
+            // (block, slot, kv head, d) layout.)
+            for (int32_t g = 0; g < groups; ++g) {
+                for (int32_t s = 0; s < nsplit; ++s) {
+                    DecodeItem it{};
+                    it.b = static_cast<int32_t>(b);
+                    it.kvh = g / p.head_groups;
+                    it.hg = g % p.head_groups;
+                    it.t0 = static_cast<int32_t>(int64_t(tiles) * s / nsplit);
+                    it.t1 = static_cast<int32_t>(int64_t(tiles) * (s + 1) / nsplit);
+                    it.slot = nsplit > 1 ? slots + g * nsplit + s : -1;
+                    it.qrow = q0[b];
+                    it.kvlen = klen;
+                    p.decode_items.push_back(it);
                 }
+            }
+            if (nsplit > 1) {
+                for (int32_t g = 0; g < groups; ++g) {
+                    CombineItem c{};
+                    c.kvh = g / p.head_groups;
+                    c.hg = g % p.head_groups;
+                    c.slot0 = slots + g * nsplit;
+                    c.nsplit = nsplit;
+                    c.qrow = q0[b];
+                    p.combine_items.push_back(c);
+                }
+                slots += groups * nsplit;
             }
         }
         p.partial_slots = slots;
+        // longest ranges first: the hardware hands out workgroups in launch order, so
+        // this is a greedy longest-processing-time schedule and shortens the tail
+        std::stable_sort(p.decode_items.begin(), p.decode_items.end(),
+                         [](const DecodeItem& x, const DecodeItem& y) {
+                             return (x.t1 - x.t0) > (y.t1 - y.t0);
+                         });
         const int64_t geff = std::min<int32_t>(p.group, kHeadPack);
         // work lists: in the op's pinned host buffer; partials: in the device workspace
         p.off_items = 0;

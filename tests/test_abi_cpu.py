@@ -151,6 +151,7 @@ def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
                     assert (b, kvh, hg) not in by_key
                     continue
                 assert parts, (b, kvh, hg)
+                parts.sort()                    # launch order is a schedule, not tile order
                 tiles = -(-kl // 32)
                 cur = 0
                 for t0, t1, slot, qrow, kvlen in parts:
