@@ -188,7 +188,8 @@ pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop);
  * NUL.  Keys: "mode" ("noop", "fill", "decode", "prefill"), "workspace_bytes",
  * "chunk_tiles", "partial_slots", and the work lists "decode_items"
  * [b, kvh, hg, t0, t1, slot, qrow, kvlen], "combine_items" [kvh, hg, slot0, nsplit, qrow],
- * "prefill_items" [b, h, qbeg, qlen, kvlen, qrow0, ktiles].  Host only, no HIP call.
+ * "prefill_items" [b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads] (heads query heads from
+ * h, 128/heads query rows from qbeg).  Host only, no HIP call.
  * For inspection and tests: not a stable interface.  op == NULL returns 0. */
 uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap);
 

@@ -284,7 +284,8 @@ uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
         if (i) s += ", ";
         s += "[" + std::to_string(q.b) + ", " + std::to_string(q.h) + ", " + std::to_string(q.qbeg) +
              ", " + std::to_string(q.qlen) + ", " + std::to_string(q.kvlen) + ", " +
-             std::to_string(q.qrow0) + ", " + std::to_string(q.ktiles) + "]";
+             std::to_string(q.qrow0) + ", " + std::to_string(q.ktiles) + ", " +
+             std::to_string(q.heads) + "]";
     }
     s += "]}";
     if (buf != nullptr && cap > 0) {

@@ -43,16 +43,18 @@ struct CombineItem {
 };
 static_assert(sizeof(CombineItem) == 32, "CombineItem layout");
 
-// One prefill workgroup: kPrefillBM query rows of one (sequence, head).
+// One prefill workgroup: `heads` consecutive query heads of one kv group (1, 2 or 4)
+// times kPrefillBM / heads query rows of one sequence; wave w takes head
+// h + w % heads and rows qbeg + 32 * (w / heads) .. +31.
 struct PrefillItem {
     int32_t b;
-    int32_t h;
+    int32_t h;        // first query head
     int32_t qbeg;     // first local query row of the tile
     int32_t qlen;     // seqLen[b]
     int32_t kvlen;    // kvSeqLen[b]
     int32_t qrow0;    // packed row of local query 0 of this sequence
     int32_t ktiles;   // key tiles (kPrefillBN) the tile must visit
-    int32_t pad;
+    int32_t heads;    // query heads sharing the workgroup's K/V tiles
 };
 static_assert(sizeof(PrefillItem) == 32, "PrefillItem layout");
 

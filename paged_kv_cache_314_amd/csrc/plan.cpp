@@ -312,6 +312,12 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
     REQUIRE(mult16(qv.row_stride, eb_q) && mult16(qv.head_stride, eb_q) &&
                 mult16(ov.row_stride, eb_q) && mult16(ov.head_stride, eb_q),
             PA_ERR_PARAM_INVALID, "query/attnOut strides must be multiples of 16 bytes");
+    // the kernels address rows inside a block with 32-bit byte offsets
+    REQUIRE(kv.slot_stride >= 0 && vv.slot_stride >= 0 && kv.blk_stride >= 0 &&
+                vv.blk_stride >= 0 && kv.head_stride >= 0 && vv.head_stride >= 0,
+            PA_ERR_PARAM_INVALID, "key/value strides must be non-negative");
+    REQUIRE((bs * std::max(kv.slot_stride, vv.slot_stride) + qv.d) * eb_kv < (int64_t(1) << 31),
+            PA_ERR_UNSUPPORTED, "a cache block must span less than 2 GiB");
     REQUIRE(mult16(kv.blk_stride, eb_kv) && mult16(kv.slot_stride, eb_kv) &&
                 mult16(kv.head_stride, eb_kv) && mult16(vv.blk_stride, eb_kv) &&
                 mult16(vv.slot_stride, eb_kv) && mult16(vv.head_stride, eb_kv),
@@ -468,22 +474,26 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         off = align256(off + uint64_t(slots) * geff * 2 * sizeof(float));
         p.workspace_bytes = slots > 0 ? off : 0;
     } else {
-        // ---- prefill: (sequence, head, 128-row query tile) items, heaviest first
+        // ---- prefill: (sequence, query-head block, query-row tile) items, heaviest first.
+        // A workgroup covers up to 4 query heads of one kv group (so each K/V tile is
+        // staged once for all of them) and kPrefillBM / heads query rows.
         p.mode = Mode::kPrefill;
         const bool causal = maskType == PA_MASK_CAUSAL || maskType == PA_MASK_ALIBI;
+        const int32_t hpw = (p.group % 4 == 0) ? 4 : (p.group % 2 == 0 ? 2 : 1);
+        const int32_t rows = kPrefillBM / hpw;
         for (int64_t b = 0; b < B; ++b) {
             const int32_t qlen = ql[b * qls], klen = kl[b * kls];
-            for (int32_t qb = 0; qb < qlen; qb += kPrefillBM) {
+            for (int32_t qb = 0; qb < qlen; qb += rows) {
                 int64_t last_key;   // last key index any row of the tile can see
                 if (causal) {
-                    const int64_t last_row = std::min<int64_t>(qb + kPrefillBM, qlen) - 1;
+                    const int64_t last_row = std::min<int64_t>(qb + rows, qlen) - 1;
                     last_key = std::min<int64_t>(int64_t(klen) - qlen + last_row, int64_t(klen) - 1);
                 } else {
                     last_key = int64_t(klen) - 1;
                 }
                 const int32_t ktiles =
                     last_key < 0 ? 0 : static_cast<int32_t>((last_key + kPrefillBN) / kPrefillBN);
-                for (int32_t h = 0; h < headNum; ++h) {
+                for (int32_t h = 0; h < headNum; h += hpw) {
                     PrefillItem it{};
                     it.b = static_cast<int32_t>(b);
                     it.h = h;
@@ -492,6 +502,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                     it.kvlen = klen;
                     it.qrow0 = q0[b];
                     it.ktiles = ktiles;
+                    it.heads = hpw;
                     p.prefill_items.push_back(it);
                 }
             }

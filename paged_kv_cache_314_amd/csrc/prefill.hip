@@ -7,15 +7,20 @@
 // slopes[h] * (j - p_i) plus causal, qkScale post-multiplying Q*K^T.  Query i of a
 // sequence sits at absolute position p_i = kvSeqLen - seqLen + i.
 //
-// One workgroup = 4 waves = 128 query rows of one (sequence, head); wave w owns rows
-// 32w .. 32w+31.  Keys are visited in tiles of 64 up to the last key any of the 128 rows
-// can see.  Per tile:
-//   all threads: K tile (64 x D) -> LDS row-major; V tile -> LDS transposed (V^T, keys
-//                permuted so each lane's 8 MFMA k-slots are 16 contiguous bytes)
+// One workgroup = 4 waves covering `heads` (1, 2 or 4) query heads of one kv group and
+// 128 / heads query rows; wave w owns head h + w % heads and 32 rows.  All heads of the
+// workgroup read the same K/V, so each key tile is staged in LDS once for all of them.
+// Keys are visited in tiles of 64 up to the last key any of the rows can see.  Per tile:
+//   wave w:      loads keys 16w .. 16w+15 of the tile (one 16-key group always lies in
+//                one cache block: a uniform base + constant per-lane offsets) into LDS,
+//                K and V both row-major
 //   per wave:    S^T[64 keys x 32 rows] = K . Q^T      (D/16 x 2 MFMA 32x32x16)
-//                scale, ALiBi bias, causal / tail mask, online softmax, in registers:
-//                a lane owns one query row, so row max / sum need one cross-lane step
-//                O^T[D x 32 rows] += V^T . P^T          (D/32 x 4 MFMA 32x32x16)
+//                scale, ALiBi bias, causal / tail mask, online softmax in registers
+//                (a lane owns one query row; one cross-lane step per reduction), with
+//                the row maximum re-based only when it grows by more than 2^8
+//                O^T[D x 32 rows] += V^T . P^T          (D/32 x 4 MFMA 32x32x16), the
+//                V^T operands read straight from row-major V with the LDS transpose
+//                read ds_read_b64_tr_b16
 // Q stays in registers as the B operand; LDS is double-buffered so one barrier per key
 // tile suffices, and the next tile's global loads are in flight during the MFMA work.
 // int8 K/V are converted exactly to f16 on the way into LDS; the per-channel K scale is
@@ -28,16 +33,19 @@ namespace pa {
 
 namespace {
 
-constexpr int BM = kPrefillBM;   // 128 query rows per workgroup
-constexpr int BN = kPrefillBN;   // 64 keys per tile
-constexpr int KPAD = 8;          // LDS row padding (16-bit elements) against bank conflicts
-constexpr int VPAD = 8;
+constexpr int BN = kPrefillBN;          // 64 keys per tile
+constexpr float kRescaleSlack = 8.0f;   // log2 units a row max may exceed its reference
 
-// LDS position of key tau (0..63) inside a V^T row: tau = 16*kt + 8*a + 4*g + c is
-// placed at 16*kt + 8*g + 4*a + c, so lane group g reads keys {16kt + 4g + 0..3,
-// 16kt + 8 + 4g + 0..3} as one 16-byte run -- the k-slot order of the P^T operand.
-__device__ __forceinline__ int vt_pos4(int tg4) {   // position of key 4*tg4 (c = 0)
-    return 16 * (tg4 >> 2) + 8 * (tg4 & 1) + 4 * ((tg4 >> 1) & 1);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16;
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane 4*j + p supplies the 4 16-bit
+// values at its address; lane i of the group receives value i % 4 of lanes
+// i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4 (in that order).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16)(reinterpret_cast<uintptr_t>(p)));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 template <int D, bool BF16, bool I8>
@@ -45,36 +53,37 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     constexpr bool MBF = BF16 && !I8;
     constexpr int KS = D / 16;            // QK k-steps (32x32x16)
     constexpr int DT = D / 32;            // PV output row blocks
-    constexpr int KLD = D + KPAD;         // K tile LDS row length
-    constexpr int VLD = BN + VPAD;        // V^T LDS row length
-    // 16-bit global K loads: D/8 chunks of 16 bytes per key row
-    constexpr int CH = D / 8;
-    constexpr int NK = I8 ? (BN * (D / 16) + 255) / 256 : (BN * CH + 255) / 256;
-    constexpr int NV = (16 * CH + 255) / 256;   // V sub-blocks (4 keys x 8 d) per thread
+    constexpr int KLD = D + 8;            // K tile LDS row (16-bit elements)
+    constexpr int VLD = D + 32;           // V tile LDS row: conflict-free transposed reads
+    constexpr int ESZ = I8 ? 1 : 2;       // bytes per global K/V element
+    constexpr int CH = D * ESZ / 16;      // 16-byte chunks per global K/V row
+    constexpr int NL = 16 * CH / 64;      // 16-byte loads per lane for a 16-key group
+    constexpr int EPC = 16 / ESZ;         // elements per 16-byte chunk
 
     __shared__ uint16_t s_k[2][BN * KLD];
-    __shared__ uint16_t s_v[2][D * VLD];
+    __shared__ uint16_t s_v[2][BN * VLD];
 
     const PrefillItem it = a.items[blockIdx.x];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qcol = lane & 31;           // query row of this lane inside the wave
     const int g2 = lane >> 5;             // k-slot half
+    const int heads = it.heads;
+    const int h = it.h + wave % heads;    // this wave's query head
     const int kvh = it.h / a.group;
     const int64_t kvh_off = static_cast<int64_t>(kvh) * D;      // into the [Hkv, D] scales
-    const int64_t k_head_off = static_cast<int64_t>(kvh) * a.k_head_stride;
-    const int64_t v_head_off = static_cast<int64_t>(kvh) * a.v_head_stride;
     const int kvlen = it.kvlen;
     const int qlen = it.qlen;
     const bool causal = a.mask_type == PA_MASK_CAUSAL || a.mask_type == PA_MASK_ALIBI;
+    const bool alibi = a.mask_type == PA_MASK_ALIBI;
     const int shift = kvlen - qlen;       // p_i = shift + i
 
-    const int qi = it.qbeg + 32 * wave + qcol;            // local query row of this lane
+    const int wave_q0 = it.qbeg + 32 * (wave / heads);      // first local row of the wave
+    const int qi = wave_q0 + qcol;                          // local query row of this lane
     const bool qvalid = qi < qlen;
-    const int pos = shift + qi;                           // its absolute position
-    const int wave_q0 = it.qbeg + 32 * wave;
-    const int wave_q1 = min(wave_q0 + 31, qlen - 1);      // last valid row of the wave
+    const int pos = shift + qi;                             // its absolute position
+    const int wave_q1 = min(wave_q0 + 31, qlen - 1);        // last valid row of the wave
     const bool wave_live = wave_q0 < qlen;
     const int wave_pmin = shift + wave_q0;
     const int wave_pmax = shift + wave_q1;
@@ -85,7 +94,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     {
         const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                                static_cast<int64_t>(it.qrow0 + (qvalid ? qi : 0)) * a.q_tok_stride +
-                               static_cast<int64_t>(it.h) * a.q_head_stride;
+                               static_cast<int64_t>(h) * a.q_head_stride;
         if constexpr (!I8) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -139,132 +148,84 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             }
         }
     }
-    const float slope2 = (a.mask_type == PA_MASK_ALIBI) ? a.slopes[it.h] * kLog2e : 0.0f;
+    const float slope2 = alibi ? a.slopes[h] * kLog2e : 0.0f;
 
     // ---------------------------------------------------------- tile loads
-    const int32_t* trow = a.table + static_cast<int64_t>(it.b) * a.table_stride;
+    // Wave w stages keys 16w .. 16w+15 of each tile.  They lie in one cache block, so
+    // the block base is uniform and each lane reads at fixed offsets from it.
+    using ctab_t = const __attribute__((address_space(4))) int32_t*;
+    const ctab_t ctab = reinterpret_cast<ctab_t>(
+        reinterpret_cast<uintptr_t>(a.table + static_cast<int64_t>(it.b) * a.table_stride));
     const int bs = a.block_size;
-    const float inv_bs = 1.0f / static_cast<float>(bs);
-    const bool one_block_per_tile = (bs % BN) == 0;
+    const char* kpool = static_cast<const char*>(a.k) + static_cast<int64_t>(kvh) * a.k_head_stride * ESZ;
+    const char* vpool = static_cast<const char*>(a.v) + static_cast<int64_t>(kvh) * a.v_head_stride * ESZ;
+    const int64_t kblk_bytes = a.k_blk_stride * ESZ, vblk_bytes = a.v_blk_stride * ESZ;
+    const int64_t kslot_bytes = a.k_slot_stride * ESZ, vslot_bytes = a.v_slot_stride * ESZ;
+    int lrow[NL], lchunk[NL];
+    uint32_t koff[NL], voff[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int idx = i * 64 + lane;
+        lrow[i] = idx / CH;
+        lchunk[i] = idx % CH;
+        koff[i] = static_cast<uint32_t>(lrow[i] * kslot_bytes) + 16u * lchunk[i];
+        voff[i] = static_cast<uint32_t>(lrow[i] * vslot_bytes) + 16u * lchunk[i];
+    }
 
-    // element offset of key j0 + delta (j0 = first key of the tile, delta < 64)
-    auto key_off = [&](int j0, int delta, int phys0, int r0, int64_t blk_stride,
-                       int64_t slot_stride, int64_t head_off) -> int64_t {
-        if (one_block_per_tile) {
-            return static_cast<int64_t>(phys0) * blk_stride +
-                   static_cast<int64_t>(r0 + delta) * slot_stride + head_off;
-        }
-        const int u = r0 + delta;
-        const int nb = static_cast<int>((static_cast<float>(u) + 0.5f) * inv_bs);
-        const int phys = trow[j0 / bs + nb];
-        return static_cast<int64_t>(phys) * blk_stride +
-               static_cast<int64_t>(u - nb * bs) * slot_stride + head_off;
-    };
-
-    u32x4 kreg[NK];
-    u32x4 vreg[NV][4];
+    u32x4 kreg[NL], vreg[NL];
     auto load_tile = [&](int jt) {
         const int j0 = jt * BN;
-        const int blk = j0 / bs;
-        const int r0 = j0 - blk * bs;
-        const int phys0 = one_block_per_tile ? trow[blk] : 0;
+        // a 16-key group wholly past kvlen re-reads the tile's first group (its V rows
+        // are zeroed before they reach LDS, its K rows are masked)
+        const int tok0 = (j0 + 16 * wave < kvlen) ? j0 + 16 * wave : j0;
+        const int blk = tok0 / bs;
+        const int slot0 = tok0 - blk * bs;
+        const int e = ctab[blk];
+        const char* kb = kpool + e * kblk_bytes + slot0 * kslot_bytes;
+        const char* vb = vpool + e * vblk_bytes + slot0 * vslot_bytes;
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int idx = i * 256 + tid;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            if constexpr (!I8) {
-                const int delta = idx / CH, chunk = idx % CH;
-                const bool ok = (idx < BN * CH) && (j0 + delta < kvlen);
-                if (ok) {
-                    const uint16_t* p = static_cast<const uint16_t*>(a.k) +
-                                        key_off(j0, delta, phys0, r0, a.k_blk_stride, a.k_slot_stride, k_head_off);
-                    kreg[i] = *reinterpret_cast<const u32x4*>(p + 8 * chunk);
-                } else {
-                    kreg[i] = z;
-                }
-            } else {
-                constexpr int CH16 = D / 16;
-                const int delta = idx / CH16, chunk = idx % CH16;
-                const bool ok = (idx < BN * CH16) && (j0 + delta < kvlen);
-                if (ok) {
-                    const int8_t* p = static_cast<const int8_t*>(a.k) +
-                                      key_off(j0, delta, phys0, r0, a.k_blk_stride, a.k_slot_stride, k_head_off);
-                    kreg[i] = *reinterpret_cast<const u32x4*>(p + 16 * chunk);
-                } else {
-                    kreg[i] = z;
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int sb = i * 256 + tid;            // sub-block: keys 4*tg4.., d 8*dg..
-            const int dg = sb % CH, tg4 = sb / CH;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int delta = 4 * tg4 + c;
-                const bool ok = (sb < 16 * CH) && (j0 + delta < kvlen);
-                u32x4 z = {0u, 0u, 0u, 0u};
-                if (!ok) {
-                    vreg[i][c] = z;
-                    continue;
-                }
-                const int64_t off = key_off(j0, delta, phys0, r0, a.v_blk_stride, a.v_slot_stride, v_head_off);
-                if constexpr (!I8) {
-                    vreg[i][c] = *reinterpret_cast<const u32x4*>(
-                        static_cast<const uint16_t*>(a.v) + off + 8 * dg);
-                } else {
-                    const u32x2 raw = *reinterpret_cast<const u32x2*>(
-                        static_cast<const int8_t*>(a.v) + off + 8 * dg);
-                    const u32x2 c0 = i8x4_to_f16x4(raw.x), c1 = i8x4_to_f16x4(raw.y);
-                    vreg[i][c] = u32x4{c0.x, c0.y, c1.x, c1.y};
-                }
-            }
+        for (int i = 0; i < NL; ++i) {
+            kreg[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
+            vreg[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, int jt) {
+        const int j0 = jt * BN;
         uint16_t* ks = s_k[buf];
         uint16_t* vs = s_v[buf];
+        const bool tail = j0 + BN > kvlen;
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int idx = i * 256 + tid;
+        for (int i = 0; i < NL; ++i) {
+            const int row = 16 * wave + lrow[i];
+            u32x4 v = vreg[i];
+            if (tail && j0 + row >= kvlen) v = u32x4{0u, 0u, 0u, 0u};   // int8 0 -> f16 0
             if constexpr (!I8) {
-                if (idx < BN * CH) {
-                    const int delta = idx / CH, chunk = idx % CH;
-                    *reinterpret_cast<u32x4*>(ks + delta * KLD + 8 * chunk) = kreg[i];
-                }
+                *reinterpret_cast<u32x4*>(ks + row * KLD + EPC * lchunk[i]) = kreg[i];
+                *reinterpret_cast<u32x4*>(vs + row * VLD + EPC * lchunk[i]) = v;
             } else {
-                constexpr int CH16 = D / 16;
-                if (idx < BN * CH16) {
-                    const int delta = idx / CH16, chunk = idx % CH16;
-                    const u32x2 c0 = i8x4_to_f16x4(kreg[i].x), c1 = i8x4_to_f16x4(kreg[i].y);
-                    const u32x2 c2 = i8x4_to_f16x4(kreg[i].z), c3 = i8x4_to_f16x4(kreg[i].w);
-                    uint16_t* dst = ks + delta * KLD + 16 * chunk;
-                    *reinterpret_cast<u32x4*>(dst) = u32x4{c0.x, c0.y, c1.x, c1.y};
-                    *reinterpret_cast<u32x4*>(dst + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int sb = i * 256 + tid;
-            if (sb < 16 * CH) {
-                const int dg = sb % CH, tg4 = sb / CH;
-                const int p0 = vt_pos4(tg4);
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const uint32_t w0 = vreg[i][0][n >> 1], w1 = vreg[i][1][n >> 1];
-                    const uint32_t w2 = vreg[i][2][n >> 1], w3 = vreg[i][3][n >> 1];
-                    u32x2 t;
-                    t.x = (n & 1) ? pack_hi(w0, w1) : pack_lo(w0, w1);
-                    t.y = (n & 1) ? pack_hi(w2, w3) : pack_lo(w2, w3);
-                    *reinterpret_cast<u32x2*>(vs + (8 * dg + n) * VLD + p0) = t;
-                }
+                const u32x4 kr = kreg[i];
+                u32x2 c0 = i8x4_to_f16x4(kr.x), c1 = i8x4_to_f16x4(kr.y);
+                u32x2 c2 = i8x4_to_f16x4(kr.z), c3 = i8x4_to_f16x4(kr.w);
+                uint16_t* kd = ks + row * KLD + EPC * lchunk[i];
+                *reinterpret_cast<u32x4*>(kd) = u32x4{c0.x, c0.y, c1.x, c1.y};
+                *reinterpret_cast<u32x4*>(kd + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
+                c0 = i8x4_to_f16x4(v.x), c1 = i8x4_to_f16x4(v.y);
+                c2 = i8x4_to_f16x4(v.z), c3 = i8x4_to_f16x4(v.w);
+                uint16_t* vd = vs + row * VLD + EPC * lchunk[i];
+                *reinterpret_cast<u32x4*>(vd) = u32x4{c0.x, c0.y, c1.x, c1.y};
+                *reinterpret_cast<u32x4*>(vd + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
             }
         }
     };
 
+    // transposed-read coordinates: lane group G = lane / 16 covers d half G % 2 and key
+    // half g2; inside the group lane 4*jj + pp reads key row jj, columns 4*pp .. 4*pp+3
+    const int tr_row = 4 * g2 + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
     // --------------------------------------------------------------- state
-    float m_run = -INFINITY, l_run = 0.0f;
+    float m_ref = -INFINITY;              // reference row max (log2 units)
+    float l_run = 0.0f;
     f32x16 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -276,7 +237,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     if (ktiles > 0) load_tile(0);
     for (int jt = 0; jt < ktiles; ++jt) {
         const int buf = jt & 1;
-        store_tile(buf);
+        store_tile(buf, jt);
         __syncthreads();
         if (jt + 1 < ktiles) load_tile(jt + 1);
 
@@ -304,16 +265,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 if constexpr (I8) sacc[mt] = mfma32x32x16<false>(kop, qlo[ks_i], sacc[mt]);
             }
         }
-        // ---- scale, bias, mask; key of sacc[mt][r] = j0 + 32mt + 8(r/4) + 4*g2 + r%4
-        const float bias0 = slope2 * static_cast<float>(j0 + 4 * g2 - pos);
+        // ---- scores relative to the reference max; key of sacc[mt][r] is
+        //      j0 + 32mt + 8(r/4) + 4*g2 + r%4
+        const float mo = (m_ref == -INFINITY) ? 0.0f : m_ref;
+        const float base = (alibi ? slope2 * static_cast<float>(j0 + 4 * g2 - pos) : 0.0f) - mo;
         float tmax = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int dj = 32 * mt + 8 * (r >> 2) + (r & 3);
-                float x = sacc[mt][r] * s_mul;
-                if (a.mask_type == PA_MASK_ALIBI) x += bias0 + slope2 * static_cast<float>(dj);
+                const float b = alibi ? fmaf(slope2, static_cast<float>(dj), base) : base;
+                float x = fmaf(sacc[mt][r], s_mul, b);
                 if (need_mask) {
                     const int j = j0 + 4 * g2 + dj;
                     const bool vis = (j < kvlen) && (!causal || j <= pos);
@@ -324,23 +287,33 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             }
         }
         tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
+        // re-base rows whose max exceeds the reference by more than the slack (or that
+        // see their first key); the rest keep p <= 2^slack
+        const bool grow = (tmax > kRescaleSlack) || (m_ref == -INFINITY && tmax > -INFINITY);
+        if (__any(grow)) {
+            const float up = grow ? tmax : 0.0f;
+            const float alpha = grow ? fast_exp2(m_ref - (mo + up)) : 1.0f;
+            m_ref = grow ? mo + up : m_ref;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[mt][r] -= up;
+            }
+        }
         float psum = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(sacc[mt][r] - m_use);
+                const float p = fast_exp2(sacc[mt][r]);
                 sacc[mt][r] = p;
                 psum += p;
             }
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        l_run += psum;
 
         // ---- P^T operands: k-step kt holds keys 16kt + 8(s/4) + 4*g2 + s%4, s = 0..7
         u32x4 pop[4];
@@ -351,14 +324,17 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < 4; ++i)
                 pop[kt][i] = pack2<MBF>(sacc[mt][rb + 2 * i], sacc[mt][rb + 2 * i + 1]);
         }
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T, V^T operands by transposed reads of row-major V: the first
+        //      read gives keys 16kt + 4*g2 + 0..3, the second 16kt + 8 + 4*g2 + 0..3
         const uint16_t* vs = s_v[buf];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const u32x4 vop = *reinterpret_cast<const u32x4*>(
-                    vs + (dt * 32 + qcol) * VLD + 16 * kt + 8 * g2);
+                const uint16_t* p0 = vs + (16 * kt + tr_row) * VLD + dt * 32 + tr_col;
+                const u32x2 lo = lds_read_tr16(p0);
+                const u32x2 hi = lds_read_tr16(p0 + 8 * VLD);
+                const u32x4 vop = {lo.x, lo.y, hi.x, hi.y};
                 oacc[dt] = mfma32x32x16<MBF>(vop, pop[kt], oacc[dt]);
             }
         }
@@ -370,7 +346,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
     uint16_t* orow = static_cast<uint16_t*>(a.out) +
                      static_cast<int64_t>(it.qrow0 + qi) * a.out_tok_stride +
-                     static_cast<int64_t>(it.h) * a.out_head_stride;
+                     static_cast<int64_t>(h) * a.out_head_stride;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -395,8 +371,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     }
     if (g2 == 0 && a.lse != nullptr) {
-        a.lse[static_cast<int64_t>(it.qrow0 + qi) * a.lse_tok_stride + it.h] =
-            (L > 0.0f) ? (m_run + fast_log2(L)) * kLn2 : INFINITY;
+        a.lse[static_cast<int64_t>(it.qrow0 + qi) * a.lse_tok_stride + h] =
+            (L > 0.0f) ? (m_ref + fast_log2(L)) * kLn2 : INFINITY;
     }
 }
 

@@ -128,7 +128,7 @@ def test_plan_for_named_workloads(name):
     if info["mode"] == "decode":
         _check_decode_plan(info, ql, kv, w.kv_head_num, w.head_num // w.kv_head_num)
     else:
-        _check_prefill_plan(info, ql, kv, w.head_num, w.mask_type)
+        _check_prefill_plan(info, ql, kv, w.head_num, w.mask_type, w.head_num // w.kv_head_num)
 
 
 def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
@@ -171,27 +171,35 @@ def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
     assert info["partial_slots"] == len(slots_seen)
 
 
-def _check_prefill_plan(info, q_lens, kv_lens, H, mask):
+def _check_prefill_plan(info, q_lens, kv_lens, H, mask, group=None):
+    """Every (sequence, query head, query row) is covered exactly once; a workgroup's
+    heads share one kv head; ktiles counts the key tiles its rows can see."""
     items = info["prefill_items"]
     ks = [it[6] for it in items]
     assert ks == sorted(ks, reverse=True), "heaviest items first"
-    seen = set()
+    covered = {}
     q0 = np.concatenate([[0], np.cumsum(q_lens)])
-    for b, h, qbeg, qlen, kvlen, qrow0, ktiles in items:
-        assert (b, h, qbeg) not in seen
-        seen.add((b, h, qbeg))
+    for b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads in items:
+        assert heads in (1, 2, 4) and 128 % heads == 0
+        if group is not None:
+            assert group % heads == 0 and h // group == (h + heads - 1) // group
+        nrows = 128 // heads
         assert qlen == q_lens[b] and kvlen == kv_lens[b] and qrow0 == q0[b]
+        rows = range(qbeg, min(qbeg + nrows, qlen))
+        for hh in range(h, h + heads):
+            for i in rows:
+                key = (b, hh, i)
+                assert key not in covered
+                covered[key] = True
         # keys that the tile's rows can see, counted independently
-        rows = range(qbeg, min(qbeg + 128, qlen))
         if mask in (pa.PA_MASK_CAUSAL, pa.PA_MASK_ALIBI):
             last = max(kvlen - qlen + i for i in rows)
         else:
             last = kvlen - 1
         want = 0 if last < 0 else last // 64 + 1
         assert ktiles == want
-    expect = {(b, h, qb) for b, ql in enumerate(q_lens) for h in range(H)
-              for qb in range(0, ql, 128)}
-    assert seen == expect
+    expect = {(b, h, i) for b, ql in enumerate(q_lens) for h in range(H) for i in range(ql)}
+    assert set(covered) == expect
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -219,7 +227,7 @@ def test_random_prefill_plans(mask):
     c = Case(q_lens=ql, kv_lens=kv, H=4, Hkv=2, D=64, bs=16, dtype=pa.PA_F16, mask=mask)
     info = c.plan()
     assert info["mode"] == "prefill"
-    _check_prefill_plan(info, ql, kv, 4, mask)
+    _check_prefill_plan(info, ql, kv, 4, mask, 2)
     assert B == len(ql) and rng is not None
 
 
