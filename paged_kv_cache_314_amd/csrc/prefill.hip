@@ -25,6 +25,8 @@
 // tile suffices, and the next tile's global loads are in flight during the MFMA work.
 // int8 K/V are converted exactly to f16 on the way into LDS; the per-channel K scale is
 // folded into Q (kept to ~22 bits as an f16 hi + lo pair), the V scale into the output.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_kernels.h"
@@ -48,7 +50,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-template <int D, bool BF16, bool I8>
+// MASK: 0 = none, 1 = causal, 2 = ALiBi (+ causal), fixed at compile time so that the
+// per-score work of each variant holds no run-time selects.
+template <int D, bool BF16, bool I8, int MASK>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     constexpr bool MBF = BF16 && !I8;
     constexpr int KS = D / 16;            // QK k-steps (32x32x16)
@@ -75,8 +79,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     const int64_t kvh_off = static_cast<int64_t>(kvh) * D;      // into the [Hkv, D] scales
     const int kvlen = it.kvlen;
     const int qlen = it.qlen;
-    const bool causal = a.mask_type == PA_MASK_CAUSAL || a.mask_type == PA_MASK_ALIBI;
-    const bool alibi = a.mask_type == PA_MASK_ALIBI;
+    constexpr bool causal = MASK != 0;
+    constexpr bool alibi = MASK == 2;
     const int shift = kvlen - qlen;       // p_i = shift + i
 
     const int wave_q0 = it.qbeg + 32 * (wave / heads);      // first local row of the wave
@@ -233,20 +237,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
     }
 
-    const int ktiles = it.ktiles;
-    if (ktiles > 0) load_tile(0);
-    for (int jt = 0; jt < ktiles; ++jt) {
-        const int buf = jt & 1;
-        store_tile(buf, jt);
-        __syncthreads();
-        if (jt + 1 < ktiles) load_tile(jt + 1);
-
-        const int j0 = jt * BN;
-        // skip the MFMA work when no row of this wave sees any key of the tile
-        const bool active = wave_live && (!causal || j0 <= wave_pmax);
-        if (!active) continue;
-        const bool need_mask = (j0 + BN > kvlen) || (causal && j0 + BN - 1 > wave_pmin);
-
+    auto tile_body = [&](int buf, int j0, bool need_mask) {
         // ---- S^T = K Q^T
         f32x16 sacc[2];
 #pragma unroll
@@ -266,25 +257,41 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             }
         }
         // ---- scores relative to the reference max; key of sacc[mt][r] is
-        //      j0 + 32mt + 8(r/4) + 4*g2 + r%4
+        //      j0 + 4*g2 + dj with dj = 32mt + 8(r/4) + r%4
         const float mo = (m_ref == -INFINITY) ? 0.0f : m_ref;
-        const float base = (alibi ? slope2 * static_cast<float>(j0 + 4 * g2 - pos) : 0.0f) - mo;
-        float tmax = -INFINITY;
+        float base = -mo;
+        if constexpr (alibi) base += slope2 * static_cast<float>(j0 + 4 * g2 - pos);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int dj = 32 * mt + 8 * (r >> 2) + (r & 3);
-                const float b = alibi ? fmaf(slope2, static_cast<float>(dj), base) : base;
-                float x = fmaf(sacc[mt][r], s_mul, b);
-                if (need_mask) {
-                    const int j = j0 + 4 * g2 + dj;
-                    const bool vis = (j < kvlen) && (!causal || j <= pos);
-                    x = vis ? x : -INFINITY;
-                }
-                sacc[mt][r] = x;
-                tmax = fmaxf(tmax, x);
+                if constexpr (alibi)
+                    sacc[mt][r] = fmaf(sacc[mt][r], s_mul, fmaf(slope2, static_cast<float>(dj), base));
+                else
+                    sacc[mt][r] = fmaf(sacc[mt][r], s_mul, base);
             }
+        }
+        if (need_mask) {
+            // only tiles on the causal diagonal or past kvlen; the empty asm keeps the
+            // compiler from turning this wave-uniform branch into selects on every tile
+            asm volatile("" ::: "memory");
+            // visible keys: dj <= lim (j < kvlen, and j <= p_i when causal)
+            const int lim = (causal ? min(pos, kvlen - 1) : kvlen - 1) - (j0 + 4 * g2);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int dj = 32 * mt + 8 * (r >> 2) + (r & 3);
+                    sacc[mt][r] = (dj <= lim) ? sacc[mt][r] : -INFINITY;
+                }
+            }
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[mt][r]);
         }
         tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
         // re-base rows whose max exceeds the reference by more than the slack (or that
@@ -338,6 +345,22 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 oacc[dt] = mfma32x32x16<MBF>(vop, pop[kt], oacc[dt]);
             }
         }
+    };
+
+    const int ktiles = it.ktiles;
+    if (ktiles > 0) load_tile(0);
+    for (int jt = 0; jt < ktiles; ++jt) {
+        const int buf = jt & 1;
+        store_tile(buf, jt);
+        __syncthreads();
+        if (jt + 1 < ktiles) load_tile(jt + 1);
+
+        const int j0 = jt * BN;
+        // skip the MFMA work when no row of this wave sees any key of the tile
+        const bool active = wave_live && (!causal || j0 <= wave_pmax);
+        if (!active) continue;
+        const bool need_mask = (j0 + BN > kvlen) || (causal && j0 + BN - 1 > wave_pmin);
+        tile_body(buf, j0, need_mask);
     }
 
     // ------------------------------------------------------------- epilogue
@@ -378,7 +401,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
 template <int D, bool BF16, bool I8>
 hipError_t launch_prefill_t(const PrefillArgs& a, int n_items, hipStream_t stream) {
-    hipLaunchKernelGGL((prefill_kernel<D, BF16, I8>), dim3(n_items), dim3(256), 0, stream, a);
+    if (a.mask_type == PA_MASK_ALIBI)
+        hipLaunchKernelGGL((prefill_kernel<D, BF16, I8, 2>), dim3(n_items), dim3(256), 0, stream, a);
+    else if (a.mask_type == PA_MASK_CAUSAL)
+        hipLaunchKernelGGL((prefill_kernel<D, BF16, I8, 1>), dim3(n_items), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, BF16, I8, 0>), dim3(n_items), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
