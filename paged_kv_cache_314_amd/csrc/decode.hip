@@ -26,8 +26,8 @@
 // Streaming: every load of a tile is issued from one uniform (scalar) base plus a 32-bit
 // per-lane offset, without branches; rows past kvSeqLen are clamped to the last valid
 // row (their scores are masked, their V rows zeroed), and the next tile's loads are in
-// flight while the current tile is computed.  Block ids come from a lane-distributed
-// window of 64 table entries read with readlane, so the table costs no load per tile.
+// flight while the current tile is computed.  Block ids are read through the scalar
+// cache (one or two s_load per 32-token tile), so the table costs no vector load.
 #include <type_traits>
 
 #include "pa_device.h"
