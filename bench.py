@@ -20,7 +20,6 @@ events recorded on its launch stream around each launch.
 """
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -32,7 +31,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense MFMA, published
-KERNEL_SOURCES = {"decode": "decode.hip", "prefill": "prefill.hip"}
 
 
 def parse():
@@ -83,16 +81,12 @@ def algorithmic_counts(inp):
     return nbytes, flops
 
 
-def source_hash(kind):
-    path = os.path.join(ROOT, "paged_kv_cache_314_amd", "csrc", KERNEL_SOURCES[kind])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def traffic_from_profiles(workload, kind):
     """HBM bytes per launch measured with rocprofv3 counters, if a summary for this
     workload exists and was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}_counters.json")
+    from paged_kv_cache_314_amd.counter_summary import kernel_source_hash
+    kernel = f"{kind}_kernel"
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     try:
@@ -100,7 +94,7 @@ def traffic_from_profiles(workload, kind):
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_sha256_16") != source_hash(kind):
+    if d.get("source_sha256_16") != kernel_source_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
 

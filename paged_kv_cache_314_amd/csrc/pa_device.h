@@ -40,10 +40,33 @@ __device__ __forceinline__ uint32_t f32_to_half(float x) {
     }
 }
 
-// Two f32 -> one dword holding two 16-bit values (lo = a).
+// Two f32 -> one dword holding two 16-bit values (lo = a), round to nearest even; one
+// v_cvt_pk_{f16,bf16}_f32 on gfx950.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return f32_to_half<BF16>(a) | (f32_to_half<BF16>(b) << 16);
+    const f32x2_t v = {a, b};
+    if constexpr (BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// max over the two 32-lane halves of the wave (lane l and l ^ 32), one v_permlane32_swap
+__device__ __forceinline__ float max_halves(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    // elements go through scalars: a bit_cast of a vector element reads element 0 here
+    const uint32_t lo = r[0], hi = r[1];
+    return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+
+// sum over the two 32-lane halves of the wave (lane l and l ^ 32)
+__device__ __forceinline__ float sum_halves(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t lo = r[0], hi = r[1];
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
 }
 
 // Four int8 (one dword) -> four exact f16 values in two dwords.  Offset-binary trick:
@@ -116,6 +139,34 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     } else {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(
             __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
+// D(32x32 f32) += A(32x8) * B(8x32); lane l holds A row l%32 / B column l%32 with
+// k = 4*(l/32) .. +3 (two 16-bit values per dword).
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32x32x8(u32x2 a, u32x2 b, f32x16 c) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(
+            __builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x8f16(
+            __builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    }
+}
+
+// c + the two 16-bit values of dword a, in f32 (v_dot2 against (1, 1): the products
+// are exact, the sums are f32).
+template <bool BF16>
+__device__ __forceinline__ float dot2_ones(uint32_t a, float c) {
+    if constexpr (BF16) {
+        const bf16x2_t one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), one, c, false);
+    } else {
+        const f16x2_t one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), one, c, false);
     }
 }
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <sstream>
 
 #include "pa_internal.h"
@@ -162,6 +163,54 @@ int env_int(const char* name, int fallback) {
 }
 
 uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
+// Workgroups are handed to the 8 XCDs of the chip round-robin by index (workgroup i runs
+// on XCD i % 8), and each XCD has its own L2.  The query tiles of one (sequence, head
+// block) all read the same K/V, so they are placed on one XCD at neighbouring dispatch
+// positions: they start together, walk the keys at the same pace and share each K/V
+// tile through that L2 instead of each fetching it from HBM.  Clusters go to the least
+// loaded XCD, heaviest first; the per-XCD lists are padded to equal length with no-op
+// items (heads == 0) so that list x, entry k lands at position 8 * k + x.
+std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items) {
+    constexpr int kXcds = 8;
+    struct Cluster { int64_t work = 0; std::vector<PrefillItem> members; };
+    std::vector<Cluster> clusters;
+    {
+        // a cluster holds at most 1/8 of the items, so that a few large clusters (one
+        // long sequence, few heads) still spread over every XCD
+        const size_t cap = std::max<size_t>(1, (items.size() + kXcds - 1) / kXcds);
+        std::map<std::pair<int32_t, int32_t>, size_t> index;   // (b, h) -> open cluster
+        for (const PrefillItem& it : items) {   // items arrive heaviest first
+            auto ins = index.emplace(std::make_pair(it.b, it.h), clusters.size());
+            if (ins.second) {
+                clusters.emplace_back();
+            } else if (clusters[ins.first->second].members.size() == cap) {
+                ins.first->second = clusters.size();
+                clusters.emplace_back();
+            }
+            Cluster& c = clusters[ins.first->second];
+            c.work += int64_t(it.ktiles) + 1;
+            c.members.push_back(it);
+        }
+    }
+    std::stable_sort(clusters.begin(), clusters.end(),
+                     [](const Cluster& x, const Cluster& y) { return x.work > y.work; });
+    std::vector<std::vector<PrefillItem>> lists(kXcds);
+    int64_t load[kXcds] = {};
+    for (const Cluster& c : clusters) {
+        int x = 0;
+        for (int i = 1; i < kXcds; ++i)
+            if (load[i] < load[x]) x = i;
+        load[x] += c.work;
+        lists[x].insert(lists[x].end(), c.members.begin(), c.members.end());
+    }
+    size_t len = 0;
+    for (const auto& l : lists) len = std::max(len, l.size());
+    std::vector<PrefillItem> out(len * kXcds);   // value-initialised: heads == 0 = no-op
+    for (int x = 0; x < kXcds; ++x)
+        for (size_t k = 0; k < lists[x].size(); ++k) out[k * kXcds + x] = lists[x][k];
+    return out;
+}
 
 void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
                const pa_tensor* blockTables, const pa_tensor* mask, const pa_tensor* seqLen,
@@ -509,6 +558,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         }
         std::stable_sort(p.prefill_items.begin(), p.prefill_items.end(),
                          [](const PrefillItem& x, const PrefillItem& y) { return x.ktiles > y.ktiles; });
+        if (env_int("PA_PREFILL_XCD_ORDER", 1) != 0) p.prefill_items = xcd_order(p.prefill_items);
         p.off_items = 0;
         p.items_bytes = align256(p.prefill_items.size() * sizeof(PrefillItem));
         p.workspace_bytes = 0;

@@ -10,7 +10,8 @@
 // One workgroup = 4 waves covering `heads` (1, 2 or 4) query heads of one kv group and
 // 128 / heads query rows; wave w owns head h + w % heads and 32 rows.  All heads of the
 // workgroup read the same K/V, so each key tile is staged in LDS once for all of them.
-// Keys are visited in tiles of 64 up to the last key any of the rows can see.  Per tile:
+// Keys are visited in tiles of 64, from the tile holding the last key any of the rows
+// can see down to key 0.  Per tile:
 //   wave w:      loads keys 16w .. 16w+15 of the tile (one 16-key group always lies in
 //                one cache block: a uniform base + constant per-lane offsets) into LDS,
 //                K and V both row-major
@@ -68,6 +69,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     __shared__ uint16_t s_v[2][BN * VLD];
 
     const PrefillItem it = a.items[blockIdx.x];
+    if (it.heads == 0) return;            // padding item of the XCD-ordered list
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -153,6 +155,34 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     }
     const float slope2 = alibi ? a.slopes[h] * kLog2e : 0.0f;
+    // ALiBi's within-tile part slope2 * dj (dj = key offset from the tile start) enters
+    // the QK accumulator as one extra rank-1 bf16 product per 32-key block:
+    // A[key m][k] = dj_m for k = 0..2 (exact), B[k][row] = c = slope2 / s_mul in raw
+    // score units, split into three bf16 terms (~24 bits); lanes 32..63 (k = 4..7) hold
+    // zeros.  If c is not usable (s_mul ~ 0, i.e. qkScale ~ 0) the row's Q*K term is
+    // below f32 resolution next to the bias: the row then takes Q = 0, s_mul = 1.
+    u32x2 bias_a[2] = {{0u, 0u}, {0u, 0u}}, bias_b = {0u, 0u};
+    if constexpr (alibi) {
+        float c = slope2 / s_mul;
+        if (!(fabsf(c) < 1e30f)) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qhi[ks] = qlo[ks] = u32x4{0u, 0u, 0u, 0u};
+            s_mul = 1.0f;
+            c = slope2;
+        }
+        if (g2 == 0) {
+            const uint32_t hi = f32_to_half<true>(c);
+            const float r1 = c - half_to_f32<true>(hi);
+            const uint32_t mid = f32_to_half<true>(r1);
+            const uint32_t lo = f32_to_half<true>(r1 - half_to_f32<true>(mid));
+            bias_b = u32x2{hi | (mid << 16), lo};
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const uint32_t d = f32_to_half<true>(static_cast<float>(32 * mt + qcol));
+                bias_a[mt] = u32x2{d | (d << 16), d};
+            }
+        }
+    }
 
     // ---------------------------------------------------------- tile loads
     // Wave w stages keys 16w .. 16w+15 of each tile.  They lie in one cache block, so
@@ -165,16 +195,16 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     const char* vpool = static_cast<const char*>(a.v) + static_cast<int64_t>(kvh) * a.v_head_stride * ESZ;
     const int64_t kblk_bytes = a.k_blk_stride * ESZ, vblk_bytes = a.v_blk_stride * ESZ;
     const int64_t kslot_bytes = a.k_slot_stride * ESZ, vslot_bytes = a.v_slot_stride * ESZ;
-    int lrow[NL], lchunk[NL];
-    uint32_t koff[NL], voff[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int idx = i * 64 + lane;
-        lrow[i] = idx / CH;
-        lchunk[i] = idx % CH;
-        koff[i] = static_cast<uint32_t>(lrow[i] * kslot_bytes) + 16u * lchunk[i];
-        voff[i] = static_cast<uint32_t>(lrow[i] * vslot_bytes) + 16u * lchunk[i];
-    }
+    // load i of a lane covers row RPI*i + lane / CH, 16-byte chunk lane % CH of the
+    // wave's 16-key group: one 32-bit lane offset, the row step goes into the scalar base
+    constexpr int RPI = 64 / CH;          // rows per load instruction
+    const int lrow = lane / CH, lch = lane % CH;
+    const uint32_t koff = static_cast<uint32_t>(lrow * kslot_bytes) + 16u * lch;
+    const uint32_t voff = static_cast<uint32_t>(lrow * vslot_bytes) + 16u * lch;
+    // LDS element offsets of the lane's first K / V row (row 16*wave + lrow)
+    constexpr int KLW = I8 ? 2 : 1;       // 16-byte LDS stores per loaded chunk
+    const int lds_k = (16 * wave + lrow) * KLD + EPC * lch;
+    const int lds_v = (16 * wave + lrow) * VLD + EPC * lch;
 
     u32x4 kreg[NL], vreg[NL];
     auto load_tile = [&](int jt) {
@@ -187,35 +217,49 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         const int e = ctab[blk];
         const char* kb = kpool + e * kblk_bytes + slot0 * kslot_bytes;
         const char* vb = vpool + e * vblk_bytes + slot0 * vslot_bytes;
+        // every load = uniform base (pinned to SGPRs) + the lane's 32-bit offset (kept
+        // 32-bit inside the loop), so that it takes the scalar-base form with no
+        // per-load address arithmetic
+        uint32_t ko = koff, vo = voff;
+        asm volatile("" : "+v"(ko), "+v"(vo));
+        using gptr = const __attribute__((address_space(1))) u32x4*;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            kreg[i] = *reinterpret_cast<const u32x4*>(kb + koff[i]);
-            vreg[i] = *reinterpret_cast<const u32x4*>(vb + voff[i]);
+            uint64_t kbi = reinterpret_cast<uintptr_t>(kb + i * RPI * kslot_bytes);
+            uint64_t vbi = reinterpret_cast<uintptr_t>(vb + i * RPI * vslot_bytes);
+            asm volatile("" : "+s"(kbi), "+s"(vbi));
+            kreg[i] = *reinterpret_cast<gptr>(kbi + ko);
+            vreg[i] = *reinterpret_cast<gptr>(vbi + vo);
         }
     };
     auto store_tile = [&](int buf, int jt) {
         const int j0 = jt * BN;
-        uint16_t* ks = s_k[buf];
-        uint16_t* vs = s_v[buf];
-        const bool tail = j0 + BN > kvlen;
+        uint16_t* ks = s_k[buf] + lds_k;
+        uint16_t* vs = s_v[buf] + lds_v;
+        if (j0 + BN > kvlen) {
+            // tail tile only (wave-uniform): zero the V rows past kvlen; the empty asm
+            // keeps the compiler from turning this into selects on every tile
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                if (j0 + 16 * wave + RPI * i + lrow >= kvlen) vreg[i] = u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int row = 16 * wave + lrow[i];
-            u32x4 v = vreg[i];
-            if (tail && j0 + row >= kvlen) v = u32x4{0u, 0u, 0u, 0u};   // int8 0 -> f16 0
             if constexpr (!I8) {
-                *reinterpret_cast<u32x4*>(ks + row * KLD + EPC * lchunk[i]) = kreg[i];
-                *reinterpret_cast<u32x4*>(vs + row * VLD + EPC * lchunk[i]) = v;
+                *reinterpret_cast<u32x4*>(ks + RPI * i * KLD) = kreg[i];
+                *reinterpret_cast<u32x4*>(vs + RPI * i * VLD) = vreg[i];
             } else {
-                const u32x4 kr = kreg[i];
+                static_assert(KLW == 2, "int8 chunks expand to two f16 chunks");
+                const u32x4 kr = kreg[i], v = vreg[i];
                 u32x2 c0 = i8x4_to_f16x4(kr.x), c1 = i8x4_to_f16x4(kr.y);
                 u32x2 c2 = i8x4_to_f16x4(kr.z), c3 = i8x4_to_f16x4(kr.w);
-                uint16_t* kd = ks + row * KLD + EPC * lchunk[i];
+                uint16_t* kd = ks + RPI * i * KLD;
                 *reinterpret_cast<u32x4*>(kd) = u32x4{c0.x, c0.y, c1.x, c1.y};
                 *reinterpret_cast<u32x4*>(kd + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
                 c0 = i8x4_to_f16x4(v.x), c1 = i8x4_to_f16x4(v.y);
                 c2 = i8x4_to_f16x4(v.z), c3 = i8x4_to_f16x4(v.w);
-                uint16_t* vd = vs + row * VLD + EPC * lchunk[i];
+                uint16_t* vd = vs + RPI * i * VLD;
                 *reinterpret_cast<u32x4*>(vd) = u32x4{c0.x, c0.y, c1.x, c1.y};
                 *reinterpret_cast<u32x4*>(vd + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
             }
@@ -256,22 +300,21 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 if constexpr (I8) sacc[mt] = mfma32x32x16<false>(kop, qlo[ks_i], sacc[mt]);
             }
         }
+        if constexpr (alibi) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32x32x8<true>(bias_a[mt], bias_b, sacc[mt]);
+        }
         // ---- scores relative to the reference max; key of sacc[mt][r] is
         //      j0 + 4*g2 + dj with dj = 32mt + 8(r/4) + r%4
         const float mo = (m_ref == -INFINITY) ? 0.0f : m_ref;
         float base = -mo;
-        if constexpr (alibi) base += slope2 * static_cast<float>(j0 + 4 * g2 - pos);
+        if constexpr (alibi) base += slope2 * static_cast<float>(j0 - pos);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dj = 32 * mt + 8 * (r >> 2) + (r & 3);
-                if constexpr (alibi)
-                    sacc[mt][r] = fmaf(sacc[mt][r], s_mul, fmaf(slope2, static_cast<float>(dj), base));
-                else
-                    sacc[mt][r] = fmaf(sacc[mt][r], s_mul, base);
-            }
+            for (int r = 0; r < 16; ++r) sacc[mt][r] = fmaf(sacc[mt][r], s_mul, base);
         }
+
         if (need_mask) {
             // only tiles on the causal diagonal or past kvlen; the empty asm keeps the
             // compiler from turning this wave-uniform branch into selects on every tile
@@ -293,7 +336,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[mt][r]);
         }
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        tmax = max_halves(tmax);
         // re-base rows whose max exceeds the reference by more than the slack (or that
         // see their first key); the rest keep p <= 2^slack
         const bool grow = (tmax > kRescaleSlack) || (m_ref == -INFINITY && tmax > -INFINITY);
@@ -310,27 +353,30 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 for (int r = 0; r < 16; ++r) sacc[mt][r] -= up;
             }
         }
-        float psum = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(sacc[mt][r]);
-                sacc[mt][r] = p;
-                psum += p;
-            }
+            for (int r = 0; r < 16; ++r) sacc[mt][r] = fast_exp2(sacc[mt][r]);
         }
-        l_run += psum;
 
-        // ---- P^T operands: k-step kt holds keys 16kt + 8(s/4) + 4*g2 + s%4, s = 0..7
+        // ---- P^T operands: k-step kt holds keys 16kt + 8(s/4) + 4*g2 + s%4, s = 0..7.
+        //      Row sums: f16 P (relative rounding <= 2^-11) is summed as rounded, two
+        //      values per v_dot2; bf16 rounding (2^-9) would show in lse, so bf16 sums
+        //      the f32 values.
         u32x4 pop[4];
+        float psum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int mt = kt >> 1, rb = 8 * (kt & 1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                pop[kt][i] = pack2<MBF>(sacc[mt][rb + 2 * i], sacc[mt][rb + 2 * i + 1]);
+            for (int i = 0; i < 4; ++i) {
+                const float p0 = sacc[mt][rb + 2 * i], p1 = sacc[mt][rb + 2 * i + 1];
+                pop[kt][i] = pack2<MBF>(p0, p1);
+                if constexpr (MBF) psum[i] += p0 + p1;
+                else psum[i] = dot2_ones<false>(pop[kt][i], psum[i]);
+            }
         }
+        l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
         // ---- O^T += V^T P^T, V^T operands by transposed reads of row-major V: the first
         //      read gives keys 16kt + 4*g2 + 0..3, the second 16kt + 8 + 4*g2 + 0..3
         const uint16_t* vs = s_v[buf];
@@ -347,13 +393,17 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     };
 
+    // Key tiles are visited from the last one down: under a causal mask (and even more
+    // with ALiBi, whose bias grows towards the diagonal) the first tile then holds the
+    // row maxima, so later tiles rarely re-base the running sums.
     const int ktiles = it.ktiles;
-    if (ktiles > 0) load_tile(0);
-    for (int jt = 0; jt < ktiles; ++jt) {
-        const int buf = jt & 1;
+    if (ktiles > 0) load_tile(ktiles - 1);
+    for (int n = 0; n < ktiles; ++n) {
+        const int jt = ktiles - 1 - n;
+        const int buf = n & 1;
         store_tile(buf, jt);
         __syncthreads();
-        if (jt + 1 < ktiles) load_tile(jt + 1);
+        if (jt > 0) load_tile(jt - 1);
 
         const int j0 = jt * BN;
         // skip the MFMA work when no row of this wave sees any key of the tile
@@ -364,7 +414,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
 
     // ------------------------------------------------------------- epilogue
-    const float L = l_run + shfl_xor_f(l_run, 32);
+    const float L = sum_halves(l_run);
     if (!qvalid) return;
     const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
     uint16_t* orow = static_cast<uint16_t*>(a.out) +

@@ -171,12 +171,29 @@ def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
     assert info["partial_slots"] == len(slots_seen)
 
 
+def _check_xcd_order(items, xcds=8):
+    """Items sharing (sequence, head block) sit on one XCD (position % 8) unless the
+    cluster exceeds 1/8 of the items; no-op padding (heads == 0) only ends a list."""
+    assert len(items) % xcds == 0
+    real = sum(1 for it in items if it[7] != 0)
+    cap = max(1, -(-real // xcds))
+    where = {}
+    for pos, it in enumerate(items):
+        if it[7] == 0:
+            assert all(v == 0 for v in it)
+            assert all(items[q][7] == 0 for q in range(pos, len(items), xcds)), "padding ends a list"
+            continue
+        where.setdefault((it[0], it[1]), []).append(pos % xcds)
+    for key, xs in where.items():
+        assert len(set(xs)) <= -(-len(xs) // cap), (key, xs)
+
+
 def _check_prefill_plan(info, q_lens, kv_lens, H, mask, group=None):
     """Every (sequence, query head, query row) is covered exactly once; a workgroup's
     heads share one kv head; ktiles counts the key tiles its rows can see."""
     items = info["prefill_items"]
-    ks = [it[6] for it in items]
-    assert ks == sorted(ks, reverse=True), "heaviest items first"
+    _check_xcd_order(items)
+    items = [it for it in items if it[7] != 0]
     covered = {}
     q0 = np.concatenate([[0], np.cumsum(q_lens)])
     for b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads in items:
