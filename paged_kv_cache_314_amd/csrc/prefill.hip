@@ -38,6 +38,9 @@ namespace {
 
 constexpr int BN = kPrefillBN;          // 64 keys per tile
 constexpr float kRescaleSlack = 8.0f;   // log2 units a row max may exceed its reference
+// s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16;
@@ -58,8 +61,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     constexpr bool MBF = BF16 && !I8;
     constexpr int KS = D / 16;            // QK k-steps (32x32x16)
     constexpr int DT = D / 32;            // PV output row blocks
-    constexpr int KLD = D + 8;            // K tile LDS row (16-bit elements)
-    constexpr int VLD = D + 32;           // V tile LDS row: conflict-free transposed reads
+    // 16-bit K/V go global -> LDS directly into swizzled, unpadded rows; int8 K/V pass
+    // through registers (exact conversion to f16) into padded rows
+    constexpr bool DIRECT = !I8;
+    constexpr int KLD = DIRECT ? D : D + 8;     // K tile LDS row (16-bit elements)
+    constexpr int VLD = DIRECT ? D : D + 32;    // V tile LDS row
     constexpr int ESZ = I8 ? 1 : 2;       // bytes per global K/V element
     constexpr int CH = D * ESZ / 16;      // 16-byte chunks per global K/V row
     constexpr int NL = 16 * CH / 64;      // 16-byte loads per lane for a 16-key group
@@ -207,35 +213,55 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     const int lds_v = (16 * wave + lrow) * VLD + EPC * lch;
 
     u32x4 kreg[NL], vreg[NL];
-    auto load_tile = [&](int jt) {
+    // uniform base of this wave's 16-key group of tile jt (a group wholly past kvlen
+    // re-reads the tile's first group: its V rows are zeroed before they reach LDS, its
+    // K rows are masked)
+    auto group_base = [&](const char* pool, int64_t blk_bytes, int64_t slot_bytes, int jt) {
         const int j0 = jt * BN;
-        // a 16-key group wholly past kvlen re-reads the tile's first group (its V rows
-        // are zeroed before they reach LDS, its K rows are masked)
         const int tok0 = (j0 + 16 * wave < kvlen) ? j0 + 16 * wave : j0;
         const int blk = tok0 / bs;
         const int slot0 = tok0 - blk * bs;
         const int e = ctab[blk];
-        const char* kb = kpool + e * kblk_bytes + slot0 * kslot_bytes;
-        const char* vb = vpool + e * vblk_bytes + slot0 * vslot_bytes;
-        // every load = uniform base (pinned to SGPRs) + the lane's 32-bit offset (kept
-        // 32-bit inside the loop), so that it takes the scalar-base form with no
-        // per-load address arithmetic
-        uint32_t ko = koff, vo = voff;
-        asm volatile("" : "+v"(ko), "+v"(vo));
-        using gptr = const __attribute__((address_space(1))) u32x4*;
+        return pool + e * blk_bytes + slot0 * slot_bytes;
+    };
+    // every load = uniform base (pinned to SGPRs) + the lane's 32-bit offset (kept 32-bit
+    // inside the loop), so that it takes the scalar-base form with no per-load address
+    // arithmetic
+    using gptr = const __attribute__((address_space(1))) u32x4*;
+    auto load_rows = [&](u32x4 (&reg)[NL], const char* base, int64_t slot_bytes, uint32_t off) {
+        asm volatile("" : "+v"(off));
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            uint64_t kbi = reinterpret_cast<uintptr_t>(kb + i * RPI * kslot_bytes);
-            uint64_t vbi = reinterpret_cast<uintptr_t>(vb + i * RPI * vslot_bytes);
-            asm volatile("" : "+s"(kbi), "+s"(vbi));
-            kreg[i] = *reinterpret_cast<gptr>(kbi + ko);
-            vreg[i] = *reinterpret_cast<gptr>(vbi + vo);
+            uint64_t bi = reinterpret_cast<uintptr_t>(base + i * RPI * slot_bytes);
+            asm volatile("" : "+s"(bi));
+            reg[i] = *reinterpret_cast<gptr>(bi + off);
         }
     };
-    auto store_tile = [&](int buf, int jt) {
-        const int j0 = jt * BN;
+    auto load_k = [&](int jt) {
+        load_rows(kreg, group_base(kpool, kblk_bytes, kslot_bytes, jt), kslot_bytes, koff);
+    };
+    auto load_v = [&](int jt) {
+        load_rows(vreg, group_base(vpool, vblk_bytes, vslot_bytes, jt), vslot_bytes, voff);
+    };
+    // 16-byte chunk(s) to LDS; int8 chunks become two f16 chunks (exact)
+    auto put = [&](uint16_t* dst, const u32x4& x) {
+        if constexpr (!I8) {
+            *reinterpret_cast<u32x4*>(dst) = x;
+        } else {
+            static_assert(KLW == 2, "int8 chunks expand to two f16 chunks");
+            const u32x2 c0 = i8x4_to_f16x4(x.x), c1 = i8x4_to_f16x4(x.y);
+            const u32x2 c2 = i8x4_to_f16x4(x.z), c3 = i8x4_to_f16x4(x.w);
+            *reinterpret_cast<u32x4*>(dst) = u32x4{c0.x, c0.y, c1.x, c1.y};
+            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
+        }
+    };
+    auto store_k = [&](int buf) {
         uint16_t* ks = s_k[buf] + lds_k;
-        uint16_t* vs = s_v[buf] + lds_v;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) put(ks + RPI * i * KLD, kreg[i]);
+    };
+    auto store_v = [&](int buf, int jt) {
+        const int j0 = jt * BN;
         if (j0 + BN > kvlen) {
             // tail tile only (wave-uniform): zero the V rows past kvlen; the empty asm
             // keeps the compiler from turning this into selects on every tile
@@ -244,27 +270,73 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < NL; ++i)
                 if (j0 + 16 * wave + RPI * i + lrow >= kvlen) vreg[i] = u32x4{0u, 0u, 0u, 0u};
         }
+        uint16_t* vs = s_v[buf] + lds_v;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) put(vs + RPI * i * VLD, vreg[i]);
+    };
+
+    // ---- direct global -> LDS staging (16-bit K/V).  LDS rows hold D elements with no
+    //      padding; 16-byte chunk c of tile row r sits at position c ^ (r & 7) for K and
+    //      c ^ 2 (r & 3) for V, which keeps the K operand reads (8 consecutive rows, one
+    //      chunk) and the transposed V reads (4 rows, 2 chunks per 16 lanes) free of bank
+    //      conflicts.  global_load_lds_dwordx4 writes lane L's 16 bytes to slot L of a
+    //      1 KB run (RPI rows) at the uniform LDS address in M0, so lane L loads the
+    //      chunk that belongs at its slot.  Rows past kvlen re-read row kvlen - 1 (finite
+    //      values: their V rows meet P = 0, their K rows are masked).
+    auto kswz = [](int r) { return r & 7; };
+    auto vswz = [](int r) { return 2 * (r & 3); };
+    using gvoid = __attribute__((address_space(1))) void;
+    using lvoid = __attribute__((address_space(3))) void;
+    auto token_addr = [&](const char* pool, int64_t blk_bytes, int64_t slot_bytes, int tok) {
+        const int blk = tok / bs;
+        return pool + ctab[blk] * blk_bytes + (tok - blk * bs) * slot_bytes;
+    };
+    // one 16-key group: base = uniform address of source row 0, src[i] = the lane's
+    // source row (relative) of load i, dst = LDS row 0 of the group
+    auto issue_group = [&](const char* base, int64_t slot_bytes, uint16_t* dst, int ld,
+                           const int (&src)[NL], bool is_k) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            if constexpr (!I8) {
-                *reinterpret_cast<u32x4*>(ks + RPI * i * KLD) = kreg[i];
-                *reinterpret_cast<u32x4*>(vs + RPI * i * VLD) = vreg[i];
-            } else {
-                static_assert(KLW == 2, "int8 chunks expand to two f16 chunks");
-                const u32x4 kr = kreg[i], v = vreg[i];
-                u32x2 c0 = i8x4_to_f16x4(kr.x), c1 = i8x4_to_f16x4(kr.y);
-                u32x2 c2 = i8x4_to_f16x4(kr.z), c3 = i8x4_to_f16x4(kr.w);
-                uint16_t* kd = ks + RPI * i * KLD;
-                *reinterpret_cast<u32x4*>(kd) = u32x4{c0.x, c0.y, c1.x, c1.y};
-                *reinterpret_cast<u32x4*>(kd + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
-                c0 = i8x4_to_f16x4(v.x), c1 = i8x4_to_f16x4(v.y);
-                c2 = i8x4_to_f16x4(v.z), c3 = i8x4_to_f16x4(v.w);
-                uint16_t* vd = vs + RPI * i * VLD;
-                *reinterpret_cast<u32x4*>(vd) = u32x4{c0.x, c0.y, c1.x, c1.y};
-                *reinterpret_cast<u32x4*>(vd + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
-            }
+            const int r = RPI * i + lrow;                       // LDS row in the group
+            const int pos = lch ^ (is_k ? kswz(r) : vswz(r));   // the lane's slot holds
+            uint32_t off = static_cast<uint32_t>(src[i] * slot_bytes) + 16u * pos;
+            asm volatile("" : "+v"(off));
+            uint64_t bi = reinterpret_cast<uintptr_t>(base);
+            asm volatile("" : "+s"(bi));
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const gvoid*>(bi + off),
+                reinterpret_cast<lvoid*>(reinterpret_cast<uintptr_t>(dst + RPI * i * ld)), 16, 0, 0);
         }
     };
+    auto load_tile_direct = [&](int buf, int t) {
+        const int j0 = t * BN;
+        const int g0 = j0 + 16 * wave;
+        int src[NL];
+        int gb = g0;
+        if (j0 + BN <= kvlen) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) src[i] = RPI * i;
+        } else {
+            // tail tile (wave-uniform branch): clamp rows to kvlen - 1
+            asm volatile("" ::: "memory");
+            const int last = kvlen - 1;
+            gb = g0 <= last ? g0 : last;
+#pragma unroll
+            for (int i = 0; i < NL; ++i) src[i] = min(RPI * i + lrow, last - gb) - lrow;
+        }
+        // src[i] + lrow is the source row; fold lrow in here so the common case keeps
+        // loop-invariant offsets
+#pragma unroll
+        for (int i = 0; i < NL; ++i) src[i] += lrow;
+        issue_group(token_addr(kpool, kblk_bytes, kslot_bytes, gb), kslot_bytes,
+                    s_k[buf] + 16 * wave * KLD, KLD, src, true);
+        issue_group(token_addr(vpool, vblk_bytes, vslot_bytes, gb), vslot_bytes,
+                    s_v[buf] + 16 * wave * VLD, VLD, src, false);
+    };
+
+    // element offset of 16-byte chunk c of K / V tile row r
+    auto kpos = [&](int r, int c) { return r * KLD + 8 * (DIRECT ? (c ^ kswz(r)) : c); };
+    auto vpos = [&](int r, int c) { return r * VLD + 8 * (DIRECT ? (c ^ vswz(r)) : c); };
 
     // transposed-read coordinates: lane group G = lane / 16 covers d half G % 2 and key
     // half g2; inside the group lane 4*jj + pp reads key row jj, columns 4*pp .. 4*pp+3
@@ -281,9 +353,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
     }
 
-    auto tile_body = [&](int buf, int j0, bool need_mask) {
-        // ---- S^T = K Q^T
-        f32x16 sacc[2];
+    // ---- stage 1: S^T = K Q^T for the K tile in s_k[buf] (plus the ALiBi term)
+    auto qk = [&](int buf, f32x16 (&sacc)[2]) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -295,7 +366,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const u32x4 kop = *reinterpret_cast<const u32x4*>(
-                    ks + (mt * 32 + qcol) * KLD + 16 * ks_i + 8 * g2);
+                    ks + kpos(mt * 32 + qcol, 2 * ks_i + g2));
                 sacc[mt] = mfma32x32x16<MBF>(kop, qhi[ks_i], sacc[mt]);
                 if constexpr (I8) sacc[mt] = mfma32x32x16<false>(kop, qlo[ks_i], sacc[mt]);
             }
@@ -304,8 +375,25 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma32x32x8<true>(bias_a[mt], bias_b, sacc[mt]);
         }
-        // ---- scores relative to the reference max; key of sacc[mt][r] is
-        //      j0 + 4*g2 + dj with dj = 32mt + 8(r/4) + r%4
+        if constexpr (!I8) {
+            // keep four operand reads in flight ahead of the MFMAs that consume them
+            constexpr int NR = 2 * KS;
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);          // DS read
+#pragma unroll
+            for (int i = 0; i < NR - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, alibi ? 6 : 4, 0);
+        }
+    };
+
+    // ---- scores of one tile relative to the reference max, masked, then the row max:
+    //      rows whose max exceeds the reference by more than the slack (or that see
+    //      their first key) are re-based, which rescales O and l.  Afterwards every
+    //      score is <= slack, so exp2 of it is safe to round to 16 bits.
+    //      The key of sacc[mt][r] is j0 + 4*g2 + dj, dj = 32mt + 8(r/4) + r%4.
+    auto scores = [&](f32x16 (&sacc)[2], int j0, bool need_mask) {
         const float mo = (m_ref == -INFINITY) ? 0.0f : m_ref;
         float base = -mo;
         if constexpr (alibi) base += slope2 * static_cast<float>(j0 - pos);
@@ -314,7 +402,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[mt][r] = fmaf(sacc[mt][r], s_mul, base);
         }
-
         if (need_mask) {
             // only tiles on the causal diagonal or past kvlen; the empty asm keeps the
             // compiler from turning this wave-uniform branch into selects on every tile
@@ -337,8 +424,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[mt][r]);
         }
         tmax = max_halves(tmax);
-        // re-base rows whose max exceeds the reference by more than the slack (or that
-        // see their first key); the rest keep p <= 2^slack
         const bool grow = (tmax > kRescaleSlack) || (m_ref == -INFINITY && tmax > -INFINITY);
         if (__any(grow)) {
             const float up = grow ? tmax : 0.0f;
@@ -353,40 +438,42 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 for (int r = 0; r < 16; ++r) sacc[mt][r] -= up;
             }
         }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[mt][r] = fast_exp2(sacc[mt][r]);
-        }
+    };
 
-        // ---- P^T operands: k-step kt holds keys 16kt + 8(s/4) + 4*g2 + s%4, s = 0..7.
-        //      Row sums: f16 P (relative rounding <= 2^-11) is summed as rounded, two
-        //      values per v_dot2; bf16 rounding (2^-9) would show in lse, so bf16 sums
-        //      the f32 values.
-        u32x4 pop[4];
+    // ---- P = exp2(scores), packed as the P^T operands (k-step kt holds keys
+    //      16kt + 8(s/4) + 4*g2 + s%4, s = 0..7), and the row sums.  f16 P (relative
+    //      rounding <= 2^-11) is summed as rounded, two values per v_dot2; bf16 rounding
+    //      (2^-9) would show in lse, so bf16 sums the f32 values.
+    auto probs = [&](f32x16 (&sacc)[2], u32x4 (&pop)[4]) {
         float psum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int mt = kt >> 1, rb = 8 * (kt & 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p0 = sacc[mt][rb + 2 * i], p1 = sacc[mt][rb + 2 * i + 1];
+                const float p0 = fast_exp2(sacc[mt][rb + 2 * i]);
+                const float p1 = fast_exp2(sacc[mt][rb + 2 * i + 1]);
                 pop[kt][i] = pack2<MBF>(p0, p1);
                 if constexpr (MBF) psum[i] += p0 + p1;
                 else psum[i] = dot2_ones<false>(pop[kt][i], psum[i]);
             }
         }
         l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
-        // ---- O^T += V^T P^T, V^T operands by transposed reads of row-major V: the first
-        //      read gives keys 16kt + 4*g2 + 0..3, the second 16kt + 8 + 4*g2 + 0..3
+    };
+
+    // ---- O^T += V^T P^T with the V tile in s_v[buf], V^T operands by transposed reads of
+    //      row-major V: the first read gives keys 16kt + 4*g2 + 0..3, the second
+    //      16kt + 8 + 4*g2 + 0..3
+    auto pv = [&](const u32x4 (&pop)[4], int buf) {
         const uint16_t* vs = s_v[buf];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const uint16_t* p0 = vs + (16 * kt + tr_row) * VLD + dt * 32 + tr_col;
-                const u32x2 lo = lds_read_tr16(p0);
-                const u32x2 hi = lds_read_tr16(p0 + 8 * VLD);
+                // columns dt*32 + tr_col .. +3: chunk 4dt + tr_col/8, half (tr_col/4) & 1
+                const int c = 4 * dt + (tr_col >> 3), h4 = 4 * ((tr_col >> 2) & 1);
+                const u32x2 lo = lds_read_tr16(vs + vpos(16 * kt + tr_row, c) + h4);
+                const u32x2 hi = lds_read_tr16(vs + vpos(16 * kt + 8 + tr_row, c) + h4);
                 const u32x4 vop = {lo.x, lo.y, hi.x, hi.y};
                 oacc[dt] = mfma32x32x16<MBF>(vop, pop[kt], oacc[dt]);
             }
@@ -395,22 +482,52 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
     // Key tiles are visited from the last one down: under a causal mask (and even more
     // with ALiBi, whose bias grows towards the diagonal) the first tile then holds the
-    // row maxima, so later tiles rarely re-base the running sums.
-    const int ktiles = it.ktiles;
-    if (ktiles > 0) load_tile(ktiles - 1);
-    for (int n = 0; n < ktiles; ++n) {
-        const int jt = ktiles - 1 - n;
-        const int buf = n & 1;
-        store_tile(buf, jt);
-        __syncthreads();
-        if (jt > 0) load_tile(jt - 1);
+    // row maxima, so later tiles rarely re-base the running sums.  Tile t is staged in
+    // s_k[t % 2] / s_v[t % 2].  A wave works on tiles 0 .. t_act (the rows it owns see
+    // no key of a higher tile); tiles on the diagonal or past kvlen are masked.
+    const int T = it.ktiles - 1;
+    const int t_act = !wave_live ? -1
+                    : (!causal ? T : (wave_pmax < 0 ? -1 : min(T, wave_pmax / BN)));
+    auto need_mask = [&](int t) {
+        return (t * BN + BN > kvlen) || (causal && t * BN + BN - 1 > wave_pmin);
+    };
 
-        const int j0 = jt * BN;
-        // skip the MFMA work when no row of this wave sees any key of the tile
-        const bool active = wave_live && (!causal || j0 <= wave_pmax);
-        if (!active) continue;
-        const bool need_mask = (j0 + BN > kvlen) || (causal && j0 + BN - 1 > wave_pmin);
-        tile_body(buf, j0, need_mask);
+    // one stage per iteration: tile t - 1 loads while tile t is computed
+    auto compute = [&](int t) {
+        if (t <= t_act) {
+            f32x16 sacc[2];
+            u32x4 pop[4];
+            qk(t & 1, sacc);
+            scores(sacc, t * BN, need_mask(t));
+            probs(sacc, pop);
+            pv(pop, t & 1);
+        }
+    };
+    if constexpr (DIRECT) {
+        // the loads into s_*[(t-1) % 2] start after the barrier that follows every read
+        // of that buffer's previous tile (t + 1); vmcnt(0) + barrier publish them
+        if (T >= 0) load_tile_direct(T & 1, T);
+        for (int t = T; t >= 0; --t) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (t >= 1) load_tile_direct((t - 1) & 1, t - 1);
+            compute(t);
+        }
+    } else {
+        if (T >= 0) {
+            load_k(T);
+            load_v(T);
+        }
+        for (int t = T; t >= 0; --t) {
+            store_k(t & 1);
+            store_v(t & 1, t);
+            __syncthreads();
+            if (t >= 1) {
+                load_k(t - 1);
+                load_v(t - 1);
+            }
+            compute(t);
+        }
     }
 
     // ------------------------------------------------------------- epilogue
