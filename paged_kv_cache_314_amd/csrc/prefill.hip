@@ -276,15 +276,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     };
 
     // ---- direct global -> LDS staging (16-bit K/V).  LDS rows hold D elements with no
-    //      padding; 16-byte chunk c of tile row r sits at position c ^ (r & 7) for K and
-    //      c ^ 2 (r & 3) for V, which keeps the K operand reads (8 consecutive rows, one
-    //      chunk) and the transposed V reads (4 rows, 2 chunks per 16 lanes) free of bank
-    //      conflicts.  global_load_lds_dwordx4 writes lane L's 16 bytes to slot L of a
-    //      1 KB run (RPI rows) at the uniform LDS address in M0, so lane L loads the
-    //      chunk that belongs at its slot.  Rows past kvlen re-read row kvlen - 1 (finite
-    //      values: their V rows meet P = 0, their K rows are masked).
-    auto kswz = [](int r) { return r & 7; };
-    auto vswz = [](int r) { return 2 * (r & 3); };
+    //      padding, and LDS serves 256 bytes (64 banks) per cycle: 16 lanes of a
+    //      ds_read_b128, 32 lanes of a transposed ds_read_b64.  The K operand reads take
+    //      one chunk of 16 consecutive rows, the transposed V reads 4 chunks of 4 rows,
+    //      so 16-byte chunk c of tile row r sits at position c ^ kswz(r) / c ^ vswz(r),
+    //      which spreads each of those sets over all 16 chunk positions of a 256-byte
+    //      bank line (D = 64 rows pack two to a line).  global_load_lds_dwordx4 writes
+    //      lane L's 16 bytes to slot L of a 1 KB run (RPI rows) at the uniform LDS
+    //      address in M0, so lane L loads the chunk that belongs at its slot.  Rows past
+    //      kvlen re-read row kvlen - 1 (finite values: their V rows meet P = 0, their K
+    //      rows are masked).
+    auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+    auto vswz = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
     using gvoid = __attribute__((address_space(1))) void;
     using lvoid = __attribute__((address_space(3))) void;
     auto token_addr = [&](const char* pool, int64_t blk_bytes, int64_t slot_bytes, int tok) {
