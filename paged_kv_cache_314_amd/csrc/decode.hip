@@ -38,6 +38,8 @@ namespace pa {
 
 namespace {
 
+constexpr float kRescaleSlack = 8.0f;   // log2 units a head's max may exceed its reference
+
 // d-chunk (in units of 8 elements) that lane group qg covers at QK k-step kk.
 // 16-bit K rows: chunk 4*kk + qg (a load instruction covers 64 contiguous bytes per row).
 // int8 K rows: each lane loads 16 bytes = 2 chunks, chunks 2*(qg + 4*(kk/2)) + kk%2.
@@ -54,7 +56,7 @@ struct DecodeTileRegs {
     std::conditional_t<I8, u32x2, u32x4> v[8];
 };
 
-template <int D, bool BF16, bool I8>
+template <int D, bool BF16, bool I8, bool ALIBI>
 __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     constexpr int KK = D / 32;                 // QK k-steps
     constexpr int KP = D / 64;                 // int8 16-byte loads per K row
@@ -93,61 +95,64 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
         }
         s_mul = a.scale_log2;
     } else {
-        // q' = q * sK * qkScale * log2(e), brought to |q'| < 2^14 by a power of two and
-        // split into f16 hi + lo, so that the f16 MFMA sees q' to ~22 bits.
+        // q' = q * sK * qkScale * log2(e) per channel.  Per head, y = q' * 127 / amax is
+        // split into two int8 parts, hi = rint(y) and lo = rint((y - hi) * 256), so that
+        // the int8 MFMA gives K.y = acc_hi + acc_lo / 256 (exact integer sums) to about
+        // 15 bits relative to the head's largest |q'|; the score in log2 units is then
+        // (acc_hi * 256 + acc_lo) * amax / (127 * 256).
         const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                                static_cast<int64_t>(it.qrow) * a.q_tok_stride +
                                static_cast<int64_t>(head) * a.q_head_stride;
-        float qf[KK][8];
+        float qf[KP][16];
         float amax = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int d0 = 8 * dchunk<I8>(qg, kk);
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (hvalid) raw = *reinterpret_cast<const u32x4*>(qrow + d0);
+        for (int kp = 0; kp < KP; ++kp) {
+            const int d0 = 64 * kp + 16 * qg;       // the lane's 16 channels of k-step kp
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w = raw[e >> 1];
-                const float qv = half_to_f32<BF16>((e & 1) ? (w >> 16) : (w & 0xffffu));
-                const int d = d0 + e;
-                float sk;
-                if (a.scale_is_f32) {
-                    sk = static_cast<const float*>(a.kscale)[it.kvh * D + d];
-                } else {
-                    sk = half_to_f32<BF16>(static_cast<const uint16_t*>(a.kscale)[it.kvh * D + d]);
+            for (int h8 = 0; h8 < 2; ++h8) {
+                u32x4 raw = {0u, 0u, 0u, 0u};
+                if (hvalid) raw = *reinterpret_cast<const u32x4*>(qrow + d0 + 8 * h8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = raw[e >> 1];
+                    const float qv = half_to_f32<BF16>((e & 1) ? (w >> 16) : (w & 0xffffu));
+                    const int d = d0 + 8 * h8 + e;
+                    float sk;
+                    if (a.scale_is_f32) {
+                        sk = static_cast<const float*>(a.kscale)[it.kvh * D + d];
+                    } else {
+                        sk = half_to_f32<BF16>(static_cast<const uint16_t*>(a.kscale)[it.kvh * D + d]);
+                    }
+                    qf[kp][8 * h8 + e] = qv * sk * a.scale_log2;
+                    amax = fmaxf(amax, fabsf(qf[kp][8 * h8 + e]));
                 }
-                qf[kk][e] = qv * sk * a.scale_log2;
-                amax = fmaxf(amax, fabsf(qf[kk][e]));
             }
         }
         amax = fmaxf(amax, shfl_xor_f(amax, 16));
         amax = fmaxf(amax, shfl_xor_f(amax, 32));
-        int ex = 0;
-        if (amax > 0.0f && amax < INFINITY) {
-            int x;
-            frexpf(amax, &x);                  // amax = f * 2^x, f in [0.5, 1)
-            ex = 14 - x;
-            ex = ex > 120 ? 120 : (ex < -120 ? -120 : ex);
-        }
-        const float up = ldexpf(1.0f, ex);
-        s_mul = ldexpf(1.0f, -ex);
+        const bool ok = amax > 0.0f && amax < INFINITY;
+        const float inv = ok ? 127.0f / amax : 0.0f;
+        s_mul = ok ? amax * (1.0f / (127.0f * 256.0f)) : 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+        for (int kp = 0; kp < KP; ++kp) {
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const float x0 = qf[kk][e] * up, x1 = qf[kk][e + 1] * up;
-                const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
-                const _Float16 l0 = static_cast<_Float16>(x0 - static_cast<float>(h0));
-                const _Float16 l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
-                qhi[kk][e >> 1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
-                                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
-                qlo[kk][e >> 1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l0)) |
-                                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l1)) << 16);
+            for (int w = 0; w < 4; ++w) {
+                uint32_t hw = 0u, lw = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = qf[kp][4 * w + e] * inv;
+                    const float hi = rintf(y);
+                    const float lo = fminf(fmaxf(rintf((y - hi) * 256.0f), -127.0f), 127.0f);
+                    hw |= (static_cast<uint32_t>(static_cast<int>(hi)) & 0xffu) << (8 * e);
+                    lw |= (static_cast<uint32_t>(static_cast<int>(lo)) & 0xffu) << (8 * e);
+                }
+                qhi[kp][w] = hw;
+                qlo[kp][w] = lw;
             }
         }
     }
     float slope2 = 0.0f;
-    if (a.mask_type == PA_MASK_ALIBI) slope2 = a.slopes[head] * kLog2e;
+    if constexpr (ALIBI) slope2 = a.slopes[head] * kLog2e;
     const int pos = kvlen - 1;                  // absolute position of the decode query
 
     // --------------------------------------------------------------- state
@@ -234,57 +239,67 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     // loads right after the transpose consumes V, so two tiles are always in flight.
     auto step = [&](Tile& t, const TileBase& cur, const TileBase& next) {
         const int T = cur.T;
-        // ---- S = K Q^T, scaled to log2 units, bias + mask
+        // ---- S = K Q^T, scaled to log2 units, bias
         float s[8];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            f32x4 c;
             if constexpr (!I8) {
+                c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) c = mfma16x16x32<MBF>(t.k[m][kk], qhi[kk], c);
             } else {
+                i32x4 ch = {0, 0, 0, 0}, cl = {0, 0, 0, 0};
 #pragma unroll
                 for (int kp = 0; kp < KP; ++kp) {
-                    const u32x4 raw = t.k[m][kp];
-                    const u32x2 c0 = i8x4_to_f16x4(raw.x), c1 = i8x4_to_f16x4(raw.y);
-                    const u32x2 c2 = i8x4_to_f16x4(raw.z), c3 = i8x4_to_f16x4(raw.w);
-                    const u32x4 k0 = {c0.x, c0.y, c1.x, c1.y};
-                    const u32x4 k1 = {c2.x, c2.y, c3.x, c3.y};
-                    c = mfma16x16x32<false>(k0, qhi[2 * kp], c);
-                    c = mfma16x16x32<false>(k0, qlo[2 * kp], c);
-                    c = mfma16x16x32<false>(k1, qhi[2 * kp + 1], c);
-                    c = mfma16x16x32<false>(k1, qlo[2 * kp + 1], c);
+                    ch = mfma16x16x64_i8(t.k[m][kp], qhi[kp], ch);
+                    cl = mfma16x16x64_i8(t.k[m][kp], qlo[kp], cl);
                 }
+                // |acc_hi| <= 127*127*128, so acc_hi * 256 + acc_lo stays below 2^31
+#pragma unroll
+                for (int r = 0; r < 4; ++r) c[r] = static_cast<float>(ch[r] * 256 + cl[r]);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int j = T + 16 * m + 4 * qg + r;
                 float x = c[r] * s_mul;
-                if (a.mask_type == PA_MASK_ALIBI) x += slope2 * static_cast<float>(j - pos);
-                s[4 * m + r] = (j < kvlen) ? x : -INFINITY;
+                if constexpr (ALIBI) x += slope2 * static_cast<float>(T + 16 * m + 4 * qg + r - pos);
+                s[4 * m + r] = x;
             }
         }
         issue_k(t, next);
-        // ---- online softmax (head `col`; its 32 scores live in 4 lanes x 8)
+        if (T + kDecodeTile > kvlen) {
+            // last tile of the sequence only (wave-uniform): keys past kvlen; the empty asm
+            // keeps the compiler from turning this into selects on every tile
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (T + 16 * (i >> 2) + 4 * qg + (i & 3) >= kvlen) s[i] = -INFINITY;
+        }
+        // ---- online softmax (head `col`; its 32 scores live in 4 lanes x 8) against a
+        //      lazy reference m_run: heads whose tile max exceeds it by more than the slack
+        //      (or that see their first key) re-base it, rescaling O and l; the rest keep
+        //      p <= 2^slack
         float tmax = s[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, s[i]);
         tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
         tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        const bool grow = tmax > m_run + kRescaleSlack || (m_run == -INFINITY && tmax > -INFINITY);
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : m_run;
+            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
         float p[8];
-        float psum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             p[i] = fast_exp2(s[i] - m_use);
-            psum += p[i];
+            l_run += p[i];
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) acc[n] *= alpha;
         u32x4 pop;
         pop.x = pack2<MBF>(p[0], p[1]);
         pop.y = pack2<MBF>(p[2], p[3]);
@@ -461,7 +476,10 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 
 template <int D, bool BF16, bool I8>
 hipError_t launch_decode_t(const DecodeArgs& a, int n_items, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_kernel<D, BF16, I8>), dim3(n_items), dim3(256), 0, stream, a);
+    if (a.mask_type == PA_MASK_ALIBI)
+        hipLaunchKernelGGL((decode_kernel<D, BF16, I8, true>), dim3(n_items), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, BF16, I8, false>), dim3(n_items), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

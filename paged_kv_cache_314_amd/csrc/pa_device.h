@@ -142,6 +142,14 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     }
 }
 
+// D(16x16 i32) += A(16x64 i8) * B(64x16 i8); lane l holds A row l%16 / B column l%16,
+// 16 bytes of k each (lane group l/16 takes its own quarter of k); exact in i32.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 mfma16x16x64_i8(u32x4 a, u32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                                 __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
 // D(32x32 f32) += A(32x8) * B(8x32); lane l holds A row l%32 / B column l%32 with
 // k = 4*(l/32) .. +3 (two 16-bit values per dword).
 template <bool BF16>
