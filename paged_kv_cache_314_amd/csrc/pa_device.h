@@ -92,27 +92,28 @@ __device__ __forceinline__ u32x2 i8x4_to_f16x4(uint32_t w) {
     return r;
 }
 
-// Transpose-and-convert for the PV operand of an int8 V tile.  rows[r] holds 8 int8 of
-// token row r (columns c = 0..7, little-endian in .x then .y).  Returns, for column n,
-// the 8 f16 values rows[0..7][n] packed as the 4 dwords (rows 2i, 2i+1) of an MFMA
-// operand: out[n][i].  Offset-binary bytes (x ^ 0x80) are paired across two rows by one
-// perm, then each pair is placed under the f16 exponent and unbiased.
-__device__ __forceinline__ void i8_rows_to_f16_cols(const u32x2 (&rows)[8], u32x4 (&out)[8]) {
+// Transpose-and-convert for the PV operands of an int8 V tile, one half at a time.
+// rows[r] holds 8 int8 of token row r (columns c = 0..7, little-endian in .x then .y).
+// Half w returns, for column n = 4w + j, the 8 f16 values rows[0..7][n] packed as the
+// 4 dwords (rows 2i, 2i+1) of an MFMA operand: out[j][i].  Offset-binary bytes
+// (x ^ 0x80) are paired across two rows by one perm, then each pair is placed under
+// the f16 exponent and unbiased.
+__device__ __forceinline__ void i8_rows_to_f16_cols_half(const u32x2 (&rows)[8], int w,
+                                                         u32x4 (&out)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            const uint32_t a = rows[2 * i][w] ^ 0x80808080u;       // row 2i: bytes 0-3
-            const uint32_t b = rows[2 * i + 1][w] ^ 0x80808080u;   // row 2i+1: bytes 4-7
-            // [a.b0, b.b0, a.b1, b.b1] and [a.b2, b.b2, a.b3, b.b3]
-            const uint32_t t01 = __builtin_amdgcn_perm(b, a, 0x05010400u);
-            const uint32_t t23 = __builtin_amdgcn_perm(b, a, 0x07030602u);
-            out[4 * w + 0][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t01, kSelLoPair));
-            out[4 * w + 1][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t01, kSelHiPair));
-            out[4 * w + 2][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t23, kSelLoPair));
-            out[4 * w + 3][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t23, kSelHiPair));
-        }
+        const uint32_t a = rows[2 * i][w] ^ 0x80808080u;       // row 2i
+        const uint32_t b = rows[2 * i + 1][w] ^ 0x80808080u;   // row 2i+1
+        // [a.b0, b.b0, a.b1, b.b1] and [a.b2, b.b2, a.b3, b.b3]
+        const uint32_t t01 = __builtin_amdgcn_perm(b, a, 0x05010400u);
+        const uint32_t t23 = __builtin_amdgcn_perm(b, a, 0x07030602u);
+        out[0][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t01, kSelLoPair));
+        out[1][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t01, kSelHiPair));
+        out[2][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t23, kSelLoPair));
+        out[3][i] = f16_unbias(__builtin_amdgcn_perm(kF16Exp, t23, kSelHiPair));
     }
+}
+
 }
 
 // ----------------------------------------------------------------------- MFMA

@@ -162,6 +162,33 @@ def test_prefill_random(case):
     compare(out, lse, ro, rl, rows, inp["query"].dtype, f"prefill case {case}")
 
 
+# ----------------------------------------------------------- unusual qkScale
+
+SCALE_KINDS = {
+    # kind: (dtype, kv_dtype, D, H, Hkv, bs, q_lens, kv_lens)
+    "decode": ("bf16", None, 128, 8, 2, 32, [1, 1], [77, 300]),
+    "decode_i8": ("f16", "i8", 128, 8, 1, 32, [1, 1], [40, 257]),
+    "prefill": ("f16", None, 128, 4, 4, 64, [100, 70], [260, 70]),
+    "prefill_i8": ("bf16", "i8", 64, 2, 1, 32, [90], [150]),
+}
+
+
+@pytest.mark.parametrize("qk_scale", [-0.09, 0.0, 1e-3])
+@pytest.mark.parametrize("mask", [pa.PA_MASK_ALIBI, pa.PA_MASK_CAUSAL])
+@pytest.mark.parametrize("kind", list(SCALE_KINDS))
+def test_unusual_qk_scale(kind, mask, qk_scale):
+    """Negative, zero and tiny qkScale (the softmax then follows the bias / mask alone)."""
+    dt, kvdt, D, H, Hkv, bs, q_lens, kv_lens = SCALE_KINDS[kind]
+    _say(f"[scale] {kind} mask {mask} qk_scale {qk_scale}")
+    inp = wl.make_random_case(200 + len(kind), batch=len(q_lens), head_num=H,
+                              kv_head_num=Hkv, head_size=D, block_size=bs, q_lens=q_lens,
+                              kv_lens=kv_lens, dtype=dt, kv_dtype=kvdt, mask_type=mask,
+                              qk_scale=qk_scale)
+    out, lse = gpu_run(inp)
+    ro, rl, rows = oracle_run(inp)
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"{kind} qk_scale {qk_scale}")
+
+
 # ----------------------------------------------------------- empty tensors
 
 def test_empty_key_value_gives_zero_and_inf():
