@@ -346,8 +346,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
         }
     };
 
-    // Register buffers rotate over the tiles (two for 16-bit K/V, three for int8).  Past
-    // the end of the
+    // Two register buffers alternate between even and odd tiles.  Past the end of the
     // range a buffer loads row 0 of block 0 instead (the same few cache lines for every
     // wave, so L2 hits), so that no load sits behind a branch and each wait leaves the
     // later tiles' loads in flight.
@@ -356,52 +355,22 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     idle.lim[0] = idle.lim[1] = 0;
     idle.kb[0] = idle.kb[1] = kpool;
     idle.vb[0] = idle.vb[1] = vpool;
-    if constexpr (!I8) {
-        if (w0 < w1) {
-            Tile ta, tb;
-            TileBase ca = tile_base(w0);
-            TileBase cb = (w0 + 1 < w1) ? tile_base(w0 + 1) : idle;
-            issue_k(ta, ca);
-            issue_v(ta, ca);
-            issue_k(tb, cb);
-            issue_v(tb, cb);
-            for (int tile = w0; tile < w1; tile += 2) {
-                const TileBase na = (tile + 2 < w1) ? tile_base(tile + 2) : idle;
-                step(ta, ca, na);
-                ca = na;
-                if (tile + 1 >= w1) break;
-                const TileBase nb = (tile + 3 < w1) ? tile_base(tile + 3) : idle;
-                step(tb, cb, nb);
-                cb = nb;
-            }
-        }
-    } else {
-        // int8 tiles carry half the bytes of 16-bit ones: three buffers keep as many
-        // bytes in flight per wave
-        if (w0 < w1) {
-            Tile ta, tb, tc;
-            TileBase ca = tile_base(w0);
-            TileBase cb = (w0 + 1 < w1) ? tile_base(w0 + 1) : idle;
-            TileBase cc = (w0 + 2 < w1) ? tile_base(w0 + 2) : idle;
-            issue_k(ta, ca);
-            issue_v(ta, ca);
-            issue_k(tb, cb);
-            issue_v(tb, cb);
-            issue_k(tc, cc);
-            issue_v(tc, cc);
-            for (int tile = w0; tile < w1; tile += 3) {
-                const TileBase na = (tile + 3 < w1) ? tile_base(tile + 3) : idle;
-                step(ta, ca, na);
-                ca = na;
-                if (tile + 1 >= w1) break;
-                const TileBase nb = (tile + 4 < w1) ? tile_base(tile + 4) : idle;
-                step(tb, cb, nb);
-                cb = nb;
-                if (tile + 2 >= w1) break;
-                const TileBase nc = (tile + 5 < w1) ? tile_base(tile + 5) : idle;
-                step(tc, cc, nc);
-                cc = nc;
-            }
+    if (w0 < w1) {
+        Tile ta, tb;
+        TileBase ca = tile_base(w0);
+        TileBase cb = (w0 + 1 < w1) ? tile_base(w0 + 1) : idle;
+        issue_k(ta, ca);
+        issue_v(ta, ca);
+        issue_k(tb, cb);
+        issue_v(tb, cb);
+        for (int tile = w0; tile < w1; tile += 2) {
+            const TileBase na = (tile + 2 < w1) ? tile_base(tile + 2) : idle;
+            step(ta, ca, na);
+            ca = na;
+            if (tile + 1 >= w1) break;
+            const TileBase nb = (tile + 3 < w1) ? tile_base(tile + 3) : idle;
+            step(tb, cb, nb);
+            cb = nb;
         }
     }
 

@@ -114,8 +114,6 @@ __device__ __forceinline__ void i8_rows_to_f16_cols_half(const u32x2 (&rows)[8],
     }
 }
 
-}
-
 // ----------------------------------------------------------------------- MFMA
 // D(16x16 f32) += A(16x32) * B(32x16); lane l holds A row l%16 / B column l%16 with
 // k = 8*(l/16) .. 8*(l/16)+7, and D column l%16, rows 4*(l/16) .. 4*(l/16)+3.
