@@ -176,11 +176,11 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
  * work lists from its host buffer). */
 void pa_op_destroy(pa_op* op);
 
-/* Instrumentation: start and stop are hipEvent_t handles (or NULL to clear).  While set,
- * each pa_paged_attention on this op records `start` on its stream right before the main
- * kernel (the decode kernel or the prefill kernel) and `stop` right after it, so the
- * caller can time that kernel alone with hipEventElapsedTime.  The events stay owned by
- * the caller.  Host only; returns PA_ERR_NULLPTR if op is NULL. */
+/* Instrumentation: start and stop are hipEvent_t handles (or NULL to clear), created with
+ * timing enabled.  While set, each pa_paged_attention on this op attaches them to the
+ * dispatch of its main kernel (the decode kernel or the prefill kernel), so that
+ * hipEventElapsedTime(start, stop) is that kernel's own duration.  The events stay owned
+ * by the caller.  Host only; returns PA_ERR_NULLPTR if op is NULL. */
 pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop);
 
 /* Write a JSON description of the operator's plan into buf (NUL-terminated, cut at

@@ -173,12 +173,9 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.mask_type = p.mask_type;
         a.scale_is_f32 = p.scale_type == PA_F32;
         a.scale_log2 = scale_log2;
-        if (op->t_start != nullptr && (e = hipEventRecord(op->t_start, s)) != hipSuccess)
-            return hip_fail(e, "hipEventRecord(start)");
-        e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, s);
+        e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, s,
+                              op->t_start, op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-        if (op->t_stop != nullptr && (e = hipEventRecord(op->t_stop, s)) != hipSuccess)
-            return hip_fail(e, "hipEventRecord(stop)");
         if (!p.combine_items.empty()) {
             pa::CombineArgs c{};
             c.items = reinterpret_cast<const pa::CombineItem*>(lists + p.off_combine);
@@ -222,12 +219,9 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.mask_type = p.mask_type;
         a.scale_is_f32 = p.scale_type == PA_F32;
         a.scale_log2 = scale_log2;
-        if (op->t_start != nullptr && (e = hipEventRecord(op->t_start, s)) != hipSuccess)
-            return hip_fail(e, "hipEventRecord(start)");
-        e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, s);
+        e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, s,
+                               op->t_start, op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
-        if (op->t_stop != nullptr && (e = hipEventRecord(op->t_stop, s)) != hipSuccess)
-            return hip_fail(e, "hipEventRecord(stop)");
     }
     // the kernels read the op's work lists from host memory until they finish
     e = hipEventRecord(op->done, s);

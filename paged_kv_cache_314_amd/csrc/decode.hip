@@ -478,11 +478,12 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 }
 
 template <int D, bool BF16, bool I8>
-hipError_t launch_decode_t(const DecodeArgs& a, int n_items, hipStream_t stream) {
+hipError_t launch_decode_t(const DecodeArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
+                           hipEvent_t t1) {
     if (a.mask_type == PA_MASK_ALIBI)
-        hipLaunchKernelGGL((decode_kernel<D, BF16, I8, true>), dim3(n_items), dim3(256), 0, stream, a);
+        launch_256(decode_kernel<D, BF16, I8, true>, n_items, stream, t0, t1, a);
     else
-        hipLaunchKernelGGL((decode_kernel<D, BF16, I8, false>), dim3(n_items), dim3(256), 0, stream, a);
+        launch_256(decode_kernel<D, BF16, I8, false>, n_items, stream, t0, t1, a);
     return hipGetLastError();
 }
 
@@ -495,18 +496,18 @@ hipError_t launch_combine_t(const CombineArgs& a, int n_items, hipStream_t strea
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int n_items, int head_size, bool bf16, bool i8,
-                         hipStream_t stream) {
+                         hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     if (n_items <= 0) return hipSuccess;
     if (head_size == 128) {
-        if (i8) return bf16 ? launch_decode_t<128, true, true>(a, n_items, stream)
-                            : launch_decode_t<128, false, true>(a, n_items, stream);
-        return bf16 ? launch_decode_t<128, true, false>(a, n_items, stream)
-                    : launch_decode_t<128, false, false>(a, n_items, stream);
+        if (i8) return bf16 ? launch_decode_t<128, true, true>(a, n_items, stream, t0, t1)
+                            : launch_decode_t<128, false, true>(a, n_items, stream, t0, t1);
+        return bf16 ? launch_decode_t<128, true, false>(a, n_items, stream, t0, t1)
+                    : launch_decode_t<128, false, false>(a, n_items, stream, t0, t1);
     }
-    if (i8) return bf16 ? launch_decode_t<64, true, true>(a, n_items, stream)
-                        : launch_decode_t<64, false, true>(a, n_items, stream);
-    return bf16 ? launch_decode_t<64, true, false>(a, n_items, stream)
-                : launch_decode_t<64, false, false>(a, n_items, stream);
+    if (i8) return bf16 ? launch_decode_t<64, true, true>(a, n_items, stream, t0, t1)
+                        : launch_decode_t<64, false, true>(a, n_items, stream, t0, t1);
+    return bf16 ? launch_decode_t<64, true, false>(a, n_items, stream, t0, t1)
+                : launch_decode_t<64, false, false>(a, n_items, stream, t0, t1);
 }
 
 hipError_t launch_combine(const CombineArgs& a, int n_items, int head_size, bool bf16,

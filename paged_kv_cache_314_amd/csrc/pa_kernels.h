@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <cstdint>
 
 #include "pa_internal.h"
@@ -69,12 +70,23 @@ struct FillArgs {
     int64_t out_tok_stride, out_head_stride, lse_tok_stride;
 };
 
+// t0 / t1 (optional): events attached to the kernel's own dispatch, so that their
+// timestamps bracket the kernel alone (hipExtLaunchKernelGGL)
 hipError_t launch_decode(const DecodeArgs& a, int n_items, int head_size, bool bf16, bool i8,
-                         hipStream_t stream);
+                         hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, int n_items, int head_size, bool bf16,
                           hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int n_items, int head_size, bool bf16, bool i8,
-                          hipStream_t stream);
+                          hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+
+// 256-thread launch of `kernel` over n workgroups, with timing events if given
+template <typename K, typename A>
+inline void launch_256(K kernel, int n, hipStream_t s, hipEvent_t t0, hipEvent_t t1, const A& a) {
+    if (t0 != nullptr || t1 != nullptr)
+        hipExtLaunchKernelGGL(kernel, dim3(n), dim3(256), 0, s, t0, t1, 0, a);
+    else
+        hipLaunchKernelGGL(kernel, dim3(n), dim3(256), 0, s, a);
+}
 hipError_t launch_fill(const FillArgs& a, hipStream_t stream);
 
 }  // namespace pa

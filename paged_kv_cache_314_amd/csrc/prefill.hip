@@ -570,31 +570,32 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 }
 
 template <int D, bool BF16, bool I8>
-hipError_t launch_prefill_t(const PrefillArgs& a, int n_items, hipStream_t stream) {
+hipError_t launch_prefill_t(const PrefillArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
+                            hipEvent_t t1) {
     if (a.mask_type == PA_MASK_ALIBI)
-        hipLaunchKernelGGL((prefill_kernel<D, BF16, I8, 2>), dim3(n_items), dim3(256), 0, stream, a);
+        launch_256(prefill_kernel<D, BF16, I8, 2>, n_items, stream, t0, t1, a);
     else if (a.mask_type == PA_MASK_CAUSAL)
-        hipLaunchKernelGGL((prefill_kernel<D, BF16, I8, 1>), dim3(n_items), dim3(256), 0, stream, a);
+        launch_256(prefill_kernel<D, BF16, I8, 1>, n_items, stream, t0, t1, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<D, BF16, I8, 0>), dim3(n_items), dim3(256), 0, stream, a);
+        launch_256(prefill_kernel<D, BF16, I8, 0>, n_items, stream, t0, t1, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int n_items, int head_size, bool bf16, bool i8,
-                          hipStream_t stream) {
+                          hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     if (n_items <= 0) return hipSuccess;
     if (head_size == 128) {
-        if (i8) return bf16 ? launch_prefill_t<128, true, true>(a, n_items, stream)
-                            : launch_prefill_t<128, false, true>(a, n_items, stream);
-        return bf16 ? launch_prefill_t<128, true, false>(a, n_items, stream)
-                    : launch_prefill_t<128, false, false>(a, n_items, stream);
+        if (i8) return bf16 ? launch_prefill_t<128, true, true>(a, n_items, stream, t0, t1)
+                            : launch_prefill_t<128, false, true>(a, n_items, stream, t0, t1);
+        return bf16 ? launch_prefill_t<128, true, false>(a, n_items, stream, t0, t1)
+                    : launch_prefill_t<128, false, false>(a, n_items, stream, t0, t1);
     }
-    if (i8) return bf16 ? launch_prefill_t<64, true, true>(a, n_items, stream)
-                        : launch_prefill_t<64, false, true>(a, n_items, stream);
-    return bf16 ? launch_prefill_t<64, true, false>(a, n_items, stream)
-                : launch_prefill_t<64, false, false>(a, n_items, stream);
+    if (i8) return bf16 ? launch_prefill_t<64, true, true>(a, n_items, stream, t0, t1)
+                        : launch_prefill_t<64, false, true>(a, n_items, stream, t0, t1);
+    return bf16 ? launch_prefill_t<64, true, false>(a, n_items, stream, t0, t1)
+                : launch_prefill_t<64, false, false>(a, n_items, stream, t0, t1);
 }
 
 }  // namespace pa
