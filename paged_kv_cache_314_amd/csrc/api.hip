@@ -173,6 +173,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.mask_type = p.mask_type;
         a.scale_is_f32 = p.scale_type == PA_F32;
         a.scale_log2 = scale_log2;
+        a.wave_heads = p.decode_wave_heads;
         e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, s,
                               op->t_start, op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
@@ -254,6 +255,7 @@ uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
     s += modes[static_cast<int>(p.mode)];
     s += "\", \"workspace_bytes\": " + std::to_string(p.workspace_bytes);
     s += ", \"chunk_tiles\": " + std::to_string(p.decode_chunk_tiles);
+    s += ", \"decode_wave_heads\": " + std::to_string(p.decode_wave_heads);
     s += ", \"partial_slots\": " + std::to_string(p.partial_slots);
     s += ", \"decode_items\": [";
     for (size_t i = 0; i < p.decode_items.size(); ++i) {
@@ -262,7 +264,8 @@ uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
         s += "[" + std::to_string(d.b) + ", " + std::to_string(d.kvh) + ", " + std::to_string(d.hg) +
              ", " + std::to_string(d.t0) + ", " + std::to_string(d.t1) + ", " +
              std::to_string(d.slot) + ", " + std::to_string(d.qrow) + ", " +
-             std::to_string(d.kvlen) + "]";
+             std::to_string(d.kvlen) + ", " + std::to_string(d.heads) + ", " +
+             std::to_string(d.slot_stride) + "]";
     }
     s += "], \"combine_items\": [";
     for (size_t i = 0; i < p.combine_items.size(); ++i) {

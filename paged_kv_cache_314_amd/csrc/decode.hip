@@ -56,7 +56,9 @@ struct DecodeTileRegs {
     std::conditional_t<I8, u32x2, u32x4> v[8];
 };
 
-template <int D, bool BF16, bool I8, bool ALIBI>
+// WPH: the item holds 4 kv heads and wave w streams kv head kvh + w over the whole
+// tile range (else the 4 waves split the range of one kv head and merge in LDS)
+template <int D, bool BF16, bool I8, bool ALIBI, bool WPH>
 __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     constexpr int KK = D / 32;                 // QK k-steps
     constexpr int KP = D / 64;                 // int8 16-byte loads per K row
@@ -73,11 +75,12 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     const DecodeItem it = a.items[blockIdx.x];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kvh = it.kvh + (WPH ? wave : 0);  // this wave's kv head
     const int col = lane & 15;                 // packed head (QK/PV column)
     const int qg = lane >> 4;                  // lane group: k-slots 8*qg .. 8*qg+7
     const int hl = it.hg * kHeadPack + col;    // head index within the kv group
     const bool hvalid = hl < a.group;
-    const int head = it.kvh * a.group + (hvalid ? hl : 0);
+    const int head = kvh * a.group + (hvalid ? hl : 0);
     const int kvlen = it.kvlen;
 
     // ------------------------------------------------------------ Q operand
@@ -119,9 +122,9 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
                     const int d = d0 + 8 * h8 + e;
                     float sk;
                     if (a.scale_is_f32) {
-                        sk = static_cast<const float*>(a.kscale)[it.kvh * D + d];
+                        sk = static_cast<const float*>(a.kscale)[kvh * D + d];
                     } else {
-                        sk = half_to_f32<BF16>(static_cast<const uint16_t*>(a.kscale)[it.kvh * D + d]);
+                        sk = half_to_f32<BF16>(static_cast<const uint16_t*>(a.kscale)[kvh * D + d]);
                     }
                     qf[kp][8 * h8 + e] = qv * sk * a.scale_log2;
                     amax = fmaxf(amax, fabsf(qf[kp][8 * h8 + e]));
@@ -163,14 +166,14 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int ntiles = it.t1 - it.t0;
-    const int w0 = it.t0 + (ntiles * wave) / kDecodeWaves;
-    const int w1 = it.t0 + (ntiles * (wave + 1)) / kDecodeWaves;
+    const int w0 = WPH ? it.t0 : it.t0 + (ntiles * wave) / kDecodeWaves;
+    const int w1 = WPH ? it.t1 : it.t0 + (ntiles * (wave + 1)) / kDecodeWaves;
     const int32_t* trow = a.table + static_cast<int64_t>(it.b) * a.table_stride;
     const int bs = a.block_size;
     const char* kpool = static_cast<const char*>(a.k) +
-                        static_cast<int64_t>(it.kvh) * a.k_head_stride * ESZ;
+                        static_cast<int64_t>(kvh) * a.k_head_stride * ESZ;
     const char* vpool = static_cast<const char*>(a.v) +
-                        static_cast<int64_t>(it.kvh) * a.v_head_stride * ESZ;
+                        static_cast<int64_t>(kvh) * a.v_head_stride * ESZ;
     const int64_t kblk_bytes = a.k_blk_stride * ESZ, vblk_bytes = a.v_blk_stride * ESZ;
     const uint32_t kslot_bytes = static_cast<uint32_t>(a.k_slot_stride * ESZ);
     const uint32_t vslot_bytes = static_cast<uint32_t>(a.v_slot_stride * ESZ);
@@ -374,6 +377,61 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
         }
     }
 
+    if constexpr (WPH) {
+        // ---------------------------------------- each wave owns its kv head's result
+        float L = l_run;
+        L += shfl_xor_f(L, 16);
+        L += shfl_xor_f(L, 32);
+        const float M = m_run;
+        const int slot = it.slot < 0 ? -1 : it.slot + wave * it.slot_stride;
+        const int geff = a.group;                  // <= 16 in this mode
+        if (!hvalid) return;
+        const int out_head = kvh * a.group + hl;
+        // acc[n][r] = O[head col][d = 32*qg + 8*r + n]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d0 = 32 * qg + 8 * r;
+            if (d0 >= D) continue;
+            float o[8];
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                o[n] = acc[n][r];
+                if constexpr (I8) {
+                    float sv;
+                    if (a.scale_is_f32) sv = static_cast<const float*>(a.vscale)[kvh * D + d0 + n];
+                    else sv = half_to_f32<BF16>(static_cast<const uint16_t*>(a.vscale)[kvh * D + d0 + n]);
+                    o[n] *= sv;
+                }
+            }
+            if (slot < 0) {
+                const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+                u32x4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = pack2<BF16>(o[2 * i] * inv, o[2 * i + 1] * inv);
+                uint16_t* orow = static_cast<uint16_t*>(a.out) +
+                                 static_cast<int64_t>(it.qrow) * a.out_tok_stride +
+                                 static_cast<int64_t>(out_head) * a.out_head_stride;
+                *reinterpret_cast<u32x4*>(orow + d0) = w;
+            } else {
+                float* po = a.part_o + (static_cast<int64_t>(slot) * geff + hl) * D + d0;
+                *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
+            }
+        }
+        if (qg == 0) {
+            if (slot < 0) {
+                if (a.lse != nullptr)
+                    a.lse[static_cast<int64_t>(it.qrow) * a.lse_tok_stride + out_head] =
+                        (L > 0.0f) ? (M + fast_log2(L)) * kLn2 : INFINITY;
+            } else {
+                const int64_t sl = static_cast<int64_t>(slot) * geff + hl;
+                a.part_ml[2 * sl] = M;
+                a.part_ml[2 * sl + 1] = L;
+            }
+        }
+        return;
+    }
+
     // ------------------------------------------------ merge the 4 wave states
     float l_tot = l_run;
     l_tot += shfl_xor_f(l_tot, 16);
@@ -480,10 +538,14 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
 template <int D, bool BF16, bool I8>
 hipError_t launch_decode_t(const DecodeArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
                            hipEvent_t t1) {
-    if (a.mask_type == PA_MASK_ALIBI)
-        launch_256(decode_kernel<D, BF16, I8, true>, n_items, stream, t0, t1, a);
-    else
-        launch_256(decode_kernel<D, BF16, I8, false>, n_items, stream, t0, t1, a);
+    const bool alibi = a.mask_type == PA_MASK_ALIBI;
+    if (a.wave_heads) {
+        if (alibi) launch_256(decode_kernel<D, BF16, I8, true, true>, n_items, stream, t0, t1, a);
+        else launch_256(decode_kernel<D, BF16, I8, false, true>, n_items, stream, t0, t1, a);
+    } else {
+        if (alibi) launch_256(decode_kernel<D, BF16, I8, true, false>, n_items, stream, t0, t1, a);
+        else launch_256(decode_kernel<D, BF16, I8, false, false>, n_items, stream, t0, t1, a);
+    }
     return hipGetLastError();
 }
 

@@ -16,23 +16,32 @@ constexpr int kDecodeTile = 32;
 constexpr int kHeadPack = 16;
 // Waves per decode workgroup.
 constexpr int kDecodeWaves = 4;
+// Compute units of the target GPU (MI355X), for sizing work lists.
+constexpr int kComputeUnits = 256;
 // Prefill: query rows per workgroup and keys per step.
 constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
 
 enum class Mode : int32_t { kNoop = 0, kFill = 1, kDecode = 2, kPrefill = 3 };
 
-// One decode workgroup: a range of 32-token tiles of one (sequence, kv head, head group).
+// One decode workgroup: a range of 32-token tiles of one sequence and
+//   heads == 1: one (kv head, head group), the four waves splitting the tile range, or
+//   heads == 4: kv heads kvh .. kvh+3 (one head group each), wave w streaming the whole
+//               range of kv head kvh + w, so that the four waves read 4 neighbouring
+//               head slices of every token row together.
 struct DecodeItem {
     int32_t b;        // sequence
-    int32_t kvh;      // kv head
-    int32_t hg;       // group of up to 16 query heads sharing kvh
+    int32_t kvh;      // (first) kv head
+    int32_t hg;       // group of up to 16 query heads sharing kvh (0 when heads == 4)
     int32_t t0, t1;   // tile range [t0, t1)
-    int32_t slot;     // -1: write out/lse directly; >= 0: partial slot in the workspace
+    int32_t slot;     // -1: write out/lse directly; >= 0: partial slot (of kv head kvh)
     int32_t qrow;     // query/out row of this sequence's decode token
     int32_t kvlen;    // kvSeqLen[b]
+    int32_t heads;    // 1 or 4 (see above)
+    int32_t slot_stride;  // heads == 4: slot of kv head kvh + w is slot + w * slot_stride
+    int32_t pad[2];
 };
-static_assert(sizeof(DecodeItem) == 32, "DecodeItem layout");
+static_assert(sizeof(DecodeItem) == 48, "DecodeItem layout");
 
 // One combine workgroup: merge nsplit consecutive partial slots into out/lse.
 struct CombineItem {
@@ -92,6 +101,7 @@ struct Plan {
     std::vector<CombineItem> combine_items;
     std::vector<PrefillItem> prefill_items;
     int32_t decode_chunk_tiles = 0;
+    int32_t decode_wave_heads = 0;   // 1: items of 4 kv heads, one per wave
     int32_t partial_slots = 0;
 
     // work lists live in pinned host memory owned by the op (offsets into it); the

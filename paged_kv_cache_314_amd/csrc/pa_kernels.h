@@ -30,6 +30,7 @@ struct DecodeArgs {
     int32_t mask_type;
     int32_t scale_is_f32;   // antiquant scales are f32 (else the query dtype)
     float scale_log2;       // qkScale * log2(e)
+    int32_t wave_heads;     // items of 4 kv heads, one per wave (DecodeItem.heads == 4)
 };
 
 struct CombineArgs {

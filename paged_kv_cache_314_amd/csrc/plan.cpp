@@ -162,6 +162,15 @@ int env_int(const char* name, int fallback) {
     return static_cast<int>(v);
 }
 
+// 0 / 1 switch from the environment (unset or unparsable: fallback)
+bool env_flag(const char* name, bool fallback) {
+    const char* s = std::getenv(name);
+    if (s == nullptr || *s == 0) return fallback;
+    if (s[0] == '0' && s[1] == 0) return false;
+    if (s[0] == '1' && s[1] == 0) return true;
+    return fallback;
+}
+
 uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 
 // Workgroups are handed to the 8 XCDs of the chip round-robin by index (workgroup i runs
@@ -461,10 +470,33 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         for (int64_t b = 0; b < B; ++b)
             if (ql[b * qls] == 1) total_tiles += (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
         total_tiles *= static_cast<int64_t>(kvh_num) * p.head_groups;
-        const int target = env_int("PA_DECODE_TARGET_ITEMS", 2048);
-        int chunk = static_cast<int>(std::min<int64_t>((total_tiles + target - 1) / target, 1 << 20));
-        chunk = std::max(chunk, 8);
-        chunk = (chunk + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
+        // wave-per-kv-head items when kv heads come in fours and a kv group fits one
+        // MFMA column block: the four waves of a workgroup read neighbouring head slices
+        // of the same token rows.  Only with enough work to fill the GPU: on short
+        // batches splitting one kv head's range over four waves gives the shorter
+        // critical path.  PA_DECODE_WAVE_HEADS=0 / 1 turns it off / on regardless.
+        const bool wph_ok = kvh_num % 4 == 0 && p.head_groups == 1;
+        const bool wph_auto = total_tiles >= 64 * int64_t(kComputeUnits);
+        const bool wph = wph_ok && env_flag("PA_DECODE_WAVE_HEADS", wph_auto);
+        p.decode_wave_heads = wph ? 1 : 0;
+        // chunk = tiles one item gives each wave's share of work: about `target`
+        // workgroups in all, and a multiple of 4 tiles.  Wave-per-head items are 4x
+        // larger; with nearly equal sequence lengths one full round of resident
+        // workgroups (2 per CU) is best, uneven lengths need two rounds for balance.
+        int64_t max_tiles = 0, n_dec = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            if (ql[b * qls] != 1) continue;
+            max_tiles = std::max<int64_t>(max_tiles, (kl[b * kls] + kDecodeTile - 1) / kDecodeTile);
+            ++n_dec;
+        }
+        const bool even = n_dec > 0 &&
+                          4 * max_tiles * n_dec * kvh_num * p.head_groups <= 5 * total_tiles;
+        const int target = env_int("PA_DECODE_TARGET_ITEMS",
+                                   wph ? (even ? 2 : 4) * kComputeUnits : 2048);
+        const int64_t per_item = (total_tiles + target - 1) / target;      // kv-head tiles
+        int chunk = static_cast<int>(std::min<int64_t>(wph ? (per_item + 3) / 4 : per_item, 1 << 20));
+        chunk = std::max(chunk, 8);          // short sequences: no split, no combine
+        chunk = (chunk + 3) / 4 * 4;
         chunk = env_int("PA_DECODE_CHUNK_TILES", chunk);
         p.decode_chunk_tiles = chunk;
         int32_t slots = 0;
@@ -475,10 +507,9 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
             const int32_t nsplit = std::max<int32_t>(1, (tiles + chunk - 1) / chunk);
             const int32_t groups = kvh_num * p.head_groups;
             // (kv head, head group) g owns partial slots slots + g*nsplit + s.  Items are
-            // emitted head-major: the splits of one kv head launch together.  (Launching
-            // the kv heads of one token range together measured slower in the
-            // (block, slot, kv head, d) layout.)
-            for (int32_t g = 0; g < groups; ++g) {
+            // emitted head-major: the splits of one kv head (or head quad) launch together.
+            const int32_t gstep = wph ? 4 : 1;
+            for (int32_t g = 0; g < groups; g += gstep) {
                 for (int32_t s = 0; s < nsplit; ++s) {
                     DecodeItem it{};
                     it.b = static_cast<int32_t>(b);
@@ -489,6 +520,8 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                     it.slot = nsplit > 1 ? slots + g * nsplit + s : -1;
                     it.qrow = q0[b];
                     it.kvlen = klen;
+                    it.heads = gstep;
+                    it.slot_stride = nsplit;
                     p.decode_items.push_back(it);
                 }
             }

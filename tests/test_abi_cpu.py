@@ -108,8 +108,8 @@ def test_library_exports_every_header_symbol():
 
 # ---------------------------------------------------------------- planning
 
-@pytest.mark.parametrize("name", list(wl.WORKLOADS))
-def test_plan_for_named_workloads(name):
+def _named_case(name):
+    """A Case with a named workload's shape and its seeded kv lengths."""
     w = wl.WORKLOADS[name]
     rng = np.random.default_rng([314, w.index, 1])
     if isinstance(w.kv_seq_len, tuple):
@@ -123,6 +123,16 @@ def test_plan_for_named_workloads(name):
     c = Case(q_lens=ql, kv_lens=kv, H=w.head_num, Hkv=w.kv_head_num, D=w.head_size,
              bs=w.block_size, dtype=dt[w.dtype], kv_dtype=dt[w.kv_dtype], mask=w.mask_type,
              width=w.table_width)
+    return w, c, ql, kv
+
+
+def _plan_named(name):
+    return _named_case(name)[1].plan()
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_plan_for_named_workloads(name):
+    w, c, ql, kv = _named_case(name)
     info = c.plan()
     assert info["mode"] == ("decode" if w.seq_len == "decode" else "prefill")
     if info["mode"] == "decode":
@@ -137,9 +147,17 @@ def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
     combine item; single-split items write directly (slot -1)."""
     n_hg = -(-group // 16)
     items = info["decode_items"]
+    wph = info["decode_wave_heads"] == 1
+    assert not wph or (Hkv % 4 == 0 and group <= 16)
     by_key = {}
-    for b, kvh, hg, t0, t1, slot, qrow, kvlen in items:
-        by_key.setdefault((b, kvh, hg), []).append((t0, t1, slot, qrow, kvlen))
+    for b, kvh, hg, t0, t1, slot, qrow, kvlen, heads, stride in items:
+        # an item of 4 kv heads stands for one range of each of kvh .. kvh+3
+        assert heads == (4 if wph else 1)
+        if heads == 4:
+            assert kvh % 4 == 0 and hg == 0
+        for w in range(heads):
+            s = -1 if slot < 0 else slot + w * stride
+            by_key.setdefault((b, kvh + w, hg), []).append((t0, t1, s, qrow, kvlen))
     q0 = np.concatenate([[0], np.cumsum(q_lens)])
     combines = {(c[0], c[1], c[4]): c for c in info["combine_items"]}
     slots_seen = set()
@@ -305,12 +323,30 @@ def test_head_checks():
     _expect(c, pa.PA_ERR_UNSUPPORTED, "headSize")
 
 
+def test_decode_wave_per_head_switch(monkeypatch):
+    """Items of four kv heads only where kvHeadNum % 4 == 0 and a group has <= 16 heads;
+    on by default for large batches, forced on / off by PA_DECODE_WAVE_HEADS."""
+    for env, H, Hkv, want in (("1", 16, 4, 1), ("0", 16, 4, 0), ("1", 12, 3, 0),
+                              ("1", 68, 4, 0)):
+        monkeypatch.setenv("PA_DECODE_WAVE_HEADS", env)
+        c = base(H=H, Hkv=Hkv)
+        info = c.plan()
+        assert info["decode_wave_heads"] == want, (env, H, Hkv)
+        _check_decode_plan(info, [1, 1], [100, 37], Hkv, H // Hkv)
+    monkeypatch.delenv("PA_DECODE_WAVE_HEADS")
+    info = _plan_named("decode_int8_long")
+    assert info["decode_wave_heads"] == 1
+    info = _plan_named("decode_f16_small")
+    assert info["decode_wave_heads"] == 0
+
+
 def test_kv_head_num_zero_means_head_num():
     c = base(H=4, Hkv=4)
     c.Hkv = 0
     info = c.plan()
     assert info["mode"] == "decode"
-    assert {it[1] for it in info["decode_items"]} == {0, 1, 2, 3}
+    # every kv head 0..3 is covered (by 4-head items or one item per head)
+    assert {it[1] + w for it in info["decode_items"] for w in range(it[8])} == {0, 1, 2, 3}
 
 
 def test_mask_checks():

@@ -126,6 +126,34 @@ def test_decode_forced_splits(chunk, monkeypatch):
     compare(out, lse, ro, rl, rows, inp["query"].dtype, f"split chunk {chunk}")
 
 
+WAVE_HEAD_CASES = [
+    # (dtype, kv_dtype, D, H, Hkv, bs, kv_lens, mask, chunk)
+    ("bf16", None, 128, 16, 4, 32, [1, 33, 700, 4097], pa.PA_MASK_NONE, None),
+    ("f16", None, 64, 8, 8, 16, [0, 95, 96, 300], pa.PA_MASK_ALIBI, "8"),
+    ("bf16", "i8", 128, 32, 8, 64, [63, 2000, 129], pa.PA_MASK_NONE, "12"),
+    ("f16", "i8", 64, 16, 4, 32, [500, 31], pa.PA_MASK_ALIBI, None),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WAVE_HEAD_CASES)))
+def test_decode_wave_per_head(case, monkeypatch):
+    """Items of four kv heads, one per wave (forced on for small shapes)."""
+    dt, kvdt, D, H, Hkv, bs, kv_lens, mask, chunk = WAVE_HEAD_CASES[case]
+    _say(f"[decode wave-per-head] case {case}: {WAVE_HEAD_CASES[case]}")
+    monkeypatch.setenv("PA_DECODE_WAVE_HEADS", "1")
+    if chunk is not None:
+        monkeypatch.setenv("PA_DECODE_CHUNK_TILES", chunk)
+    inp = wl.make_random_case(300 + case, batch=len(kv_lens), head_num=H, kv_head_num=Hkv,
+                              head_size=D, block_size=bs, q_lens=[1] * len(kv_lens),
+                              kv_lens=kv_lens, dtype=dt, kv_dtype=kvdt, mask_type=mask)
+    out, lse, op, ws = gpu_run(inp, keep_op=True)
+    info = pa.pa_op_describe(op)
+    op.destroy()
+    assert info["decode_wave_heads"] == 1
+    ro, rl, rows = oracle_run(inp)
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"wave-per-head case {case}")
+
+
 def test_decode_skips_sequences_without_query():
     inp = wl.make_random_case(51, batch=4, head_num=4, kv_head_num=2, head_size=128,
                               block_size=16, q_lens=[1, 0, 1, 0], kv_lens=[100, 50, 0, 7],
