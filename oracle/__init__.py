@@ -14,7 +14,8 @@ Sources (the pages this follows):
   * aclnnFusedInferAttentionScoreV4 / V3, "Function" (formula
     Softmax(QK^T/sqrt(d) + mask) V), "Constraints" (empty-tensor rules,
     deterministic computation, paged-attention layout, GQA divisibility,
-    per-channel KV antiquant, and the softmax-LSE decomposition used by
+    per-channel and per-token KV antiquant with optional offsets, and the
+    softmax-LSE decomposition used by
     ring attention).
   * PrefixEncoder (Ascend Transformer Boost SelfAttention, calcType
     PREFIX_ENCODER), "Definition" and "Members" table (argument list,
@@ -30,8 +31,11 @@ from .attention import (
     MASK_NONE,
     MASK_ALIBI,
     MASK_CAUSAL,
+    ANTIQUANT_PER_CHANNEL,
+    ANTIQUANT_PER_TOKEN,
     gather_sequence,
     dequantize_per_channel,
+    dequantize_per_token,
     query_positions,
     attention_contiguous,
     paged_attention,

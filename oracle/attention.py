@@ -21,7 +21,14 @@ Readings where the pages are silent (each is listed in the design doc):
   * the ALiBi bias of maskType 3 is slope_h * (j - p_i), added after the
     qkScale multiplication, and keys j > p_i are masked (causal);
   * a row that sees no key gives out = 0 and lse = +inf;
-  * symmetric per-channel antiquant: K_hat[t, kvh, d] = scale[kvh, d] * K[t, kvh, d].
+  * antiquant K_hat = scale * (K + offset): the pages name a scale and an
+    optional offset (absent = symmetric) but print no formula; the offset is
+    taken as added to the stored integer before scaling (a zero point z is
+    passed as offset = -z);
+  * antiquant modes 0 = per-channel (scale[kvh, d]) and 1 = per-token
+    (scale[b, t], t the token's position in its sequence, shared by every kv
+    head and channel): the pages allow key mode 0 with value mode 1 as the one
+    pair of different modes, which fixes 0 as per-channel and 1 as per-token.
 """
 
 import numpy as np
@@ -29,6 +36,9 @@ import numpy as np
 MASK_NONE = 0     # no mask: every key 0 <= j < kvSeqLen is visible
 MASK_ALIBI = 3    # PrefixEncoder maskType 3, MASK_TYPE_ALIBI_COMPRESS
 MASK_CAUSAL = 9   # PrefixEncoder maskType 9, MASK_TYPE_CAUSAL_MASK
+
+ANTIQUANT_PER_CHANNEL = 0
+ANTIQUANT_PER_TOKEN = 1
 
 
 def gather_sequence(pool, table_row, kv_len, block_size):
@@ -49,16 +59,35 @@ def gather_sequence(pool, table_row, kv_len, block_size):
     return rows[:kv_len].astype(np.float64)
 
 
-def dequantize_per_channel(x, scale):
-    """Symmetric per-channel antiquant of int8 K or V rows.
+def dequantize_per_channel(x, scale, offset=None):
+    """Per-channel antiquant of int8 K or V rows.
 
     aclnnFusedInferAttentionScoreV3, Constraints on antiquantScale /
-    antiquantOffset (per-channel mode; symmetric when the offset is null):
-    the real value is the stored integer times the scale of its
-    (kv head, channel).  x: [..., kvHeadNum, headSize] integers;
-    scale: [kvHeadNum, headSize].
+    antiquantOffset (per-channel mode; symmetric when the offset is null,
+    asymmetric otherwise): the real value is (stored integer + offset) times
+    the scale of its (kv head, channel).  x: [..., kvHeadNum, headSize]
+    integers; scale, offset: [kvHeadNum, headSize].
     """
-    return np.asarray(x, dtype=np.float64) * np.asarray(scale, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    if offset is not None:
+        x = x + np.asarray(offset, dtype=np.float64)
+    return x * np.asarray(scale, dtype=np.float64)
+
+
+def dequantize_per_token(x, scale_row, offset_row=None):
+    """Per-token antiquant of one sequence's int8 K or V rows.
+
+    aclnnFusedInferAttentionScoreV3, Constraints on the KV antiquant
+    parameters, per-token mode (scale shape (B, S), float32): token t of the
+    sequence has one scale (and offset) for all its kv heads and channels.
+    x: [kv_len, kvHeadNum, headSize] integers; scale_row, offset_row: the
+    sequence's row of the (B, S) tensors, S >= kv_len.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    if offset_row is not None:
+        x = x + np.asarray(offset_row, dtype=np.float64)[:n, None, None]
+    return x * np.asarray(scale_row, dtype=np.float64)[:n, None, None]
 
 
 def query_positions(q_len, kv_len):
@@ -119,7 +148,10 @@ def attention_contiguous(q, k, v, positions, mask_type, qk_scale,
 
 def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len,
                     mask_type, head_num, kv_head_num, qk_scale, slopes=None,
-                    key_antiquant_scale=None, value_antiquant_scale=None):
+                    key_antiquant_scale=None, value_antiquant_scale=None,
+                    key_antiquant_offset=None, value_antiquant_offset=None,
+                    key_antiquant_mode=ANTIQUANT_PER_CHANNEL,
+                    value_antiquant_mode=ANTIQUANT_PER_CHANNEL):
     """Reference result of the paged fused-attention call.
 
     PrefixEncoder, Definition and Members: query [nTokens, headNum, headSize]
@@ -132,8 +164,9 @@ def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len,
     processing when the input parameter is empty): an empty query/out returns
     empty tensors; an empty key/value returns out all 0 and lse all inf.
 
-    int8 key/value are dequantised per channel with key_antiquant_scale /
-    value_antiquant_scale [kvHeadNum, headSize] before anything else.
+    int8 key/value are dequantised before anything else: per channel
+    (mode 0) with scales / offsets [kvHeadNum, headSize], or per token
+    (mode 1) with scales / offsets [batch, S] (a leading 1 is dropped).
     Returns out [nTokens, headNum, headSize] and lse [nTokens, headNum].
     """
     if kv_head_num == 0:
@@ -155,10 +188,10 @@ def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len,
         ql, kl = int(seq_len[b]), int(kv_seq_len[b])
         k_b = gather_sequence(key, block_tables[b], kl, block_size)
         v_b = gather_sequence(value, block_tables[b], kl, block_size)
-        if key_antiquant_scale is not None:
-            k_b = dequantize_per_channel(k_b, key_antiquant_scale)
-        if value_antiquant_scale is not None:
-            v_b = dequantize_per_channel(v_b, value_antiquant_scale)
+        k_b = _dequantize(k_b, b, key_antiquant_scale, key_antiquant_offset,
+                          key_antiquant_mode)
+        v_b = _dequantize(v_b, b, value_antiquant_scale, value_antiquant_offset,
+                          value_antiquant_mode)
         o_b, l_b = attention_contiguous(
             query[q0:q0 + ql], k_b, v_b, query_positions(ql, kl), mask_type,
             qk_scale, head_num, kv_head_num, slopes)
@@ -166,6 +199,21 @@ def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len,
         lse[q0:q0 + ql] = l_b
         q0 += ql
     return out, lse
+
+
+def _dequantize(x_b, b, scale, offset, mode):
+    """Antiquant of sequence b's gathered rows in the given mode (no-op without a scale)."""
+    if scale is None:
+        return x_b
+    if mode == ANTIQUANT_PER_CHANNEL:
+        return dequantize_per_channel(x_b, scale, offset)
+    scale = np.asarray(scale, dtype=np.float64)
+    scale = scale.reshape(scale.shape[-2:])
+    off_row = None
+    if offset is not None:
+        offset = np.asarray(offset, dtype=np.float64)
+        off_row = offset.reshape(offset.shape[-2:])[b]
+    return dequantize_per_token(x_b, scale[b], off_row)
 
 
 def merge_partials(outs, lses):

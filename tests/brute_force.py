@@ -12,10 +12,24 @@ aclnnFusedInferAttentionScoreV3, Constraints: softmaxLse.
 import math
 
 
+def _deq(x, b, j, c, d, scale, offset, per_token):
+    """One antiquantised element: (x + offset) * scale, the scale / offset picked by
+    (kv head, channel) in per-channel mode or by (sequence, token) in per-token mode."""
+    if scale is None:
+        return x
+    if per_token:
+        o = offset[b][j] if offset is not None else 0.0
+        return (x + o) * scale[b][j]
+    o = offset[c][d] if offset is not None else 0.0
+    return (x + o) * scale[c][d]
+
+
 def brute_attention(query, key, value, tables, seq_len, kv_seq_len, mask_type,
                     head_num, kv_head_num, qk_scale, slopes=None,
-                    key_scale=None, value_scale=None):
-    """query [T][H][D], key/value [NB][bs][Hkv][D] as nested lists."""
+                    key_scale=None, value_scale=None, key_offset=None, value_offset=None,
+                    key_per_token=False, value_per_token=False):
+    """query [T][H][D], key/value [NB][bs][Hkv][D] as nested lists; per-channel scales /
+    offsets [Hkv][D], per-token ones [B][S]."""
     n_tokens = len(query)
     D = len(query[0][0]) if n_tokens else 0
     bs = len(key[0]) if len(key) else 1
@@ -36,7 +50,7 @@ def brute_attention(query, key, value, tables, seq_len, kv_seq_len, mask_type,
                     krow = key[blk][j % bs][c]
                     terms = []
                     for d in range(D):
-                        kd = krow[d] * (key_scale[c][d] if key_scale else 1.0)
+                        kd = _deq(krow[d], b, j, c, d, key_scale, key_offset, key_per_token)
                         terms.append(query[row][h][d] * kd)
                     s = qk_scale * math.fsum(terms)
                     if mask_type == 3:
@@ -51,8 +65,8 @@ def brute_attention(query, key, value, tables, seq_len, kv_seq_len, mask_type,
                     acc = []
                     for j, w in weights:
                         blk = tables[b][j // bs]
-                        vd = value[blk][j % bs][c][d]
-                        vd *= value_scale[c][d] if value_scale else 1.0
+                        vd = _deq(value[blk][j % bs][c][d], b, j, c, d, value_scale,
+                                  value_offset, value_per_token)
                         acc.append(w * vd)
                     out[row][h][d] = math.fsum(acc) / total
                 lse[row][h] = m + math.log(total)

@@ -381,6 +381,121 @@ def test_int8_equals_float_on_dequantised_pool():
                                   [[[-3.0, -4.0, -4.0], [0.0, 16.0, 64.0]]])
 
 
+def _antiquant_case(rng, *, kmode, vmode, offsets, B=2, H=4, Hkv=2, D=5, bs=4, max_kv=11):
+    """A random int8 case with scales (and offsets) in the given modes: per-channel
+    [Hkv, D] or per-token [B, S] with S = max kv + 3 (entries past kv never used)."""
+    c = _random_case(rng, B=B, H=H, Hkv=Hkv, D=D, bs=bs, mask=MASK_NONE, int8=True,
+                     max_kv=max_kv)
+    S = max(c["kv_lens"]) + 3
+
+    def draw(mode, lo, hi):
+        return rng.uniform(lo, hi, size=(Hkv, D) if mode == 0 else (B, S))
+    c["ks"], c["vs"] = draw(kmode, 0.005, 0.02), draw(vmode, 0.005, 0.02)
+    c["ko"] = draw(kmode, -20.0, 20.0) if offsets else None
+    c["vo"] = draw(vmode, -20.0, 20.0) if offsets else None
+    c["kmode"], c["vmode"] = kmode, vmode
+    return c
+
+
+def _oracle_aq(c, mask_type, H, Hkv, scale):
+    return oracle.paged_attention(
+        c["q"], c["k"], c["v"], c["table"], c["q_lens"], c["kv_lens"], mask_type, H, Hkv,
+        scale, slopes=c["slopes"], key_antiquant_scale=c["ks"], value_antiquant_scale=c["vs"],
+        key_antiquant_offset=c["ko"], value_antiquant_offset=c["vo"],
+        key_antiquant_mode=c["kmode"], value_antiquant_mode=c["vmode"])
+
+
+@pytest.mark.parametrize("seed", range(9))
+def test_brute_force_agrees_antiquant_modes(seed):
+    """Per-channel / per-token scales with and without offsets, against the scalar twin."""
+    rng = np.random.default_rng([314, 91, seed])
+    kmode, vmode = [(0, 0), (1, 1), (0, 1)][seed % 3]
+    mask = [MASK_NONE, MASK_CAUSAL, MASK_ALIBI][(seed // 3) % 3]
+    c = _antiquant_case(rng, kmode=kmode, vmode=vmode, offsets=seed % 2 == 0)
+    out, lse = _oracle_aq(c, mask, 4, 2, 0.4)
+    lst = lambda x: None if x is None else x.tolist()
+    bo, bl = brute_attention(
+        c["q"].tolist(), c["k"].tolist(), c["v"].tolist(), c["table"].tolist(),
+        c["q_lens"], c["kv_lens"], mask, 4, 2, 0.4, slopes=c["slopes"].tolist(),
+        key_scale=lst(c["ks"]), value_scale=lst(c["vs"]), key_offset=lst(c["ko"]),
+        value_offset=lst(c["vo"]), key_per_token=kmode == 1, value_per_token=vmode == 1)
+    _same(out, np.array(bo).reshape(out.shape))
+    _same(lse, np.array(bl).reshape(lse.shape))
+
+
+def test_per_channel_key_offset_moves_lse_only():
+    """A per-channel key offset o adds qkScale * sum_d q_d s_d o_d to every score of a row:
+    out is unchanged and lse moves by that constant (which fixes where the offset
+    enters: inside the scale, added to the integer)."""
+    rng = np.random.default_rng([314, 92])
+    c = _antiquant_case(rng, kmode=0, vmode=0, offsets=True, max_kv=9)
+    c0 = dict(c, ko=None, vo=c["vo"])
+    a = _oracle_aq(c, MASK_CAUSAL, 4, 2, 0.7)
+    b = _oracle_aq(c0, MASK_CAUSAL, 4, 2, 0.7)
+    _same(a[0], b[0], 1e-10)
+    shift = 0.7 * np.einsum("thd,hd->th", c["q"], np.repeat(c["ks"] * c["ko"], 2, axis=0))
+    fin = np.isfinite(b[1])
+    assert np.max(np.abs(a[1][fin] - (b[1][fin] + shift[fin]))) < 1e-10
+    assert np.array_equal(np.isfinite(a[1]), fin)
+
+
+def test_per_token_value_offset_closed_form():
+    """Zero int8 values and zero queries: every visible key has weight 1/n, so each
+    output element is the mean of s_t * o_t over the visible tokens t and lse = ln n."""
+    rng = np.random.default_rng([314, 93])
+    c = _antiquant_case(rng, kmode=1, vmode=1, offsets=True, max_kv=10)
+    c["q"][:] = 0.0
+    c["v"][:] = 0.0
+    out, lse = _oracle_aq(c, MASK_CAUSAL, 4, 2, 0.5)
+    row = 0
+    for b, (ql, kl) in enumerate(zip(c["q_lens"], c["kv_lens"])):
+        for i in range(ql):
+            n = kl - ql + i + 1
+            if n <= 0:
+                assert np.all(out[row] == 0) and np.all(lse[row] == np.inf)
+            else:
+                want = float(np.mean(c["vs"][b, :n] * c["vo"][b, :n]))
+                assert np.max(np.abs(out[row] - want)) < 1e-12
+                assert np.max(np.abs(lse[row] - math.log(n))) < 1e-12
+            row += 1
+
+
+def test_per_token_key_scale_closed_form():
+    """Constant int8 keys k0 and all-ones queries: the score of token t is
+    qkScale * D * s_t * (k0 + o_t), so lse = log sum_t exp(score_t) over visible t."""
+    rng = np.random.default_rng([314, 94])
+    c = _antiquant_case(rng, kmode=1, vmode=1, offsets=True, D=3, max_kv=8)
+    c["q"][:] = 1.0
+    c["k"][:] = 7.0
+    _, lse = _oracle_aq(c, MASK_NONE, 4, 2, 0.9)
+    row = 0
+    for b, (ql, kl) in enumerate(zip(c["q_lens"], c["kv_lens"])):
+        for i in range(ql):
+            if kl == 0:
+                assert np.all(lse[row] == np.inf)
+            else:
+                sc = [0.9 * 3 * c["ks"][b, t] * (7.0 + c["ko"][b, t]) for t in range(kl)]
+                m = max(sc)
+                want = m + math.log(math.fsum(math.exp(x - m) for x in sc))
+                assert np.max(np.abs(lse[row] - want)) < 1e-12
+            row += 1
+
+
+def test_uniform_per_token_equals_uniform_per_channel():
+    """The same scale and offset everywhere gives the same result in either mode."""
+    rng = np.random.default_rng([314, 95])
+    c = _antiquant_case(rng, kmode=1, vmode=1, offsets=True)
+    S = c["ks"].shape[1]
+    tok = dict(c, ks=np.full((2, S), 0.013), vs=np.full((2, S), 0.007),
+               ko=np.full((2, S), -3.0), vo=np.full((2, S), 5.5))
+    chan = dict(c, ks=np.full((2, 5), 0.013), vs=np.full((2, 5), 0.007),
+                ko=np.full((2, 5), -3.0), vo=np.full((2, 5), 5.5), kmode=0, vmode=0)
+    a = _oracle_aq(tok, MASK_ALIBI, 4, 2, 0.8)
+    b = _oracle_aq(chan, MASK_ALIBI, 4, 2, 0.8)
+    _same(a[0], b[0])
+    _same(a[1], b[1])
+
+
 def test_empty_tensor_rules():
     """aclnnFusedInferAttentionScoreV4, Constraints, empty input: empty
     query/out returns empty; empty key/value gives out 0 and lse inf."""
