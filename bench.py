@@ -76,7 +76,15 @@ def algorithmic_counts(inp):
     qo_bytes = 2 * T * H * D * q_elt
     lse_bytes = T * H * 4 if inp["want_lse"] else 0
     table_bytes = int(np.sum((kl + bs - 1) // bs)) * 4
-    scale_bytes = 2 * Hkv * D * 4 if inp.get("key_scale") is not None else 0
+    # antiquant parameters: the whole per-channel tensors, or the per-token entries of
+    # the valid tokens
+    scale_bytes = 0
+    for name, mode in (("key_scale", "key_mode"), ("value_scale", "value_mode"),
+                       ("key_offset", "key_mode"), ("value_offset", "value_mode")):
+        if inp.get(name) is None:
+            continue
+        per_token = inp.get(mode, 0) == 1
+        scale_bytes += (int(np.sum(kl)) if per_token else Hkv * D) * 4
     nbytes = kv_bytes + qo_bytes + lse_bytes + table_bytes + scale_bytes
     return nbytes, flops
 
@@ -109,15 +117,22 @@ def cpu_baseline(inp, nbytes, flops, decode, budget_s):
 
     import oracle
     q = inp["query"].double().numpy()
+    np64 = lambda name: inp[name].double().numpy() if inp.get(name) is not None else None
     if inp["key"].dtype.is_floating_point:
         k = inp["key"].double().numpy()
         v = inp["value"].double().numpy()
-        ks = vs = None
     else:
         k = inp["key"].numpy()
         v = inp["value"].numpy()
-        ks = inp["key_scale"].double().numpy()
-        vs = inp["value_scale"].double().numpy()
+    ks, vs, ko, vo = np64("key_scale"), np64("value_scale"), np64("key_offset"), np64("value_offset")
+    kmode, vmode = inp.get("key_mode", 0), inp.get("value_mode", 0)
+
+    def dequant(x, b, scale, offset, mode):
+        if scale is None:
+            return x
+        if mode == 0:
+            return oracle.dequantize_per_channel(x, scale, offset)
+        return oracle.dequantize_per_token(x, scale[b], None if offset is None else offset[b])
     sl = inp["slopes"].double().numpy() if inp["slopes"] is not None else None
     table = inp["block_tables"].numpy()
     ql = inp["seq_len"].numpy().astype(np.int64)
@@ -134,9 +149,8 @@ def cpu_baseline(inp, nbytes, flops, decode, budget_s):
     for b in range(len(ql)):
         kb = oracle.gather_sequence(k, table[b], kl[b], bs)
         vb = oracle.gather_sequence(v, table[b], kl[b], bs)
-        if ks is not None:
-            kb = oracle.dequantize_per_channel(kb, ks)
-            vb = oracle.dequantize_per_channel(vb, vs)
+        kb = dequant(kb, b, ks, ko, kmode)
+        vb = dequant(vb, b, vs, vo, vmode)
         oracle.attention_contiguous(q[q0[b]:q0[b + 1]], kb, vb,
                                     oracle.query_positions(ql[b], kl[b]), inp["mask_type"],
                                     inp["qk_scale"], H, Hkv, sl)
@@ -198,10 +212,11 @@ def main():
            if w.lse else None)
 
     t_plan = time.perf_counter()
-    op = pa.pa_paged_attention_get_workspace_size(
+    op = pa.pa_paged_attention_get_workspace_size_ex(
         g["query"], g["key"], g["value"], g["block_tables"], None, g["seq_len"],
         g["kv_seq_len"], g["slopes"], g["mask_type"], g["head_num"], g["kv_head_num"],
-        g["qk_scale"], g["key_scale"], g["value_scale"], out, lse)
+        g["qk_scale"], g["key_scale"], g["value_scale"], g.get("key_offset"),
+        g.get("value_offset"), g.get("key_mode", 0), g.get("value_mode", 0), out, lse)
     plan_us = (time.perf_counter() - t_plan) * 1e6
     ws = pa.alloc_workspace(op.workspace_size, dev)
     info = pa.pa_op_describe(op)

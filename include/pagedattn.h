@@ -154,6 +154,52 @@ pa_status pa_paged_attention_get_workspace_size(
     const pa_tensor* attnOut, const pa_tensor* lse,
     uint64_t* workspaceSize, pa_op** op);
 
+/* Antiquant modes (aclnnFusedInferAttentionScoreV3, Constraints on the KV antiquant
+ * parameters).  The pages number the modes without printing the table; they allow
+ * key mode 0 with value mode 1 as the only pair of different modes, described as
+ * per-channel keys with per-token values, which fixes the numbering. */
+enum {
+    PA_ANTIQUANT_PER_CHANNEL = 0,   /* scale[kvh, d]: kvHeadNum*headSize elements */
+    PA_ANTIQUANT_PER_TOKEN = 1      /* scale[b, t]: shape (batch, S) or (1, batch, S), f32 */
+};
+
+/*
+ * Phase 1 with the full set of KV antiquant parameters (aclnnFusedInferAttentionScoreV3,
+ * Constraints on the KV antiquant parameters: per-channel and per-token modes, optional
+ * offsets).  Every argument not listed here means exactly what it means for
+ * pa_paged_attention_get_workspace_size, which is this call with NULL offsets and both
+ * modes PA_ANTIQUANT_PER_CHANNEL.
+ *
+ * Dequantisation of int8 K (V likewise): K_hat = scale * (K + offset).  The pages give
+ * no formula for the offset; it is taken as added to the stored integer before scaling
+ * (pass offset = -z for a zero point z).  Without offsets the dequant is symmetric.
+ *
+ * keyAntiquantMode, valueAntiquantMode
+ *              PA_ANTIQUANT_PER_CHANNEL or PA_ANTIQUANT_PER_TOKEN.  The two must be
+ *              equal, except key per-channel with value per-token; other values or pairs
+ *              give PA_ERR_PARAM_INVALID.  Modes other than per-channel need int8 K/V.
+ * keyAntiquantScale, valueAntiquantScale
+ *              per-channel: as for pa_paged_attention_get_workspace_size (f32 or the
+ *              query dtype, kvHeadNum*headSize contiguous elements; the two scales of a
+ *              per-channel pair share one dtype).  per-token: device f32, shape
+ *              (batch, S) or (1, batch, S) with S >= max_b kvSeqLen[b], last stride 1,
+ *              row stride free; token t of sequence b (its position in the sequence,
+ *              not its cache slot) uses element [b, t] for every kv head and channel.
+ * keyAntiquantOffset, valueAntiquantOffset
+ *              device, NULL for symmetric dequant.  Both NULL or both given.  Each has
+ *              the shape, strides and dtype of its scale.
+ */
+pa_status pa_paged_attention_get_workspace_size_ex(
+    const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
+    const pa_tensor* blockTables, const pa_tensor* mask,
+    const pa_tensor* seqLen, const pa_tensor* kvSeqLen, const pa_tensor* slopes,
+    int maskType, int32_t headNum, int32_t kvHeadNum, float qkScale,
+    const pa_tensor* keyAntiquantScale, const pa_tensor* valueAntiquantScale,
+    const pa_tensor* keyAntiquantOffset, const pa_tensor* valueAntiquantOffset,
+    int keyAntiquantMode, int valueAntiquantMode,
+    const pa_tensor* attnOut, const pa_tensor* lse,
+    uint64_t* workspaceSize, pa_op** op);
+
 /*
  * Phase 2: enqueue the computation on `stream` (a hipStream_t; NULL = the null
  * stream).  (PrefixEncoder, Definition: AtbSelfAttentionPrefixEncoder; the pages'

@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     Op,
+    PA_ANTIQUANT_PER_CHANNEL,
+    PA_ANTIQUANT_PER_TOKEN,
     PA_BF16,
     PA_ERR_HIP,
     PA_ERR_HOST_ALLOC,
@@ -35,6 +37,7 @@ from ._lib import (  # noqa: F401
     pa_op_set_timing_events,
     pa_paged_attention,
     pa_paged_attention_get_workspace_size,
+    pa_paged_attention_get_workspace_size_ex,
     pa_status_string,
     pa_version,
     paged_attention,

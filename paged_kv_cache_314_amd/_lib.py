@@ -24,6 +24,7 @@ PA_ERR_HOST_ALLOC = 6
 
 PA_F16, PA_BF16, PA_I8, PA_F32, PA_I32 = 1, 2, 3, 4, 5
 PA_MASK_NONE, PA_MASK_ALIBI, PA_MASK_CAUSAL = 0, 3, 9
+PA_ANTIQUANT_PER_CHANNEL, PA_ANTIQUANT_PER_TOKEN = 0, 1
 
 _DTYPE_CODE = {
     torch.float16: PA_F16,
@@ -35,6 +36,7 @@ _DTYPE_CODE = {
 
 EXPORTED = (
     "pa_paged_attention_get_workspace_size",
+    "pa_paged_attention_get_workspace_size_ex",
     "pa_paged_attention",
     "pa_op_destroy",
     "pa_op_describe",
@@ -81,6 +83,13 @@ def load():
         P, P, P, P, P, P, P, P,
         ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
         P, P, P, P,
+        ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p),
+    ]
+    lib.pa_paged_attention_get_workspace_size_ex.restype = ctypes.c_int
+    lib.pa_paged_attention_get_workspace_size_ex.argtypes = [
+        P, P, P, P, P, P, P, P,
+        ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+        P, P, P, P, ctypes.c_int, ctypes.c_int, P, P,
         ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p),
     ]
     lib.pa_paged_attention.restype = ctypes.c_int
@@ -184,6 +193,37 @@ def pa_paged_attention_get_workspace_size(query, key, value, block_tables, mask,
     return Op(handle.value, int(ws.value), keep)
 
 
+def pa_paged_attention_get_workspace_size_ex(query, key, value, block_tables, mask, seq_len,
+                                             kv_seq_len, slopes, mask_type, head_num,
+                                             kv_head_num, qk_scale, key_antiquant_scale,
+                                             value_antiquant_scale, key_antiquant_offset,
+                                             value_antiquant_offset, key_antiquant_mode,
+                                             value_antiquant_mode, attn_out, lse):
+    """Phase 1 with antiquant offsets and modes (include/pagedattn.h).  Returns an Op."""
+    lib = load()
+    descs = [
+        describe(query, device="cuda"), describe(key, device="cuda"),
+        describe(value, device="cuda"), describe(block_tables, device="cuda"),
+        describe(mask, device="cuda"), describe(seq_len, device="cpu"),
+        describe(kv_seq_len, device="cpu"), describe(slopes, device="cuda"),
+    ]
+    aq = [describe(t, device="cuda") for t in (key_antiquant_scale, value_antiquant_scale,
+                                               key_antiquant_offset, value_antiquant_offset)]
+    tail = [describe(attn_out, device="cuda"), describe(lse, device="cuda")]
+    ws = ctypes.c_uint64(0)
+    handle = ctypes.c_void_p(None)
+    st = lib.pa_paged_attention_get_workspace_size_ex(
+        *[_ref(d) for d in descs], int(mask_type), int(head_num), int(kv_head_num),
+        float(qk_scale), *[_ref(d) for d in aq], int(key_antiquant_mode),
+        int(value_antiquant_mode), *[_ref(d) for d in tail], ctypes.byref(ws),
+        ctypes.byref(handle))
+    _check(st)
+    keep = (query, key, value, block_tables, mask, seq_len, kv_seq_len, slopes,
+            key_antiquant_scale, value_antiquant_scale, key_antiquant_offset,
+            value_antiquant_offset, attn_out, lse)
+    return Op(handle.value, int(ws.value), keep)
+
+
 def pa_paged_attention(workspace, workspace_size, op, stream=None):
     """Phase 2: enqueue on ``stream`` (torch.cuda.Stream, raw handle int, or None =
     torch's current stream).  ``workspace`` is a uint8 CUDA tensor or None."""
@@ -247,7 +287,10 @@ def alloc_workspace(nbytes, device):
 
 def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len, *, head_num,
                     kv_head_num=0, qk_scale=1.0, mask_type=PA_MASK_NONE, slopes=None,
-                    key_antiquant_scale=None, value_antiquant_scale=None, want_lse=False,
+                    key_antiquant_scale=None, value_antiquant_scale=None,
+                    key_antiquant_offset=None, value_antiquant_offset=None,
+                    key_antiquant_mode=PA_ANTIQUANT_PER_CHANNEL,
+                    value_antiquant_mode=PA_ANTIQUANT_PER_CHANNEL, want_lse=False,
                     out=None, lse=None, stream=None):
     """One-shot helper: allocate out (and lse), plan, run, free the plan.
     Returns (out, lse or None)."""
@@ -255,9 +298,11 @@ def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len, *, hea
         out = torch.empty_like(query)
     if want_lse and lse is None:
         lse = torch.empty((query.shape[0], head_num), dtype=torch.float32, device=query.device)
-    op = pa_paged_attention_get_workspace_size(
+    op = pa_paged_attention_get_workspace_size_ex(
         query, key, value, block_tables, None, seq_len, kv_seq_len, slopes, mask_type,
-        head_num, kv_head_num, qk_scale, key_antiquant_scale, value_antiquant_scale, out, lse)
+        head_num, kv_head_num, qk_scale, key_antiquant_scale, value_antiquant_scale,
+        key_antiquant_offset, value_antiquant_offset, key_antiquant_mode,
+        value_antiquant_mode, out, lse)
     try:
         ws = alloc_workspace(op.workspace_size, query.device)
         pa_paged_attention(ws, op.workspace_size, op, stream)

@@ -67,6 +67,20 @@ pa_status ensure_staging(pa_op* op) {
     return PA_OK;
 }
 
+pa::AntiquantArgs antiquant_args(const pa::Plan& p) {
+    pa::AntiquantArgs q{};
+    q.koff = p.koff;
+    q.voff = p.voff;
+    q.ktok_stride = p.ktok_stride;
+    q.vtok_stride = p.vtok_stride;
+    q.kmode = p.kmode;
+    q.vmode = p.vmode;
+    q.vscale_is_f32 = p.vscale_type == PA_F32;
+    q.extended = (p.kmode != PA_ANTIQUANT_PER_CHANNEL || p.vmode != PA_ANTIQUANT_PER_CHANNEL ||
+                  p.koff != nullptr) ? 1 : 0;
+    return q;
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,6 +92,20 @@ pa_status pa_paged_attention_get_workspace_size(
     int32_t kvHeadNum, float qkScale, const pa_tensor* keyAntiquantScale,
     const pa_tensor* valueAntiquantScale, const pa_tensor* attnOut, const pa_tensor* lse,
     uint64_t* workspaceSize, pa_op** op) {
+    return pa_paged_attention_get_workspace_size_ex(
+        query, key, value, blockTables, mask, seqLen, kvSeqLen, slopes, maskType, headNum,
+        kvHeadNum, qkScale, keyAntiquantScale, valueAntiquantScale, nullptr, nullptr,
+        PA_ANTIQUANT_PER_CHANNEL, PA_ANTIQUANT_PER_CHANNEL, attnOut, lse, workspaceSize, op);
+}
+
+pa_status pa_paged_attention_get_workspace_size_ex(
+    const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
+    const pa_tensor* blockTables, const pa_tensor* mask, const pa_tensor* seqLen,
+    const pa_tensor* kvSeqLen, const pa_tensor* slopes, int maskType, int32_t headNum,
+    int32_t kvHeadNum, float qkScale, const pa_tensor* keyAntiquantScale,
+    const pa_tensor* valueAntiquantScale, const pa_tensor* keyAntiquantOffset,
+    const pa_tensor* valueAntiquantOffset, int keyAntiquantMode, int valueAntiquantMode,
+    const pa_tensor* attnOut, const pa_tensor* lse, uint64_t* workspaceSize, pa_op** op) {
     if (op != nullptr) *op = nullptr;
     if (workspaceSize == nullptr || op == nullptr)
         return fail(PA_ERR_NULLPTR, "workspaceSize and op must not be NULL");
@@ -87,7 +115,8 @@ pa_status pa_paged_attention_get_workspace_size(
     std::string err;
     const pa_status st = pa::plan(query, key, value, blockTables, mask, seqLen, kvSeqLen, slopes,
                                   maskType, headNum, kvHeadNum, qkScale, keyAntiquantScale,
-                                  valueAntiquantScale, attnOut, lse, h->plan, err);
+                                  valueAntiquantScale, keyAntiquantOffset, valueAntiquantOffset,
+                                  keyAntiquantMode, valueAntiquantMode, attnOut, lse, h->plan, err);
     if (st != PA_OK) {
         delete h;
         return fail(st, err);
@@ -174,6 +203,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.scale_is_f32 = p.scale_type == PA_F32;
         a.scale_log2 = scale_log2;
         a.wave_heads = p.decode_wave_heads;
+        a.aq = antiquant_args(p);
         e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, s,
                               op->t_start, op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
@@ -220,6 +250,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.mask_type = p.mask_type;
         a.scale_is_f32 = p.scale_type == PA_F32;
         a.scale_log2 = scale_log2;
+        a.aq = antiquant_args(p);
         e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, s,
                                op->t_start, op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
@@ -256,6 +287,8 @@ uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
     s += "\", \"workspace_bytes\": " + std::to_string(p.workspace_bytes);
     s += ", \"chunk_tiles\": " + std::to_string(p.decode_chunk_tiles);
     s += ", \"decode_wave_heads\": " + std::to_string(p.decode_wave_heads);
+    s += ", \"antiquant\": [" + std::to_string(p.kmode) + ", " + std::to_string(p.vmode) + ", " +
+         std::to_string(p.koff != nullptr ? 1 : 0) + "]";
     s += ", \"partial_slots\": " + std::to_string(p.partial_slots);
     s += ", \"decode_items\": [";
     for (size_t i = 0; i < p.decode_items.size(); ++i) {

@@ -28,6 +28,20 @@
 // row (their scores are masked, their V rows zeroed), and the next tile's loads are in
 // flight while the current tile is computed.  Block ids are read through the scalar
 // cache (one or two s_load per 32-token tile), so the table costs no vector load.
+//
+// General int8 antiquant (XQ; aclnnFusedInferAttentionScoreV3, Constraints on the KV
+// antiquant parameters), K_hat = scale * (K + offset):
+//   per-channel K offset   adds sum_d q'_d o_d (q' = q * sK * qkScale * log2 e) to every
+//                          score of a row: out is unchanged, the row max (hence lse and
+//                          the split partials' max) carries the constant
+//   per-token K            s_j = sK_j * (q'.k_j + oK_j * sum_d q'_d) with q' = q * qkScale
+//                          * log2 e (no channel factor)
+//   per-token V            P_j is multiplied by sV_j before the PV product (the row sum
+//                          keeps P_j), and sum_j P_j sV_j oV_j is added to every O_d
+//   per-channel V offset   out_d = sV_d * (O_d / l + oV_d)
+// Per-token scales / offsets of a tile: lane l loads entry T + (l & 31) of the K (l < 32)
+// or V (l >= 32) tensor with the tile's K rows, and each lane picks its tokens' values
+// with cross-lane reads.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -54,12 +68,14 @@ struct DecodeTileRegs {
     static constexpr int KN = I8 ? D / 64 : D / 32;   // 16-byte K loads per row
     u32x4 k[2][KN];
     std::conditional_t<I8, u32x2, u32x4> v[8];
+    float ta, tb;             // per-token scale / offset of one token (XQ only)
 };
 
 // WPH: the item holds 4 kv heads and wave w streams kv head kvh + w over the whole
 // tile range (else the 4 waves split the range of one kv head and merge in LDS)
-template <int D, bool BF16, bool I8, bool ALIBI, bool WPH>
+template <int D, bool BF16, bool I8, bool ALIBI, bool WPH, bool XQ>
 __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
+    static_assert(!XQ || I8, "general antiquant applies to int8 K/V");
     constexpr int KK = D / 32;                 // QK k-steps
     constexpr int KP = D / 64;                 // int8 16-byte loads per K row
     constexpr bool MBF = BF16 && !I8;          // MFMA element type (int8 path runs in f16)
@@ -86,6 +102,8 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     // ------------------------------------------------------------ Q operand
     u32x4 qhi[KK], qlo[KK];
     float s_mul;                               // multiplies the raw MFMA score
+    float qsum = 0.0f;                         // XQ, per-token K: sum_d q'_d of head col
+    float kconst = 0.0f;                       // XQ, per-channel K offset: sum_d q'_d oK_d
     if constexpr (!I8) {
         const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                                static_cast<int64_t>(it.qrow) * a.q_tok_stride +
@@ -120,19 +138,37 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
                     const uint32_t w = raw[e >> 1];
                     const float qv = half_to_f32<BF16>((e & 1) ? (w >> 16) : (w & 0xffffu));
                     const int d = d0 + 8 * h8 + e;
-                    float sk;
-                    if (a.scale_is_f32) {
-                        sk = static_cast<const float*>(a.kscale)[kvh * D + d];
-                    } else {
-                        sk = half_to_f32<BF16>(static_cast<const uint16_t*>(a.kscale)[kvh * D + d]);
+                    float sk = 1.0f;                 // per-token K: no channel factor
+                    if (!XQ || a.aq.kmode == 0) {
+                        if (a.scale_is_f32) {
+                            sk = static_cast<const float*>(a.kscale)[kvh * D + d];
+                        } else {
+                            sk = half_to_f32<BF16>(static_cast<const uint16_t*>(a.kscale)[kvh * D + d]);
+                        }
                     }
                     qf[kp][8 * h8 + e] = qv * sk * a.scale_log2;
                     amax = fmaxf(amax, fabsf(qf[kp][8 * h8 + e]));
+                    if constexpr (XQ) {
+                        if (a.aq.kmode == 1) {
+                            qsum += qf[kp][8 * h8 + e];
+                        } else if (a.aq.koff != nullptr) {
+                            const float ok = a.scale_is_f32
+                                ? static_cast<const float*>(a.aq.koff)[kvh * D + d]
+                                : half_to_f32<BF16>(static_cast<const uint16_t*>(a.aq.koff)[kvh * D + d]);
+                            kconst += qf[kp][8 * h8 + e] * ok;
+                        }
+                    }
                 }
             }
         }
         amax = fmaxf(amax, shfl_xor_f(amax, 16));
         amax = fmaxf(amax, shfl_xor_f(amax, 32));
+        if constexpr (XQ) {
+            qsum += shfl_xor_f(qsum, 16);
+            qsum += shfl_xor_f(qsum, 32);
+            kconst += shfl_xor_f(kconst, 16);
+            kconst += shfl_xor_f(kconst, 32);
+        }
         const bool ok = amax > 0.0f && amax < INFINITY;
         const float inv = ok ? 127.0f / amax : 0.0f;
         s_mul = ok ? amax * (1.0f / (127.0f * 256.0f)) : 0.0f;
@@ -161,6 +197,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     // --------------------------------------------------------------- state
     float m_run = -INFINITY;                    // running max (log2 units) of head `col`
     float l_run = 0.0f;                         // this lane's share of the running sum
+    float c_run = 0.0f;                         // XQ per-token V offsets: sum P sV oV
     f32x4 acc[8];
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -179,6 +216,22 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     const uint32_t vslot_bytes = static_cast<uint32_t>(a.v_slot_stride * ESZ);
 
     const uint32_t vcol = (I8 ? 8u : 16u) * static_cast<uint32_t>(col & (VCOLS - 1));
+
+    // XQ: this lane's per-token tensors (K for lanes 0..31, V for 32..63; a lane whose
+    // side is per-channel reads the other side's tensor, which is then per-token)
+    const bool ktok = XQ && a.aq.kmode == 1, vtok = XQ && a.aq.vmode == 1;
+    const bool tok_loads = ktok || vtok;
+    const bool tok_off = XQ && a.aq.koff != nullptr;
+    const bool kside = lane < 32 ? ktok : !vtok;
+    const float* tok_scale = nullptr;
+    const float* tok_offset = nullptr;
+    if constexpr (XQ) {
+        if (tok_loads) {
+            const int64_t row = static_cast<int64_t>(it.b) * (kside ? a.aq.ktok_stride : a.aq.vtok_stride);
+            tok_scale = static_cast<const float*>(kside ? a.kscale : a.vscale) + row;
+            if (tok_off) tok_offset = static_cast<const float*>(kside ? a.aq.koff : a.aq.voff) + row;
+        }
+    }
 
     // Each 16-token half of a 32-token tile lies inside one block (blockSize is a
     // multiple of 16 and tiles start at multiples of 32), so every load of a tile uses a
@@ -227,6 +280,14 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
             for (int i = 0; i < Tile::KN; ++i)
                 t.k[m][i] = *reinterpret_cast<const u32x4*>(b.kb[m] + (ro + 64u * i));
         }
+        if constexpr (XQ) {
+            if (tok_loads) {
+                // clamp to the sequence's last token (entries past kvSeqLen may not exist)
+                const int tk = min(b.T + (lane & 31), max(kvlen - 1, 0));
+                t.ta = tok_scale[tk];
+                if (tok_off) t.tb = tok_offset[tk];
+            }
+        }
     };
     auto issue_v = [&](Tile& t, const TileBase& b) {
 #pragma unroll
@@ -265,8 +326,28 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float x = c[r] * s_mul;
+                if constexpr (XQ) {
+                    if (ktok) {
+                        const int j = 16 * m + 4 * qg + r;      // token of this score in the tile
+                        const float sk = __shfl(t.ta, j);
+                        const float ok = tok_off ? __shfl(t.tb, j) : 0.0f;
+                        x = (x + ok * qsum) * sk;
+                    }
+                }
                 if constexpr (ALIBI) x += slope2 * static_cast<float>(T + 16 * m + 4 * qg + r - pos);
                 s[4 * m + r] = x;
+            }
+        }
+        // per-token V values of this lane's 8 tokens (read before issue_k refills t)
+        float pv_s[8], pv_o[8];
+        if constexpr (XQ) {
+            if (vtok) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int j = 32 + 16 * (i >> 2) + 4 * qg + (i & 3);
+                    pv_s[i] = __shfl(t.ta, j);
+                    pv_o[i] = tok_off ? __shfl(t.tb, j) : 0.0f;
+                }
             }
         }
         issue_k(t, next);
@@ -292,6 +373,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
             const float m_new = grow ? tmax : m_run;
             const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
             l_run *= alpha;
+            if constexpr (XQ) c_run *= alpha;
 #pragma unroll
             for (int n = 0; n < 8; ++n) acc[n] *= alpha;
             m_run = m_new;
@@ -302,6 +384,17 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
         for (int i = 0; i < 8; ++i) {
             p[i] = fast_exp2(s[i] - m_use);
             l_run += p[i];
+        }
+        if constexpr (XQ) {
+            if (vtok) {
+                // V_hat_j = sV_j (V_j + oV_j): weight P_j sV_j on V_j, and the offset part
+                // sum_j P_j sV_j oV_j (rows past kvlen have P = 0)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    p[i] *= pv_s[i];
+                    c_run = fmaf(p[i], pv_o[i], c_run);
+                }
+            }
         }
         u32x4 pop;
         pop.x = pack2<MBF>(p[0], p[1]);
@@ -377,12 +470,25 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
         }
     }
 
+    // per-channel V scale (and offset) of channel d of kv head c
+    auto vchan = [&](int c, int d, bool f32, const void* src) -> float {
+        return f32 ? static_cast<const float*>(src)[c * D + d]
+                   : half_to_f32<BF16>(static_cast<const uint16_t*>(src)[c * D + d]);
+    };
+    const bool vscale_f32 = XQ ? a.aq.vscale_is_f32 != 0 : a.scale_is_f32 != 0;
+    const bool voff_chan = XQ && !vtok && a.aq.voff != nullptr;
+    float c_tot = 0.0f;                         // XQ per-token V offsets, whole head
+    if constexpr (XQ) {
+        c_tot = c_run + shfl_xor_f(c_run, 16);
+        c_tot += shfl_xor_f(c_tot, 32);
+    }
+
     if constexpr (WPH) {
         // ---------------------------------------- each wave owns its kv head's result
         float L = l_run;
         L += shfl_xor_f(L, 16);
         L += shfl_xor_f(L, 32);
-        const float M = m_run;
+        const float M = m_run + kconst;
         const int slot = it.slot < 0 ? -1 : it.slot + wave * it.slot_stride;
         const int geff = a.group;                  // <= 16 in this mode
         if (!hvalid) return;
@@ -397,10 +503,13 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
             for (int n = 0; n < 8; ++n) {
                 o[n] = acc[n][r];
                 if constexpr (I8) {
-                    float sv;
-                    if (a.scale_is_f32) sv = static_cast<const float*>(a.vscale)[kvh * D + d0 + n];
-                    else sv = half_to_f32<BF16>(static_cast<const uint16_t*>(a.vscale)[kvh * D + d0 + n]);
-                    o[n] *= sv;
+                    if (vtok) {
+                        o[n] += c_tot;
+                    } else {
+                        const float sv = vchan(kvh, d0 + n, vscale_f32, a.vscale);
+                        if (voff_chan) o[n] = fmaf(vchan(kvh, d0 + n, vscale_f32, a.aq.voff), L, o[n]);
+                        o[n] *= sv;
+                    }
                 }
             }
             if (slot < 0) {
@@ -437,7 +546,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     l_tot += shfl_xor_f(l_tot, 16);
     l_tot += shfl_xor_f(l_tot, 32);
     if (qg == 0) {
-        s_m[wave][col] = m_run;
+        s_m[wave][col] = m_run + kconst;
         s_l[wave][col] = l_tot;
     }
     // acc[n][r] = O[head col][d = 32*qg + 8*r + n]
@@ -446,7 +555,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
             const int d = 32 * qg + 8 * r + n;
-            if (d < D) s_o[wave][col][d] = acc[n][r];
+            if (d < D) s_o[wave][col][d] = acc[n][r] + c_tot;
         }
     }
     __syncthreads();
@@ -469,10 +578,10 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
             }
         }
         if constexpr (I8) {
-            float sv;
-            if (a.scale_is_f32) sv = static_cast<const float*>(a.vscale)[it.kvh * D + d];
-            else sv = half_to_f32<BF16>(static_cast<const uint16_t*>(a.vscale)[it.kvh * D + d]);
-            O *= sv;
+            if (!vtok) {
+                if (voff_chan) O = fmaf(vchan(it.kvh, d, vscale_f32, a.aq.voff), L, O);
+                O *= vchan(it.kvh, d, vscale_f32, a.vscale);
+            }
         }
         const int out_head = it.kvh * a.group + hlocal;
         if (it.slot < 0) {
@@ -535,17 +644,29 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     }
 }
 
+template <int D, bool BF16, bool I8, bool XQ>
+void launch_decode_x(const DecodeArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
+                     hipEvent_t t1) {
+    const bool alibi = a.mask_type == PA_MASK_ALIBI;
+    if (a.wave_heads) {
+        if (alibi) launch_256(decode_kernel<D, BF16, I8, true, true, XQ>, n_items, stream, t0, t1, a);
+        else launch_256(decode_kernel<D, BF16, I8, false, true, XQ>, n_items, stream, t0, t1, a);
+    } else {
+        if (alibi) launch_256(decode_kernel<D, BF16, I8, true, false, XQ>, n_items, stream, t0, t1, a);
+        else launch_256(decode_kernel<D, BF16, I8, false, false, XQ>, n_items, stream, t0, t1, a);
+    }
+}
+
 template <int D, bool BF16, bool I8>
 hipError_t launch_decode_t(const DecodeArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
                            hipEvent_t t1) {
-    const bool alibi = a.mask_type == PA_MASK_ALIBI;
-    if (a.wave_heads) {
-        if (alibi) launch_256(decode_kernel<D, BF16, I8, true, true>, n_items, stream, t0, t1, a);
-        else launch_256(decode_kernel<D, BF16, I8, false, true>, n_items, stream, t0, t1, a);
-    } else {
-        if (alibi) launch_256(decode_kernel<D, BF16, I8, true, false>, n_items, stream, t0, t1, a);
-        else launch_256(decode_kernel<D, BF16, I8, false, false>, n_items, stream, t0, t1, a);
+    if constexpr (I8) {
+        if (a.aq.extended) {
+            launch_decode_x<D, BF16, true, true>(a, n_items, stream, t0, t1);
+            return hipGetLastError();
+        }
     }
+    launch_decode_x<D, BF16, I8, false>(a, n_items, stream, t0, t1);
     return hipGetLastError();
 }
 

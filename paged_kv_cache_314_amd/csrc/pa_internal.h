@@ -72,7 +72,9 @@ struct Plan {
     Mode mode = Mode::kNoop;
     pa_dtype qtype = PA_F16;     // query / out dtype
     pa_dtype kvtype = PA_F16;    // key / value dtype
-    pa_dtype scale_type = PA_F32;
+    pa_dtype scale_type = PA_F32;   // key antiquant scale dtype
+    pa_dtype vscale_type = PA_F32;  // value antiquant scale dtype
+    int32_t kmode = 0, vmode = 0;   // antiquant modes: 0 per-channel, 1 per-token
     int32_t batch = 0, head_num = 0, kv_head_num = 0, group = 1, head_groups = 1;
     int32_t head_size = 0, block_size = 0, num_blocks = 0, n_tokens = 0;
     int32_t mask_type = 0;
@@ -88,6 +90,9 @@ struct Plan {
     const float* slopes = nullptr;
     const void* kscale = nullptr;
     const void* vscale = nullptr;
+    const void* koff = nullptr;     // antiquant offsets (NULL: symmetric)
+    const void* voff = nullptr;
+    int64_t ktok_stride = 0, vtok_stride = 0;   // per-token scale / offset row strides
 
     // strides in elements
     int64_t q_tok_stride = 0, q_head_stride = 0, out_tok_stride = 0, out_head_stride = 0;
@@ -116,6 +121,8 @@ pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                const pa_tensor* seqLen, const pa_tensor* kvSeqLen, const pa_tensor* slopes,
                int maskType, int32_t headNum, int32_t kvHeadNum, float qkScale,
                const pa_tensor* keyAntiquantScale, const pa_tensor* valueAntiquantScale,
+               const pa_tensor* keyAntiquantOffset, const pa_tensor* valueAntiquantOffset,
+               int keyAntiquantMode, int valueAntiquantMode,
                const pa_tensor* attnOut, const pa_tensor* lse, Plan& p, std::string& err);
 
 }  // namespace pa

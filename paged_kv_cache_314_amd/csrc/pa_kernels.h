@@ -9,6 +9,18 @@
 
 namespace pa {
 
+// KV antiquant beyond symmetric per-channel scales (int8 K/V): K_hat = scale * (K + offset)
+// with per-channel [kvHeadNum, headSize] or per-token [batch, S] scales / offsets.
+struct AntiquantArgs {
+    const void* koff;       // offsets, layout and dtype of their scale; NULL: symmetric
+    const void* voff;
+    int64_t ktok_stride;    // per-token mode: row stride (elements) of the [batch, S] tensors
+    int64_t vtok_stride;
+    int32_t kmode, vmode;   // 0 per-channel, 1 per-token
+    int32_t vscale_is_f32;  // value scale dtype (the key scale's is scale_is_f32)
+    int32_t extended;       // anything but per-channel symmetric scales on both
+};
+
 struct DecodeArgs {
     const DecodeItem* items;
     const void* q;
@@ -31,6 +43,7 @@ struct DecodeArgs {
     int32_t scale_is_f32;   // antiquant scales are f32 (else the query dtype)
     float scale_log2;       // qkScale * log2(e)
     int32_t wave_heads;     // items of 4 kv heads, one per wave (DecodeItem.heads == 4)
+    AntiquantArgs aq;
 };
 
 struct CombineArgs {
@@ -62,6 +75,7 @@ struct PrefillArgs {
     int32_t mask_type;
     int32_t scale_is_f32;
     float scale_log2;
+    AntiquantArgs aq;
 };
 
 struct FillArgs {

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <map>
 #include <sstream>
+#include <tuple>
 
 #include "pa_internal.h"
 
@@ -226,6 +227,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                const pa_tensor* kvSeqLen, const pa_tensor* slopes, int maskType,
                int32_t headNum, int32_t kvHeadNum, float qkScale,
                const pa_tensor* keyScale, const pa_tensor* valueScale,
+               const pa_tensor* keyOffset, const pa_tensor* valueOffset, int kmode, int vmode,
                const pa_tensor* attnOut, const pa_tensor* lse, Plan& p) {
     // -- required descriptors (aclnnFusedInferAttentionScoreV3, Constraints: null inputs)
     REQUIRE(query, PA_ERR_NULLPTR, "query is NULL");
@@ -336,31 +338,6 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
     REQUIRE(bs <= 4096, PA_ERR_UNSUPPORTED, "blockSize " << bs << " > 4096");
     REQUIRE(key->data != nullptr && value->data != nullptr, PA_ERR_NULLPTR, "key/value data is NULL");
 
-    // scales (int8 only)
-    if (kv_i8) {
-        REQUIRE(keyScale != nullptr && valueScale != nullptr, PA_ERR_NULLPTR,
-                "int8 key/value need keyAntiquantScale and valueAntiquantScale");
-        check_desc(keyScale, "keyAntiquantScale");
-        check_desc(valueScale, "valueAntiquantScale");
-        for (const pa_tensor* s : {keyScale, valueScale}) {
-            REQUIRE(numel(s) == kvh_num * qv.d, PA_ERR_PARAM_INVALID,
-                    "antiquant scale must hold kvHeadNum*headSize = " << kvh_num * qv.d
-                                                                     << " elements, got " << numel(s));
-            REQUIRE(is_contiguous(s), PA_ERR_PARAM_INVALID, "antiquant scale must be contiguous");
-            REQUIRE(s->dtype == PA_F32 || s->dtype == query->dtype, PA_ERR_PARAM_INVALID,
-                    "antiquant scale dtype must be f32 or the query dtype");
-            REQUIRE(s->data != nullptr, PA_ERR_NULLPTR, "antiquant scale data is NULL");
-        }
-        REQUIRE(keyScale->dtype == valueScale->dtype, PA_ERR_PARAM_INVALID,
-                "key and value antiquant scales differ in dtype");
-        p.kscale = keyScale->data;
-        p.vscale = valueScale->data;
-        p.scale_type = static_cast<pa_dtype>(keyScale->dtype);
-    } else {
-        REQUIRE(keyScale == nullptr && valueScale == nullptr, PA_ERR_PARAM_INVALID,
-                "antiquant scales given for non-int8 key/value");
-    }
-
     // alignment of every vector access: 16-byte rows
     const int eb_q = 2, eb_kv = kv_i8 ? 1 : 2;
     REQUIRE(aligned16(query->data) && aligned16(attnOut->data) && aligned16(key->data) &&
@@ -425,6 +402,87 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
     REQUIRE(kv.blocks >= need_blocks, PA_ERR_PARAM_INVALID,
             "numBlocks " << kv.blocks << " < blocks the sequences need (" << need_blocks << ")");
     REQUIRE(blockTables->data != nullptr || max_blocks == 0, PA_ERR_NULLPTR, "blockTables data is NULL");
+
+    // antiquant parameters (int8 only; aclnnFusedInferAttentionScoreV3, Constraints on
+    // the KV antiquant parameters)
+    int32_t max_kv = 0;
+    for (int64_t b = 0; b < B; ++b) max_kv = std::max(max_kv, kl[b * kls]);
+    if (kv_i8) {
+        REQUIRE(keyScale != nullptr && valueScale != nullptr, PA_ERR_NULLPTR,
+                "int8 key/value need keyAntiquantScale and valueAntiquantScale");
+        REQUIRE((kmode == PA_ANTIQUANT_PER_CHANNEL || kmode == PA_ANTIQUANT_PER_TOKEN) &&
+                    (vmode == PA_ANTIQUANT_PER_CHANNEL || vmode == PA_ANTIQUANT_PER_TOKEN),
+                PA_ERR_PARAM_INVALID, "antiquant modes must be 0 (per-channel) or 1 (per-token)");
+        REQUIRE(kmode == vmode || (kmode == PA_ANTIQUANT_PER_CHANNEL && vmode == PA_ANTIQUANT_PER_TOKEN),
+                PA_ERR_PARAM_INVALID,
+                "key and value antiquant modes must be equal, or key per-channel with value per-token");
+        REQUIRE((keyOffset == nullptr) == (valueOffset == nullptr), PA_ERR_PARAM_INVALID,
+                "keyAntiquantOffset and valueAntiquantOffset must both be given or both be NULL");
+        // one scale (or offset) tensor: shape / dtype for its mode; returns the row stride
+        // of a per-token tensor (0 for per-channel)
+        auto check_aq = [&](const pa_tensor* t, int mode, const char* name) -> int64_t {
+            check_desc(t, name);
+            REQUIRE(t->data != nullptr, PA_ERR_NULLPTR, name << " data is NULL");
+            if (mode == PA_ANTIQUANT_PER_CHANNEL) {
+                REQUIRE(numel(t) == kvh_num * qv.d, PA_ERR_PARAM_INVALID,
+                        name << " (per-channel) must hold kvHeadNum*headSize = " << kvh_num * qv.d
+                             << " elements, got " << numel(t));
+                REQUIRE(is_contiguous(t), PA_ERR_PARAM_INVALID, name << " must be contiguous");
+                REQUIRE(t->dtype == PA_F32 || t->dtype == query->dtype, PA_ERR_PARAM_INVALID,
+                        name << " (per-channel) dtype must be f32 or the query dtype");
+                REQUIRE(reinterpret_cast<uintptr_t>(t->data) % elem_bytes(t->dtype) == 0,
+                        PA_ERR_PARAM_INVALID, name << " data must be aligned to its element size");
+                return 0;
+            }
+            REQUIRE(t->dtype == PA_F32, PA_ERR_PARAM_INVALID, name << " (per-token) must be f32");
+            const bool lead1 = t->ndim == 3 && t->shape[0] == 1;
+            REQUIRE(t->ndim == 2 || lead1, PA_ERR_PARAM_INVALID,
+                    name << " (per-token) must be (batch, S) or (1, batch, S)");
+            const int r = t->ndim - 2;
+            REQUIRE(t->shape[r] == B, PA_ERR_PARAM_INVALID,
+                    name << " (per-token) has " << t->shape[r] << " rows, batch is " << B);
+            REQUIRE(t->shape[r + 1] >= max_kv, PA_ERR_PARAM_INVALID,
+                    name << " (per-token) has " << t->shape[r + 1] << " columns, max kvSeqLen is " << max_kv);
+            REQUIRE(t->stride[r + 1] == 1 || t->shape[r + 1] <= 1, PA_ERR_PARAM_INVALID,
+                    name << " (per-token) columns must be contiguous");
+            REQUIRE(t->stride[r] >= 0 && (t->stride[r] >= t->shape[r + 1] || B == 1),
+                    PA_ERR_PARAM_INVALID, name << " (per-token) rows overlap");
+            REQUIRE(reinterpret_cast<uintptr_t>(t->data) % 4 == 0, PA_ERR_PARAM_INVALID,
+                    name << " (per-token) data must be 4-byte aligned");
+            return t->stride[r];
+        };
+        p.ktok_stride = check_aq(keyScale, kmode, "keyAntiquantScale");
+        p.vtok_stride = check_aq(valueScale, vmode, "valueAntiquantScale");
+        if (kmode == vmode && kmode == PA_ANTIQUANT_PER_CHANNEL)
+            REQUIRE(keyScale->dtype == valueScale->dtype, PA_ERR_PARAM_INVALID,
+                    "key and value antiquant scales differ in dtype");
+        if (keyOffset != nullptr) {
+            for (auto [off, sc, mode, row_stride, name] :
+                 {std::tuple{keyOffset, keyScale, kmode, p.ktok_stride, "keyAntiquantOffset"},
+                  std::tuple{valueOffset, valueScale, vmode, p.vtok_stride, "valueAntiquantOffset"}}) {
+                const int64_t st = check_aq(off, mode, name);
+                bool same_shape = off->ndim == sc->ndim;
+                for (int i = 0; same_shape && i < off->ndim; ++i) same_shape = off->shape[i] == sc->shape[i];
+                REQUIRE(off->dtype == sc->dtype && same_shape && st == row_stride, PA_ERR_PARAM_INVALID,
+                        name << " must have the shape, strides and dtype of its scale");
+            }
+            p.koff = keyOffset->data;
+            p.voff = valueOffset->data;
+        }
+        p.kscale = keyScale->data;
+        p.vscale = valueScale->data;
+        p.scale_type = static_cast<pa_dtype>(keyScale->dtype);
+        p.vscale_type = static_cast<pa_dtype>(valueScale->dtype);
+        p.kmode = kmode;
+        p.vmode = vmode;
+    } else {
+        REQUIRE(keyScale == nullptr && valueScale == nullptr, PA_ERR_PARAM_INVALID,
+                "antiquant scales given for non-int8 key/value");
+        REQUIRE(keyOffset == nullptr && valueOffset == nullptr, PA_ERR_PARAM_INVALID,
+                "antiquant offsets given for non-int8 key/value");
+        REQUIRE(kmode == PA_ANTIQUANT_PER_CHANNEL && vmode == PA_ANTIQUANT_PER_CHANNEL,
+                PA_ERR_PARAM_INVALID, "antiquant modes other than per-channel need int8 key/value");
+    }
 
     // slopes
     if (maskType == PA_MASK_ALIBI) {
@@ -605,11 +663,14 @@ pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                const pa_tensor* kvSeqLen, const pa_tensor* slopes, int maskType,
                int32_t headNum, int32_t kvHeadNum, float qkScale,
                const pa_tensor* keyAntiquantScale, const pa_tensor* valueAntiquantScale,
+               const pa_tensor* keyAntiquantOffset, const pa_tensor* valueAntiquantOffset,
+               int keyAntiquantMode, int valueAntiquantMode,
                const pa_tensor* attnOut, const pa_tensor* lse, Plan& p, std::string& err) {
     try {
         plan_impl(query, key, value, blockTables, mask, seqLen, kvSeqLen, slopes, maskType,
-                  headNum, kvHeadNum, qkScale, keyAntiquantScale, valueAntiquantScale, attnOut,
-                  lse, p);
+                  headNum, kvHeadNum, qkScale, keyAntiquantScale, valueAntiquantScale,
+                  keyAntiquantOffset, valueAntiquantOffset, keyAntiquantMode, valueAntiquantMode,
+                  attnOut, lse, p);
     } catch (const Fail& f) {
         err = f.msg;
         return f.status;

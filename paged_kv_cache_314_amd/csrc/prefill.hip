@@ -26,6 +26,11 @@
 // tile suffices, and the next tile's global loads are in flight during the MFMA work.
 // int8 K/V are converted exactly to f16 on the way into LDS; the per-channel K scale is
 // folded into Q (kept to ~22 bits as an f16 hi + lo pair), the V scale into the output.
+// General antiquant (aclnnFusedInferAttentionScoreV3, Constraints on the KV antiquant
+// parameters; K_hat = scale * (K + offset)): per-token K or V rows are dequantised on the
+// way into LDS, sK_j (K_j + oK_j) rounded to f16; a per-channel K offset adds
+// sum_d q'_d oK_d to every score of a row, which only moves the row max (lse); a
+// per-channel V offset gives out_d = sV_d (O_d / l + oV_d).
 #include <type_traits>
 
 #include "pa_device.h"
@@ -103,6 +108,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     // ---------------------------------------------------------------- Q^T
     u32x4 qhi[KS], qlo[KS];
     float s_mul;
+    // general int8 antiquant: per-token sides, and the per-channel K offset's row constant
+    const bool ktok = I8 && a.aq.kmode == 1, vtok = I8 && a.aq.vmode == 1;
+    const bool tok_off = I8 && a.aq.koff != nullptr;
+    float kconst = 0.0f;
     {
         const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                                static_cast<int64_t>(it.qrow0 + (qvalid ? qi : 0)) * a.q_tok_stride +
@@ -127,14 +136,23 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t w = raw[e >> 1];
                     const float qv = half_to_f32<BF16>((e & 1) ? (w >> 16) : (w & 0xffffu));
-                    float sk;
-                    if (a.scale_is_f32) sk = static_cast<const float*>(a.kscale)[kvh_off + d0 + e];
-                    else sk = half_to_f32<BF16>(static_cast<const uint16_t*>(a.kscale)[kvh_off + d0 + e]);
+                    float sk = 1.0f;                 // per-token K: dequantised in LDS
+                    if (!ktok) {
+                        if (a.scale_is_f32) sk = static_cast<const float*>(a.kscale)[kvh_off + d0 + e];
+                        else sk = half_to_f32<BF16>(static_cast<const uint16_t*>(a.kscale)[kvh_off + d0 + e]);
+                    }
                     qf[ks][e] = qv * sk * a.scale_log2;
                     amax = fmaxf(amax, fabsf(qf[ks][e]));
+                    if (!ktok && a.aq.koff != nullptr) {
+                        const float ok = a.scale_is_f32
+                            ? static_cast<const float*>(a.aq.koff)[kvh_off + d0 + e]
+                            : half_to_f32<BF16>(static_cast<const uint16_t*>(a.aq.koff)[kvh_off + d0 + e]);
+                        kconst += qf[ks][e] * ok;
+                    }
                 }
             }
             amax = fmaxf(amax, shfl_xor_f(amax, 32));
+            kconst += shfl_xor_f(kconst, 32);
             int ex = 0;
             if (amax > 0.0f && amax < INFINITY) {
                 int x;
@@ -213,6 +231,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     const int lds_v = (16 * wave + lrow) * VLD + EPC * lch;
 
     u32x4 kreg[NL], vreg[NL];
+    float ktok_s[NL], ktok_o[NL], vtok_s[NL], vtok_o[NL];   // per-token values of the rows
+    // per-token scale / offset of load i's row of tile jt (token clamped to kvlen - 1)
+    auto load_tok = [&](const void* sc, const void* off, int64_t stride, float (&vs)[NL],
+                        float (&vo)[NL], int jt) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int tok = min(jt * BN + 16 * wave + RPI * i + lrow, kvlen - 1);
+            const int64_t at = static_cast<int64_t>(it.b) * stride + tok;
+            vs[i] = static_cast<const float*>(sc)[at];
+            vo[i] = tok_off ? static_cast<const float*>(off)[at] : 0.0f;
+        }
+    };
     // uniform base of this wave's 16-key group of tile jt (a group wholly past kvlen
     // re-reads the tile's first group: its V rows are zeroed before they reach LDS, its
     // K rows are masked)
@@ -239,9 +269,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     };
     auto load_k = [&](int jt) {
         load_rows(kreg, group_base(kpool, kblk_bytes, kslot_bytes, jt), kslot_bytes, koff);
+        if (ktok) load_tok(a.kscale, a.aq.koff, a.aq.ktok_stride, ktok_s, ktok_o, jt);
     };
     auto load_v = [&](int jt) {
         load_rows(vreg, group_base(vpool, vblk_bytes, vslot_bytes, jt), vslot_bytes, voff);
+        if (vtok) load_tok(a.vscale, a.aq.voff, a.aq.vtok_stride, vtok_s, vtok_o, jt);
     };
     // 16-byte chunk(s) to LDS; int8 chunks become two f16 chunks (exact)
     auto put = [&](uint16_t* dst, const u32x4& x) {
@@ -255,8 +287,31 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             *reinterpret_cast<u32x4*>(dst + 8) = u32x4{c2.x, c2.y, c3.x, c3.y};
         }
     };
+    // 16 int8 values -> f16 of sc * (x + of), two 16-byte chunks (per-token rows)
+    auto put_tok = [&](uint16_t* dst, const u32x4& x, float sc, float of) {
+        if constexpr (I8) {
+            uint32_t w[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int lo = static_cast<int8_t>((x[q] >> (16 * h)) & 0xffu);
+                    const int hi = static_cast<int8_t>((x[q] >> (16 * h + 8)) & 0xffu);
+                    w[2 * q + h] = pack2<false>((static_cast<float>(lo) + of) * sc,
+                                                (static_cast<float>(hi) + of) * sc);
+                }
+            }
+            *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{w[4], w[5], w[6], w[7]};
+        }
+    };
     auto store_k = [&](int buf) {
         uint16_t* ks = s_k[buf] + lds_k;
+        if (ktok) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) put_tok(ks + RPI * i * KLD, kreg[i], ktok_s[i], ktok_o[i]);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < NL; ++i) put(ks + RPI * i * KLD, kreg[i]);
     };
@@ -271,6 +326,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 if (j0 + 16 * wave + RPI * i + lrow >= kvlen) vreg[i] = u32x4{0u, 0u, 0u, 0u};
         }
         uint16_t* vs = s_v[buf] + lds_v;
+        if (vtok) {
+            // rows past kvlen: zero after the dequant (their P is 0; keep them finite)
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const bool live = j0 + 16 * wave + RPI * i + lrow < kvlen;
+                put_tok(vs + RPI * i * VLD, vreg[i], live ? vtok_s[i] : 0.0f, vtok_o[i]);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < NL; ++i) put(vs + RPI * i * VLD, vreg[i]);
     };
@@ -550,10 +614,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             for (int c = 0; c < 4; ++c) {
                 float val = oacc[dt][4 * r4 + c] * inv;
                 if constexpr (I8) {
-                    float sv;
-                    if (a.scale_is_f32) sv = static_cast<const float*>(a.vscale)[kvh_off + d0 + c];
-                    else sv = half_to_f32<BF16>(static_cast<const uint16_t*>(a.vscale)[kvh_off + d0 + c]);
-                    val *= sv;
+                    if (!vtok) {
+                        const bool f32 = a.aq.extended ? a.aq.vscale_is_f32 != 0 : a.scale_is_f32 != 0;
+                        auto chan = [&](const void* src) {
+                            return f32 ? static_cast<const float*>(src)[kvh_off + d0 + c]
+                                       : half_to_f32<BF16>(static_cast<const uint16_t*>(src)[kvh_off + d0 + c]);
+                        };
+                        if (a.aq.voff != nullptr && L > 0.0f) val += chan(a.aq.voff);
+                        val *= chan(a.vscale);
+                    }
                 }
                 o[c] = val;
             }
@@ -565,7 +634,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
     if (g2 == 0 && a.lse != nullptr) {
         a.lse[static_cast<int64_t>(it.qrow0 + qi) * a.lse_tok_stride + h] =
-            (L > 0.0f) ? (m_ref + fast_log2(L)) * kLn2 : INFINITY;
+            (L > 0.0f) ? (m_ref + kconst + fast_log2(L)) * kLn2 : INFINITY;
     }
 }
 

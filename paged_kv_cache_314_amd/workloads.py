@@ -62,6 +62,7 @@ class Workload:
     pool: object = "exact"      # "exact", ("plus", 0.10) or an int block count
     table_width: object = None  # None = max blocks needed
     table_padding: str = "minus_one"   # "minus_one" | "ids"
+    antiquant: object = None    # int8 only: (key mode, value mode, offsets?); None = (0, 0, False)
     extra: dict = field(default_factory=dict)
 
 
@@ -83,6 +84,10 @@ WORKLOADS = {
     "decode_int8_long": Workload(
         "decode_int8_long", 5, "bf16", "i8", 32, 64, 8, 128, 128, "decode", 16384,
         MASK_NONE, 1.0 / math.sqrt(128.0), pool=("plus", 0.10)),
+    # the INT8 long decode with per-token scales and offsets on K and V (same shapes)
+    "decode_int8_pertoken_long": Workload(
+        "decode_int8_pertoken_long", 6, "bf16", "i8", 32, 64, 8, 128, 128, "decode", 16384,
+        MASK_NONE, 1.0 / math.sqrt(128.0), pool=("plus", 0.10), antiquant=(1, 1, True)),
 }
 
 
@@ -101,6 +106,22 @@ def _kv_pool(rng, shape, kv_dtype):
     if kv_dtype == "i8":
         return torch.from_numpy(rng.integers(-127, 128, size=shape, dtype=np.int8))
     return _normal(rng, shape, kv_dtype)
+
+
+def antiquant_params(rng, kmode, vmode, offsets, kv_head_num, head_size, batch, kv_lens,
+                     pad_cols=5):
+    """Random int8 antiquant scales (and offsets): per-channel (mode 0) [Hkv, D] or
+    per-token (mode 1) [batch, max(kv_lens) + pad_cols], fp32; scales U(0.005, 0.02),
+    offsets U(-20, 20).  Returns (key_scale, value_scale, key_offset, value_offset)."""
+    S = max([int(n) for n in kv_lens] + [0]) + pad_cols
+
+    def draw(mode, lo, hi):
+        shape = (kv_head_num, head_size) if mode == 0 else (batch, S)
+        return torch.from_numpy(rng.uniform(lo, hi, size=shape).astype(np.float32))
+    ks, vs = draw(kmode, 0.005, 0.02), draw(vmode, 0.005, 0.02)
+    ko = draw(kmode, -20.0, 20.0) if offsets else None
+    vo = draw(vmode, -20.0, 20.0) if offsets else None
+    return ks, vs, ko, vo
 
 
 def build_block_tables(rng, kv_lens, block_size, num_blocks, width, padding):
@@ -192,10 +213,14 @@ def make_inputs(w, seed=None, poison=False, kv_lens=None, q_scale=1.0):
     key = _kv_pool(rng, (num_blocks, bs, Hkv, D), w.kv_dtype)
     value = _kv_pool(rng, (num_blocks, bs, Hkv, D), w.kv_dtype)
     tables = build_block_tables(rng, kvl, bs, num_blocks, width, w.table_padding)
-    key_scale = value_scale = None
-    if w.kv_dtype == "i8":
+    key_scale = value_scale = key_offset = value_offset = None
+    kmode, vmode, offs = w.antiquant or (0, 0, False)
+    if w.kv_dtype == "i8" and w.antiquant is None:
         key_scale = torch.from_numpy(rng.uniform(0.005, 0.02, size=(Hkv, D)).astype(np.float32))
         value_scale = torch.from_numpy(rng.uniform(0.005, 0.02, size=(Hkv, D)).astype(np.float32))
+    elif w.kv_dtype == "i8":
+        key_scale, value_scale, key_offset, value_offset = antiquant_params(
+            rng, kmode, vmode, offs, Hkv, D, B, kvl)
     seq_len = torch.tensor(q_lens_fixed, dtype=torch.int32)
     kv_seq_len = torch.tensor(kvl, dtype=torch.int32)
     if poison:
@@ -207,6 +232,7 @@ def make_inputs(w, seed=None, poison=False, kv_lens=None, q_scale=1.0):
         seq_len=seq_len, kv_seq_len=kv_seq_len,
         slopes=alibi_slopes(H) if w.alibi else None,
         key_scale=key_scale, value_scale=value_scale,
+        key_offset=key_offset, value_offset=value_offset, key_mode=kmode, value_mode=vmode,
         mask_type=w.mask_type, head_num=H, kv_head_num=Hkv,
         qk_scale=float(w.qk_scale), want_lse=bool(w.lse),
     )
@@ -215,7 +241,7 @@ def make_inputs(w, seed=None, poison=False, kv_lens=None, q_scale=1.0):
 def make_random_case(seed, *, batch, head_num, kv_head_num, head_size, block_size,
                      q_lens, kv_lens, dtype="bf16", kv_dtype=None, mask_type=MASK_NONE,
                      qk_scale=None, extra_blocks=3, poison=True, q_scale=1.0,
-                     table_extra_cols=1):
+                     table_extra_cols=1, antiquant=None):
     """Small random case with explicit per-sequence lengths (parity tests).
 
     The pool has the needed blocks plus ``extra_blocks`` spare ones, handed
@@ -234,10 +260,14 @@ def make_random_case(seed, *, batch, head_num, kv_head_num, head_size, block_siz
     key = _kv_pool(rng, (num_blocks, bs, Hkv, D), kv_dtype)
     value = _kv_pool(rng, (num_blocks, bs, Hkv, D), kv_dtype)
     tables = build_block_tables(rng, kv_lens, bs, num_blocks, width, "minus_one")
-    key_scale = value_scale = None
-    if kv_dtype == "i8":
+    key_scale = value_scale = key_offset = value_offset = None
+    kmode, vmode, offs = antiquant or (0, 0, False)
+    if kv_dtype == "i8" and antiquant is None:
         key_scale = torch.from_numpy(rng.uniform(0.005, 0.02, size=(Hkv, D)).astype(np.float32))
         value_scale = torch.from_numpy(rng.uniform(0.005, 0.02, size=(Hkv, D)).astype(np.float32))
+    elif kv_dtype == "i8":
+        key_scale, value_scale, key_offset, value_offset = antiquant_params(
+            rng, kmode, vmode, offs, Hkv, D, len(kv_lens), kv_lens)
     seq_len = torch.tensor([int(x) for x in q_lens], dtype=torch.int32)
     kv_seq_len = torch.tensor([int(x) for x in kv_lens], dtype=torch.int32)
     if poison and num_blocks > 0:
@@ -253,6 +283,7 @@ def make_random_case(seed, *, batch, head_num, kv_head_num, head_size, block_siz
         query=query, key=key, value=value, block_tables=tables,
         seq_len=seq_len, kv_seq_len=kv_seq_len, slopes=slopes,
         key_scale=key_scale, value_scale=value_scale,
+        key_offset=key_offset, value_offset=value_offset, key_mode=kmode, value_mode=vmode,
         mask_type=mask_type, head_num=H, kv_head_num=Hkv,
         qk_scale=float(qk_scale), want_lse=True,
     )

@@ -15,7 +15,8 @@ LSE_RTOL = 1e-3
 
 def to_device(inp, device="cuda"):
     d = dict(inp)
-    for k in ("query", "key", "value", "block_tables", "slopes", "key_scale", "value_scale"):
+    for k in ("query", "key", "value", "block_tables", "slopes", "key_scale", "value_scale",
+              "key_offset", "value_offset"):
         if d.get(k) is not None:
             d[k] = d[k].to(device)
     return d
@@ -30,10 +31,11 @@ def gpu_run(inp, *, want_lse=True, out=None, lse=None, stream=None, keep_op=Fals
     if want_lse and lse is None:
         lse = torch.full((q.shape[0], g["head_num"]), float("nan"), dtype=torch.float32,
                          device=q.device)
-    op = pa.pa_paged_attention_get_workspace_size(
+    op = pa.pa_paged_attention_get_workspace_size_ex(
         q, g["key"], g["value"], g["block_tables"], None, g["seq_len"], g["kv_seq_len"],
         g["slopes"], g["mask_type"], g["head_num"], g["kv_head_num"], g["qk_scale"],
-        g["key_scale"], g["value_scale"], out, lse if want_lse else None)
+        g["key_scale"], g["value_scale"], g.get("key_offset"), g.get("value_offset"),
+        g.get("key_mode", 0), g.get("value_mode", 0), out, lse if want_lse else None)
     ws = pa.alloc_workspace(op.workspace_size, q.device)
     pa.pa_paged_attention(ws, op.workspace_size, op, stream)
     torch.cuda.synchronize()
@@ -51,16 +53,25 @@ def oracle_inputs(inp):
     else:
         k = key.double().numpy()
         v = value.double().numpy()
-    ks = inp["key_scale"].double().numpy() if inp.get("key_scale") is not None else None
-    vs = inp["value_scale"].double().numpy() if inp.get("value_scale") is not None else None
-    sl = inp["slopes"].double().numpy() if inp.get("slopes") is not None else None
-    return k, v, ks, vs, sl
+    np64 = lambda name: inp[name].double().numpy() if inp.get(name) is not None else None
+    aq = dict(ks=np64("key_scale"), vs=np64("value_scale"), ko=np64("key_offset"),
+              vo=np64("value_offset"), kmode=inp.get("key_mode", 0),
+              vmode=inp.get("value_mode", 0))
+    return k, v, aq, np64("slopes")
+
+
+def _dequant(x, b, scale, offset, mode):
+    if scale is None:
+        return x
+    if mode == 0:
+        return oracle.dequantize_per_channel(x, scale, offset)
+    return oracle.dequantize_per_token(x, scale[b], None if offset is None else offset[b])
 
 
 def oracle_run(inp, batches=None):
     """fp64 oracle result.  With ``batches`` only those sequences are computed; the
     function returns (out, lse, rows) where rows are the packed query rows covered."""
-    k, v, ks, vs, sl = oracle_inputs(inp)
+    k, v, aq, sl = oracle_inputs(inp)
     q = inp["query"].double().numpy()
     table = inp["block_tables"].numpy()
     ql = inp["seq_len"].numpy().astype(np.int64)
@@ -69,7 +80,9 @@ def oracle_run(inp, batches=None):
     if batches is None:
         out, lse = oracle.paged_attention(
             q, k, v, table, ql, kl, inp["mask_type"], H, Hkv, inp["qk_scale"], slopes=sl,
-            key_antiquant_scale=ks, value_antiquant_scale=vs)
+            key_antiquant_scale=aq["ks"], value_antiquant_scale=aq["vs"],
+            key_antiquant_offset=aq["ko"], value_antiquant_offset=aq["vo"],
+            key_antiquant_mode=aq["kmode"], value_antiquant_mode=aq["vmode"])
         return out, lse, np.arange(q.shape[0])
     q0 = np.concatenate([[0], np.cumsum(ql)])
     bs = k.shape[1]
@@ -77,9 +90,8 @@ def oracle_run(inp, batches=None):
     for b in batches:
         kb = oracle.gather_sequence(k, table[b], kl[b], bs)
         vb = oracle.gather_sequence(v, table[b], kl[b], bs)
-        if ks is not None:
-            kb = oracle.dequantize_per_channel(kb, ks)
-            vb = oracle.dequantize_per_channel(vb, vs)
+        kb = _dequant(kb, b, aq["ks"], aq["ko"], aq["kmode"])
+        vb = _dequant(vb, b, aq["vs"], aq["vo"], aq["vmode"])
         r = np.arange(q0[b], q0[b + 1])
         o, l = oracle.attention_contiguous(
             q[r], kb, vb, oracle.query_positions(ql[b], kl[b]), inp["mask_type"],

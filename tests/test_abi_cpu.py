@@ -69,17 +69,29 @@ class Case:
         self.vscale = desc([Hkv, D], pa.PA_F32) if kv_dtype == pa.PA_I8 else None
         self.out = desc([T, H, D], dtype)
         self.lse = desc([T, H], pa.PA_F32) if lse else None
+        self.koff = self.voff = None
+        self.kmode = self.vmode = 0
+        self.extended = False
+        self.kv_lens = [int(k) for k in kv_lens]
 
     def call(self):
         lib = pa.load()
         ws = ctypes.c_uint64(123)
         op = ctypes.c_void_p(None)
         r = lambda d: ctypes.byref(d) if d is not None else None
-        st = lib.pa_paged_attention_get_workspace_size(
-            r(self.query), r(self.key), r(self.value), r(self.table), r(self.mask),
-            r(self.seq_len), r(self.kv_seq_len), r(self.slopes), self.mask_type, self.H,
-            self.Hkv, self.scale, r(self.kscale), r(self.vscale), r(self.out), r(self.lse),
-            ctypes.byref(ws), ctypes.byref(op))
+        if self.extended:
+            st = lib.pa_paged_attention_get_workspace_size_ex(
+                r(self.query), r(self.key), r(self.value), r(self.table), r(self.mask),
+                r(self.seq_len), r(self.kv_seq_len), r(self.slopes), self.mask_type, self.H,
+                self.Hkv, self.scale, r(self.kscale), r(self.vscale), r(self.koff),
+                r(self.voff), self.kmode, self.vmode, r(self.out), r(self.lse),
+                ctypes.byref(ws), ctypes.byref(op))
+        else:
+            st = lib.pa_paged_attention_get_workspace_size(
+                r(self.query), r(self.key), r(self.value), r(self.table), r(self.mask),
+                r(self.seq_len), r(self.kv_seq_len), r(self.slopes), self.mask_type, self.H,
+                self.Hkv, self.scale, r(self.kscale), r(self.vscale), r(self.out), r(self.lse),
+                ctypes.byref(ws), ctypes.byref(op))
         return st, int(ws.value), op.value
 
     def plan(self):
@@ -338,6 +350,72 @@ def test_decode_wave_per_head_switch(monkeypatch):
     assert info["decode_wave_heads"] == 1
     info = _plan_named("decode_f16_small")
     assert info["decode_wave_heads"] == 0
+
+
+def _i8_case(kmode, vmode, offsets, S=None):
+    c = base(dtype=pa.PA_BF16, kv_dtype=pa.PA_I8, bs=32)
+    c.extended = True
+    c.kmode, c.vmode = kmode, vmode
+    S = max(c.kv_lens) if S is None else S
+    mk = lambda mode: desc([2, 128], pa.PA_F32) if mode == 0 else desc([2, S], pa.PA_F32)
+    c.kscale, c.vscale = mk(kmode), mk(vmode)
+    if offsets:
+        c.koff, c.voff = mk(kmode), mk(vmode)
+    return c
+
+
+def test_antiquant_modes_and_offsets_plan():
+    """Per-channel / per-token antiquant pairs the pages allow, with and without offsets."""
+    for kmode, vmode in ((0, 0), (1, 1), (0, 1)):
+        for offsets in (False, True):
+            c = _i8_case(kmode, vmode, offsets)
+            info = c.plan()
+            assert info["antiquant"] == [kmode, vmode, int(offsets)]
+            _check_decode_plan(info, [1, 1], [100, 37], 2, 4)
+    # (1, batch, S) form and a larger S are accepted
+    c = _i8_case(1, 1, True, S=160)
+    c.kscale = desc([1, 2, 160], pa.PA_F32)
+    c.koff = desc([1, 2, 160], pa.PA_F32)
+    c.vscale = desc([1, 2, 160], pa.PA_F32)
+    c.voff = desc([1, 2, 160], pa.PA_F32)
+    assert c.plan()["antiquant"] == [1, 1, 1]
+
+
+def test_antiquant_checks():
+    # key per-token with value per-channel is not one of the pages' pairs
+    _expect(_i8_case(1, 0, False), pa.PA_ERR_PARAM_INVALID, "modes")
+    c = _i8_case(0, 0, False)
+    c.kmode = 2
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "modes")
+    # offsets come in pairs
+    c = _i8_case(1, 1, True)
+    c.voff = None
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "both")
+    # per-token: f32 only, batch rows, S >= max kvSeqLen
+    c = _i8_case(1, 1, False)
+    c.kscale = desc([2, 100], pa.PA_BF16)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "f32")
+    c = _i8_case(1, 1, False)
+    c.kscale = desc([3, 100], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "rows")
+    c = _i8_case(1, 1, False, S=99)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "columns")
+    # an offset's shape must match its scale's
+    c = _i8_case(1, 1, True)
+    c.koff = desc([2, 120], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "shape")
+    c = _i8_case(0, 0, True)
+    c.koff = desc([2, 128], pa.PA_BF16)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "dtype")
+    # antiquant parameters on a 16-bit cache
+    c = base()
+    c.extended = True
+    c.kmode = c.vmode = 1
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "int8")
+    c = base()
+    c.extended = True
+    c.koff = c.voff = desc([2, 128], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "offsets")
 
 
 def test_kv_head_num_zero_means_head_num():

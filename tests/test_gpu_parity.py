@@ -40,6 +40,7 @@ SAMPLES = {  # sequences whose outputs the oracle checks one by one at full size
     "decode_bf16_batched": [0, 7, 21, 42, 63],
     "prefill_alibi_f16": [0, 5],
     "decode_int8_long": [0, 13, 31],
+    "decode_int8_pertoken_long": [2, 19, 30],
 }
 
 
@@ -54,7 +55,8 @@ def test_named_workload_parity(name):
     _say(f"[parity] {name} {st}")
 
 
-@pytest.mark.parametrize("name", ["decode_bf16_batched", "decode_int8_long"])
+@pytest.mark.parametrize("name", ["decode_bf16_batched", "decode_int8_long",
+                                  "decode_int8_pertoken_long"])
 def test_high_contrast_decode(name):
     """Queries x4 sharpen the softmax so the 2e-2 bf16 gate bites harder."""
     w = wl.WORKLOADS[name]
@@ -152,6 +154,50 @@ def test_decode_wave_per_head(case, monkeypatch):
     assert info["decode_wave_heads"] == 1
     ro, rl, rows = oracle_run(inp)
     compare(out, lse, ro, rl, rows, inp["query"].dtype, f"wave-per-head case {case}")
+
+
+ANTIQUANT_MODES = [(0, 0, True), (1, 1, False), (1, 1, True), (0, 1, False), (0, 1, True)]
+
+
+@pytest.mark.parametrize("aq", ANTIQUANT_MODES, ids=lambda m: f"k{m[0]}v{m[1]}o{int(m[2])}")
+@pytest.mark.parametrize("shape", ["plain", "alibi_d64", "splits", "wave_heads"])
+def test_decode_antiquant_modes(aq, shape, monkeypatch):
+    """int8 decode with per-channel / per-token scales and offsets against the oracle."""
+    _say(f"[decode antiquant] modes {aq} shape {shape}")
+    kw = dict(batch=3, head_num=8, kv_head_num=2, head_size=128, block_size=32,
+              q_lens=[1, 1, 1], kv_lens=[300, 45, 1], dtype="bf16", mask_type=pa.PA_MASK_NONE)
+    if shape == "alibi_d64":
+        kw.update(head_size=64, dtype="f16", mask_type=pa.PA_MASK_ALIBI, kv_lens=[97, 160, 33])
+    elif shape == "splits":
+        monkeypatch.setenv("PA_DECODE_CHUNK_TILES", "8")
+        kw.update(kv_lens=[1500, 257, 31])
+    elif shape == "wave_heads":
+        monkeypatch.setenv("PA_DECODE_WAVE_HEADS", "1")
+        kw.update(head_num=32, kv_head_num=8, kv_lens=[700, 64, 2049], block_size=64)
+    inp = wl.make_random_case(400 + len(shape), kv_dtype="i8", antiquant=aq, **kw)
+    out, lse, op, ws = gpu_run(inp, keep_op=True)
+    info = pa.pa_op_describe(op)
+    op.destroy()
+    assert info["antiquant"] == [aq[0], aq[1], int(aq[2])]
+    if shape == "splits":
+        assert len(info["combine_items"]) > 0
+    if shape == "wave_heads":
+        assert info["decode_wave_heads"] == 1
+    ro, rl, rows = oracle_run(inp)
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"decode antiquant {aq} {shape}")
+
+
+@pytest.mark.parametrize("aq", ANTIQUANT_MODES, ids=lambda m: f"k{m[0]}v{m[1]}o{int(m[2])}")
+@pytest.mark.parametrize("mask", [pa.PA_MASK_CAUSAL, pa.PA_MASK_ALIBI])
+def test_prefill_antiquant_modes(aq, mask):
+    """int8 prefill (prefix encoder) with per-channel / per-token scales and offsets."""
+    _say(f"[prefill antiquant] modes {aq} mask {mask}")
+    inp = wl.make_random_case(500 + mask, batch=3, head_num=8, kv_head_num=2, head_size=128,
+                              block_size=32, q_lens=[70, 1, 130], kv_lens=[200, 33, 130],
+                              dtype="f16", kv_dtype="i8", mask_type=mask, antiquant=aq)
+    out, lse = gpu_run(inp)
+    ro, rl, rows = oracle_run(inp)
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"prefill antiquant {aq} {mask}")
 
 
 def test_decode_skips_sequences_without_query():
