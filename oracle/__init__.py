@@ -14,7 +14,8 @@ Sources (the pages this follows):
   * aclnnFusedInferAttentionScoreV4 / V3, "Function" (formula
     Softmax(QK^T/sqrt(d) + mask) V), "Constraints" (empty-tensor rules,
     deterministic computation, paged-attention layout, GQA divisibility,
-    per-channel and per-token KV antiquant with optional offsets, and the
+    per-channel and per-token KV antiquant with optional offsets, FLOAT8_E4M3FN
+    key/value codes, and the
     softmax-LSE decomposition used by
     ring attention).
   * PrefixEncoder (Ascend Transformer Boost SelfAttention, calcType
@@ -33,6 +34,7 @@ from .attention import (
     MASK_CAUSAL,
     ANTIQUANT_PER_CHANNEL,
     ANTIQUANT_PER_TOKEN,
+    decode_e4m3fn,
     gather_sequence,
     dequantize_per_channel,
     dequantize_per_token,

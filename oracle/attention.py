@@ -41,6 +41,25 @@ ANTIQUANT_PER_CHANNEL = 0
 ANTIQUANT_PER_TOKEN = 1
 
 
+def decode_e4m3fn(codes):
+    """Real values of FLOAT8_E4M3FN codes (aclnnFusedInferAttentionScoreV3, Constraints:
+    key/value may be FLOAT8_E4M3FN in the fake-quantization scenario).
+
+    The format (OCP 8-bit floating point, E4M3 "FN"): bit 7 sign, bits 6..3 a biased
+    exponent e (bias 7), bits 2..0 a mantissa m.  e > 0 gives (1 + m/8) * 2^(e-7);
+    e == 0 gives the subnormal (m/8) * 2^-6; e == 15 with m == 7 is NaN; there is no
+    infinity (e == 15, m < 7 are ordinary values up to 448).
+    codes: integer array of byte values 0..255.  Returns float64.
+    """
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
 def gather_sequence(pool, table_row, kv_len, block_size):
     """Contiguous rows [kv_len, kvHeadNum, headSize] of one sequence.
 
@@ -151,7 +170,7 @@ def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len,
                     key_antiquant_scale=None, value_antiquant_scale=None,
                     key_antiquant_offset=None, value_antiquant_offset=None,
                     key_antiquant_mode=ANTIQUANT_PER_CHANNEL,
-                    value_antiquant_mode=ANTIQUANT_PER_CHANNEL):
+                    value_antiquant_mode=ANTIQUANT_PER_CHANNEL, kv_format=None):
     """Reference result of the paged fused-attention call.
 
     PrefixEncoder, Definition and Members: query [nTokens, headNum, headSize]
@@ -167,6 +186,8 @@ def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len,
     int8 key/value are dequantised before anything else: per channel
     (mode 0) with scales / offsets [kvHeadNum, headSize], or per token
     (mode 1) with scales / offsets [batch, S] (a leading 1 is dropped).
+    kv_format="e4m3fn": key/value hold FLOAT8_E4M3FN byte codes, decoded
+    (decode_e4m3fn) before the per-channel scales are applied.
     Returns out [nTokens, headNum, headSize] and lse [nTokens, headNum].
     """
     if kv_head_num == 0:
@@ -188,6 +209,9 @@ def paged_attention(query, key, value, block_tables, seq_len, kv_seq_len,
         ql, kl = int(seq_len[b]), int(kv_seq_len[b])
         k_b = gather_sequence(key, block_tables[b], kl, block_size)
         v_b = gather_sequence(value, block_tables[b], kl, block_size)
+        if kv_format == "e4m3fn":
+            k_b = decode_e4m3fn(k_b)
+            v_b = decode_e4m3fn(v_b)
         k_b = _dequantize(k_b, b, key_antiquant_scale, key_antiquant_offset,
                           key_antiquant_mode)
         v_b = _dequantize(v_b, b, value_antiquant_scale, value_antiquant_offset,

@@ -496,6 +496,44 @@ def test_uniform_per_token_equals_uniform_per_channel():
     _same(a[1], b[1])
 
 
+def test_e4m3fn_decode_matches_library_and_hand_values():
+    """Every byte code against torch's float8_e4m3fn conversion (a library routine),
+    and the format's landmark values worked by hand."""
+    codes = np.arange(256)
+    mine = oracle.decode_e4m3fn(codes)
+    lib = torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(lib))
+    fin = ~np.isnan(lib)
+    assert np.array_equal(mine[fin], lib[fin])
+    hand = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+            0x39: 1.125, 0xB8: -1.0, 0x7E: 448.0, 0xFE: -448.0, 0x40: 2.0, 0x30: 0.5}
+    for c, v in hand.items():
+        assert oracle.decode_e4m3fn([c])[0] == v, hex(c)
+    assert np.isnan(oracle.decode_e4m3fn([0x7F, 0xFF])).all()
+
+
+def test_fp8_equals_float_on_decoded_pool():
+    """FLOAT8_E4M3FN codes with per-channel scales equal the fp cache of the decoded,
+    scaled values."""
+    rng = np.random.default_rng([314, 96])
+    c = _random_case(rng, B=2, H=4, Hkv=2, D=6, bs=4, mask=MASK_ALIBI)
+    k = rng.integers(0, 256, size=c["k"].shape)
+    v = rng.integers(0, 256, size=c["v"].shape)
+    k[(k & 0x7F) == 0x7F] = 0x10                       # no NaN codes
+    v[(v & 0x7F) == 0x7F] = 0x22
+    ks = rng.uniform(0.005, 0.02, size=(2, 6))
+    vs = rng.uniform(0.005, 0.02, size=(2, 6))
+    a = oracle.paged_attention(c["q"], k, v, c["table"], c["q_lens"], c["kv_lens"], MASK_ALIBI,
+                               4, 2, 0.3, slopes=c["slopes"], key_antiquant_scale=ks,
+                               value_antiquant_scale=vs, kv_format="e4m3fn")
+    kf = oracle.decode_e4m3fn(k) * ks[None, None]
+    vf = oracle.decode_e4m3fn(v) * vs[None, None]
+    b = oracle.paged_attention(c["q"], kf, vf, c["table"], c["q_lens"], c["kv_lens"],
+                               MASK_ALIBI, 4, 2, 0.3, slopes=c["slopes"])
+    _same(a[0], b[0])
+    _same(a[1], b[1])
+
+
 def test_empty_tensor_rules():
     """aclnnFusedInferAttentionScoreV4, Constraints, empty input: empty
     query/out returns empty; empty key/value gives out 0 and lse inf."""
