@@ -113,12 +113,17 @@ def cpu_baseline(inp, nbytes, flops, decode, budget_s):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
     whole sequences, one after another, until the time budget is spent."""
     import numpy as np
+    import torch
     from threadpoolctl import threadpool_info
 
     import oracle
     q = inp["query"].double().numpy()
     np64 = lambda name: inp[name].double().numpy() if inp.get(name) is not None else None
-    if inp["key"].dtype.is_floating_point:
+    fp8 = inp["key"].dtype == torch.float8_e4m3fn
+    if fp8:
+        k = inp["key"].view(torch.uint8).numpy()
+        v = inp["value"].view(torch.uint8).numpy()
+    elif inp["key"].dtype.is_floating_point:
         k = inp["key"].double().numpy()
         v = inp["value"].double().numpy()
     else:
@@ -149,6 +154,8 @@ def cpu_baseline(inp, nbytes, flops, decode, budget_s):
     for b in range(len(ql)):
         kb = oracle.gather_sequence(k, table[b], kl[b], bs)
         vb = oracle.gather_sequence(v, table[b], kl[b], bs)
+        if fp8:
+            kb, vb = oracle.decode_e4m3fn(kb), oracle.decode_e4m3fn(vb)
         kb = dequant(kb, b, ks, ko, kmode)
         vb = dequant(vb, b, vs, vo, vmode)
         oracle.attention_contiguous(q[q0[b]:q0[b + 1]], kb, vb,

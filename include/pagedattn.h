@@ -67,7 +67,8 @@ typedef enum pa_dtype {
     PA_BF16 = 2,
     PA_I8 = 3,
     PA_F32 = 4,
-    PA_I32 = 5
+    PA_I32 = 5,
+    PA_F8E4M3 = 6   /* FLOAT8_E4M3FN byte codes (OCP E4M3: bias 7, no infinity) */
 } pa_dtype;
 
 /* Tensor descriptor.  shape[0..ndim-1] and stride[0..ndim-1] (in elements, not bytes)
@@ -103,7 +104,10 @@ typedef struct pa_op pa_op;
  *              16 bytes; attnOut rows and heads must not overlap).  Data 16-byte aligned.
  * key, value   device, [numBlocks, blockSize, kvHeadNum, headSize] or
  *              [numBlocks, blockSize, kvHeadNum*headSize] (layout BnBsH), dtype = query
- *              dtype, or int8 with both antiquant scales given.  Same shape and dtype.
+ *              dtype, or int8 / FLOAT8_E4M3FN (PA_F8E4M3) with both antiquant scales
+ *              given (aclnnFusedInferAttentionScoreV3, Constraints, fake-quantization
+ *              scenario; fp8 takes per-channel scales without offsets, and its NaN codes
+ *              must not occur in a valid token).  Same shape and dtype.
  *              d stride 1; block, slot and head strides are free (multiples of 16
  *              bytes), so a (numBlocks, kvHeadNum, blockSize, headSize) cache can be
  *              passed as its permuted view.  Data 16-byte aligned.
@@ -130,8 +134,8 @@ typedef struct pa_op pa_op;
  * keyAntiquantScale, valueAntiquantScale
  *              device, kvHeadNum*headSize elements (shapes [kvHeadNum, headSize],
  *              [1, kvHeadNum, headSize], [kvHeadNum*headSize] ... all accepted),
- *              contiguous, f32 or the query dtype.  Required iff key/value are int8:
- *              per-channel symmetric dequant K_hat[t,c,d] = scale[c,d] * K[t,c,d]
+ *              contiguous, f32 or the query dtype.  Required iff key/value are int8 or
+ *              fp8: per-channel symmetric dequant K_hat[t,c,d] = scale[c,d] * K[t,c,d]
  *              (aclnnFusedInferAttentionScoreV3, Constraints on antiquantScale,
  *              per-channel mode; no offset).
  * attnOut      device, same shape form and dtype as query; written in full.

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     PA_ERR_WORKSPACE_TOO_SMALL,
     PA_F16,
     PA_F32,
+    PA_F8E4M3,
     PA_I8,
     PA_I32,
     PA_MASK_ALIBI,

@@ -22,7 +22,7 @@ PA_ERR_WORKSPACE_TOO_SMALL = 4
 PA_ERR_HIP = 5
 PA_ERR_HOST_ALLOC = 6
 
-PA_F16, PA_BF16, PA_I8, PA_F32, PA_I32 = 1, 2, 3, 4, 5
+PA_F16, PA_BF16, PA_I8, PA_F32, PA_I32, PA_F8E4M3 = 1, 2, 3, 4, 5, 6
 PA_MASK_NONE, PA_MASK_ALIBI, PA_MASK_CAUSAL = 0, 3, 9
 PA_ANTIQUANT_PER_CHANNEL, PA_ANTIQUANT_PER_TOKEN = 0, 1
 
@@ -32,6 +32,7 @@ _DTYPE_CODE = {
     torch.int8: PA_I8,
     torch.float32: PA_F32,
     torch.int32: PA_I32,
+    torch.float8_e4m3fn: PA_F8E4M3,
 }
 
 EXPORTED = (

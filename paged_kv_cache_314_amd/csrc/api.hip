@@ -141,7 +141,8 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         return fail(PA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = p.qtype == PA_BF16;
-    const bool i8 = p.kvtype == PA_I8;
+    const bool f8 = p.kvtype == PA_F8E4M3;
+    const bool i8 = p.kvtype == PA_I8 || f8;      // one-byte K/V
     hipError_t e;
 
     if (p.mode == pa::Mode::kFill) {
@@ -204,8 +205,8 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.scale_log2 = scale_log2;
         a.wave_heads = p.decode_wave_heads;
         a.aq = antiquant_args(p);
-        e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, s,
-                              op->t_start, op->t_stop);
+        e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, f8,
+                              s, op->t_start, op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
         if (!p.combine_items.empty()) {
             pa::CombineArgs c{};
@@ -251,8 +252,8 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.scale_is_f32 = p.scale_type == PA_F32;
         a.scale_log2 = scale_log2;
         a.aq = antiquant_args(p);
-        e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, s,
-                               op->t_start, op->t_stop);
+        e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, f8,
+                               s, op->t_start, op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
     }
     // the kernels read the op's work lists from host memory until they finish

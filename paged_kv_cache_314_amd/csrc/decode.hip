@@ -29,6 +29,11 @@
 // flight while the current tile is computed.  Block ids are read through the scalar
 // cache (one or two s_load per 32-token tile), so the table costs no vector load.
 //
+// FLOAT8_E4M3FN K/V (F8): the one-byte loads of the int8 path; Q (K scale folded in) is
+// an f16 operand, normalised by a power of two per head, and each 16-byte K load is
+// expanded exactly to f16 (two codes per conversion) as the A operands of two f16 MFMA
+// k-steps; V rows are expanded and transposed like the int8 ones.
+//
 // General int8 antiquant (XQ; aclnnFusedInferAttentionScoreV3, Constraints on the KV
 // antiquant parameters), K_hat = scale * (K + offset):
 //   per-channel K offset   adds sum_d q'_d o_d (q' = q * sK * qkScale * log2 e) to every
@@ -73,9 +78,11 @@ struct DecodeTileRegs {
 
 // WPH: the item holds 4 kv heads and wave w streams kv head kvh + w over the whole
 // tile range (else the 4 waves split the range of one kv head and merge in LDS)
-template <int D, bool BF16, bool I8, bool ALIBI, bool WPH, bool XQ>
+// I8: one-byte K/V with per-channel scales; F8 (with I8): the bytes are FLOAT8_E4M3FN codes
+template <int D, bool BF16, bool I8, bool F8, bool ALIBI, bool WPH, bool XQ>
 __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     static_assert(!XQ || I8, "general antiquant applies to int8 K/V");
+    static_assert(!F8 || (I8 && !XQ), "fp8 K/V: one-byte loads, per-channel scales only");
     constexpr int KK = D / 32;                 // QK k-steps
     constexpr int KP = D / 64;                 // int8 16-byte loads per K row
     constexpr bool MBF = BF16 && !I8;          // MFMA element type (int8 path runs in f16)
@@ -170,10 +177,31 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
             kconst += shfl_xor_f(kconst, 32);
         }
         const bool ok = amax > 0.0f && amax < INFINITY;
-        const float inv = ok ? 127.0f / amax : 0.0f;
-        s_mul = ok ? amax * (1.0f / (127.0f * 256.0f)) : 0.0f;
+        if constexpr (F8) {
+            // f16 operand y = q' * 2^ex, |y| < 2^15; k-step kk = 2 kp + h holds channels
+            // 64 kp + 16 qg + 8 h .. +7 (the K load layout)
+            int ex = 0;
+            if (ok) {
+                int x;
+                frexpf(amax, &x);
+                ex = 14 - x;
+                ex = ex > 120 ? 120 : (ex < -120 ? -120 : ex);
+            }
+            const float up = ldexpf(1.0f, ex);
+            s_mul = ldexpf(1.0f, -ex);
 #pragma unroll
-        for (int kp = 0; kp < KP; ++kp) {
+            for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    qhi[kk][e] = pack2<false>(qf[kk >> 1][8 * (kk & 1) + 2 * e] * up,
+                                              qf[kk >> 1][8 * (kk & 1) + 2 * e + 1] * up);
+                qlo[kk] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        const float inv = ok ? 127.0f / amax : 0.0f;
+        if constexpr (!F8) s_mul = ok ? amax * (1.0f / (127.0f * 256.0f)) : 0.0f;
+#pragma unroll
+        for (int kp = 0; kp < (F8 ? 0 : KP); ++kp) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 uint32_t hw = 0u, lw = 0u;
@@ -312,6 +340,14 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
                 c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) c = mfma16x16x32<MBF>(t.k[m][kk], qhi[kk], c);
+            } else if constexpr (F8) {
+                c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    const u32x4& raw = t.k[m][kk >> 1];
+                    const u32x4 kop = f8x8_to_f16x8(raw[2 * (kk & 1)], raw[2 * (kk & 1) + 1]);
+                    c = mfma16x16x32<false>(kop, qhi[kk], c);
+                }
             } else {
                 i32x4 ch = {0, 0, 0, 0}, cl = {0, 0, 0, 0};
 #pragma unroll
@@ -412,7 +448,7 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
             for (int r = 0; r < 8; ++r) {
                 const bool ok = T + 16 * (r >> 2) + 4 * qg + (r & 3) < kvlen;
                 VT z = {};
-                vrow[r] = ok ? vrow[r] : z;      // an int8 0 converts to f16 0 exactly
+                vrow[r] = ok ? vrow[r] : z;      // an int8 / fp8 0 converts to f16 0 exactly
             }
         }
         if constexpr (I8) {
@@ -420,7 +456,8 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
                 u32x4 vop[4];
-                i8_rows_to_f16_cols_half(vrow, w, vop);
+                if constexpr (F8) f8_rows_to_f16_cols_half(vrow, w, vop);
+                else i8_rows_to_f16_cols_half(vrow, w, vop);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[4 * w + j] = mfma16x16x32<MBF>(vop[j], pop, acc[4 * w + j]);
             }
@@ -644,30 +681,41 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     }
 }
 
-template <int D, bool BF16, bool I8, bool XQ>
+template <int D, bool BF16, bool I8, bool F8, bool XQ>
 void launch_decode_x(const DecodeArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
                      hipEvent_t t1) {
     const bool alibi = a.mask_type == PA_MASK_ALIBI;
     if (a.wave_heads) {
-        if (alibi) launch_256(decode_kernel<D, BF16, I8, true, true, XQ>, n_items, stream, t0, t1, a);
-        else launch_256(decode_kernel<D, BF16, I8, false, true, XQ>, n_items, stream, t0, t1, a);
+        if (alibi) launch_256(decode_kernel<D, BF16, I8, F8, true, true, XQ>, n_items, stream, t0, t1, a);
+        else launch_256(decode_kernel<D, BF16, I8, F8, false, true, XQ>, n_items, stream, t0, t1, a);
     } else {
-        if (alibi) launch_256(decode_kernel<D, BF16, I8, true, false, XQ>, n_items, stream, t0, t1, a);
-        else launch_256(decode_kernel<D, BF16, I8, false, false, XQ>, n_items, stream, t0, t1, a);
+        if (alibi) launch_256(decode_kernel<D, BF16, I8, F8, true, false, XQ>, n_items, stream, t0, t1, a);
+        else launch_256(decode_kernel<D, BF16, I8, F8, false, false, XQ>, n_items, stream, t0, t1, a);
     }
 }
 
-template <int D, bool BF16, bool I8>
+template <int D, bool BF16, bool I8, bool F8>
 hipError_t launch_decode_t(const DecodeArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
                            hipEvent_t t1) {
-    if constexpr (I8) {
+    if constexpr (I8 && !F8) {
         if (a.aq.extended) {
-            launch_decode_x<D, BF16, true, true>(a, n_items, stream, t0, t1);
+            launch_decode_x<D, BF16, true, false, true>(a, n_items, stream, t0, t1);
             return hipGetLastError();
         }
     }
-    launch_decode_x<D, BF16, I8, false>(a, n_items, stream, t0, t1);
+    launch_decode_x<D, BF16, I8, F8, false>(a, n_items, stream, t0, t1);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs& a, int n_items, bool bf16, bool i8, bool f8,
+                           hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+    if (f8) return bf16 ? launch_decode_t<D, true, true, true>(a, n_items, stream, t0, t1)
+                        : launch_decode_t<D, false, true, true>(a, n_items, stream, t0, t1);
+    if (i8) return bf16 ? launch_decode_t<D, true, true, false>(a, n_items, stream, t0, t1)
+                        : launch_decode_t<D, false, true, false>(a, n_items, stream, t0, t1);
+    return bf16 ? launch_decode_t<D, true, false, false>(a, n_items, stream, t0, t1)
+                : launch_decode_t<D, false, false, false>(a, n_items, stream, t0, t1);
 }
 
 template <int D, bool BF16>
@@ -679,18 +727,10 @@ hipError_t launch_combine_t(const CombineArgs& a, int n_items, hipStream_t strea
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int n_items, int head_size, bool bf16, bool i8,
-                         hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+                         bool f8, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     if (n_items <= 0) return hipSuccess;
-    if (head_size == 128) {
-        if (i8) return bf16 ? launch_decode_t<128, true, true>(a, n_items, stream, t0, t1)
-                            : launch_decode_t<128, false, true>(a, n_items, stream, t0, t1);
-        return bf16 ? launch_decode_t<128, true, false>(a, n_items, stream, t0, t1)
-                    : launch_decode_t<128, false, false>(a, n_items, stream, t0, t1);
-    }
-    if (i8) return bf16 ? launch_decode_t<64, true, true>(a, n_items, stream, t0, t1)
-                        : launch_decode_t<64, false, true>(a, n_items, stream, t0, t1);
-    return bf16 ? launch_decode_t<64, true, false>(a, n_items, stream, t0, t1)
-                : launch_decode_t<64, false, false>(a, n_items, stream, t0, t1);
+    if (head_size == 128) return launch_decode_d<128>(a, n_items, bf16, i8, f8, stream, t0, t1);
+    return launch_decode_d<64>(a, n_items, bf16, i8, f8, stream, t0, t1);
 }
 
 hipError_t launch_combine(const CombineArgs& a, int n_items, int head_size, bool bf16,

@@ -114,6 +114,40 @@ __device__ __forceinline__ void i8_rows_to_f16_cols_half(const u32x2 (&rows)[8],
     }
 }
 
+// FLOAT8_E4M3FN codes -> f16, exactly (every E4M3 value is an f16 value): the gfx950
+// conversion takes the two codes of one 16-bit word of its source.
+template <bool HI>
+__device__ __forceinline__ uint32_t f8x2_to_f16x2(uint32_t w) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 codes (a = codes 0..3, b = 4..7) -> 8 f16 in order
+__device__ __forceinline__ u32x4 f8x8_to_f16x8(uint32_t a, uint32_t b) {
+    return u32x4{f8x2_to_f16x2<false>(a), f8x2_to_f16x2<true>(a),
+                 f8x2_to_f16x2<false>(b), f8x2_to_f16x2<true>(b)};
+}
+
+// The fp8 counterpart of i8_rows_to_f16_cols_half: 8 rows of 8 codes (dword w = columns
+// 4w .. 4w+3) -> 4 PV operands, out[j][i] = f16 pair (row 2i, row 2i+1) of column 4w + j.
+// One perm pairs the two rows' codes per column, one conversion expands a pair.
+__device__ __forceinline__ void f8_rows_to_f16_cols_half(const u32x2 (&rows)[8], int w,
+                                                         u32x4 (&out)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t a = rows[2 * i][w];        // row 2i
+        const uint32_t b = rows[2 * i + 1][w];    // row 2i+1
+        // [a.b0, b.b0, a.b1, b.b1] and [a.b2, b.b2, a.b3, b.b3]
+        const uint32_t t01 = __builtin_amdgcn_perm(b, a, 0x05010400u);
+        const uint32_t t23 = __builtin_amdgcn_perm(b, a, 0x07030602u);
+        out[0][i] = f8x2_to_f16x2<false>(t01);
+        out[1][i] = f8x2_to_f16x2<true>(t01);
+        out[2][i] = f8x2_to_f16x2<false>(t23);
+        out[3][i] = f8x2_to_f16x2<true>(t23);
+    }
+}
+
 // ----------------------------------------------------------------------- MFMA
 // D(16x16 f32) += A(16x32) * B(32x16); lane l holds A row l%16 / B column l%16 with
 // k = 8*(l/16) .. 8*(l/16)+7, and D column l%16, rows 4*(l/16) .. 4*(l/16)+3.

@@ -87,12 +87,15 @@ struct FillArgs {
 
 // t0 / t1 (optional): events attached to the kernel's own dispatch, so that their
 // timestamps bracket the kernel alone (hipExtLaunchKernelGGL)
+// i8: one-byte K/V (int8, or FLOAT8_E4M3FN codes when f8)
 hipError_t launch_decode(const DecodeArgs& a, int n_items, int head_size, bool bf16, bool i8,
-                         hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+                         bool f8, hipStream_t stream, hipEvent_t t0 = nullptr,
+                         hipEvent_t t1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, int n_items, int head_size, bool bf16,
                           hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int n_items, int head_size, bool bf16, bool i8,
-                          hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+                          bool f8, hipStream_t stream, hipEvent_t t0 = nullptr,
+                          hipEvent_t t1 = nullptr);
 
 // 256-thread launch of `kernel` over n workgroups, with timing events if given
 template <typename K, typename A>

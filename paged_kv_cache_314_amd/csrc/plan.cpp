@@ -32,7 +32,8 @@ int elem_bytes(int32_t dt) {
     switch (dt) {
         case PA_F16:
         case PA_BF16: return 2;
-        case PA_I8: return 1;
+        case PA_I8:
+        case PA_F8E4M3: return 1;
         case PA_F32:
         case PA_I32: return 4;
         default: return 0;
@@ -44,6 +45,7 @@ const char* dtype_name(int32_t dt) {
         case PA_F16: return "f16";
         case PA_BF16: return "bf16";
         case PA_I8: return "i8";
+        case PA_F8E4M3: return "f8e4m3";
         case PA_F32: return "f32";
         case PA_I32: return "i32";
         default: return "?";
@@ -320,9 +322,12 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
             "headSize " << qv.d << " not supported (64 or 128)");
 
     // key / value
-    const bool kv_i8 = key->dtype == PA_I8;
+    // one-byte caches: INT8 and FLOAT8_E4M3FN (aclnnFusedInferAttentionScoreV3, Constraints,
+    // fake-quantization scenario), both dequantised with antiquant scales
+    const bool kv_f8 = key->dtype == PA_F8E4M3;
+    const bool kv_i8 = key->dtype == PA_I8 || kv_f8;
     REQUIRE(key->dtype == query->dtype || kv_i8, PA_ERR_PARAM_INVALID,
-            "key dtype " << dtype_name(key->dtype) << " must equal the query dtype or be i8");
+            "key dtype " << dtype_name(key->dtype) << " must equal the query dtype or be i8 / f8e4m3");
     REQUIRE(value->dtype == key->dtype, PA_ERR_PARAM_INVALID, "value dtype differs from key dtype");
     const PoolView kv = pool_view(key, "key", kvh_num);
     const PoolView vv = pool_view(value, "value", kvh_num);
@@ -332,7 +337,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
     REQUIRE(kv.d == qv.d, PA_ERR_PARAM_INVALID,
             "key headSize " << kv.d << " differs from query headSize " << qv.d);
     const int64_t bs = kv.slots;
-    const int64_t bs_align = kv_i8 ? 32 : 16;   // aclnnFusedInferAttentionScoreV3: 16 (f16/bf16), 32 (int8)
+    const int64_t bs_align = kv_i8 ? 32 : 16;   // aclnnFusedInferAttentionScoreV3: 16 (f16/bf16), 32 (int8, fp8)
     REQUIRE(bs > 0 && bs % bs_align == 0, PA_ERR_PARAM_INVALID,
             "blockSize " << bs << " must be a positive multiple of " << bs_align);
     REQUIRE(bs <= 4096, PA_ERR_UNSUPPORTED, "blockSize " << bs << " > 4096");
@@ -409,7 +414,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
     for (int64_t b = 0; b < B; ++b) max_kv = std::max(max_kv, kl[b * kls]);
     if (kv_i8) {
         REQUIRE(keyScale != nullptr && valueScale != nullptr, PA_ERR_NULLPTR,
-                "int8 key/value need keyAntiquantScale and valueAntiquantScale");
+                "int8 / f8e4m3 key/value need keyAntiquantScale and valueAntiquantScale");
         REQUIRE((kmode == PA_ANTIQUANT_PER_CHANNEL || kmode == PA_ANTIQUANT_PER_TOKEN) &&
                     (vmode == PA_ANTIQUANT_PER_CHANNEL || vmode == PA_ANTIQUANT_PER_TOKEN),
                 PA_ERR_PARAM_INVALID, "antiquant modes must be 0 (per-channel) or 1 (per-token)");
@@ -418,6 +423,11 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                 "key and value antiquant modes must be equal, or key per-channel with value per-token");
         REQUIRE((keyOffset == nullptr) == (valueOffset == nullptr), PA_ERR_PARAM_INVALID,
                 "keyAntiquantOffset and valueAntiquantOffset must both be given or both be NULL");
+        // FLOAT8_E4M3FN: per-channel scales only, no offsets (Constraints on the KV
+        // antiquant parameters, per-channel mode)
+        REQUIRE(!kv_f8 || (kmode == PA_ANTIQUANT_PER_CHANNEL && vmode == PA_ANTIQUANT_PER_CHANNEL &&
+                           keyOffset == nullptr),
+                PA_ERR_PARAM_INVALID, "f8e4m3 key/value take per-channel antiquant scales without offsets");
         // one scale (or offset) tensor: shape / dtype for its mode; returns the row stride
         // of a per-token tensor (0 for per-channel)
         auto check_aq = [&](const pa_tensor* t, int mode, const char* name) -> int64_t {

@@ -26,6 +26,7 @@
 // tile suffices, and the next tile's global loads are in flight during the MFMA work.
 // int8 K/V are converted exactly to f16 on the way into LDS; the per-channel K scale is
 // folded into Q (kept to ~22 bits as an f16 hi + lo pair), the V scale into the output.
+// FLOAT8_E4M3FN K/V take the int8 path with the codes expanded exactly to f16 instead.
 // General antiquant (aclnnFusedInferAttentionScoreV3, Constraints on the KV antiquant
 // parameters; K_hat = scale * (K + offset)): per-token K or V rows are dequantised on the
 // way into LDS, sK_j (K_j + oK_j) rounded to f16; a per-channel K offset adds
@@ -61,8 +62,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 
 // MASK: 0 = none, 1 = causal, 2 = ALiBi (+ causal), fixed at compile time so that the
 // per-score work of each variant holds no run-time selects.
-template <int D, bool BF16, bool I8, int MASK>
+// I8: one-byte K/V (int8, or FLOAT8_E4M3FN codes when F8) with per-channel scales
+template <int D, bool BF16, bool I8, bool F8, int MASK>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
+    static_assert(!F8 || I8, "fp8 K/V use the one-byte path");
     constexpr bool MBF = BF16 && !I8;
     constexpr int KS = D / 16;            // QK k-steps (32x32x16)
     constexpr int DT = D / 32;            // PV output row blocks
@@ -109,7 +112,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     u32x4 qhi[KS], qlo[KS];
     float s_mul;
     // general int8 antiquant: per-token sides, and the per-channel K offset's row constant
-    const bool ktok = I8 && a.aq.kmode == 1, vtok = I8 && a.aq.vmode == 1;
+    const bool ktok = I8 && !F8 && a.aq.kmode == 1, vtok = I8 && !F8 && a.aq.vmode == 1;
     const bool tok_off = I8 && a.aq.koff != nullptr;
     float kconst = 0.0f;
     {
@@ -279,6 +282,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     auto put = [&](uint16_t* dst, const u32x4& x) {
         if constexpr (!I8) {
             *reinterpret_cast<u32x4*>(dst) = x;
+        } else if constexpr (F8) {
+            *reinterpret_cast<u32x4*>(dst) = f8x8_to_f16x8(x.x, x.y);
+            *reinterpret_cast<u32x4*>(dst + 8) = f8x8_to_f16x8(x.z, x.w);
         } else {
             static_assert(KLW == 2, "int8 chunks expand to two f16 chunks");
             const u32x2 c0 = i8x4_to_f16x4(x.x), c1 = i8x4_to_f16x4(x.y);
@@ -638,33 +644,36 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int D, bool BF16, bool I8>
+template <int D, bool BF16, bool I8, bool F8>
 hipError_t launch_prefill_t(const PrefillArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
                             hipEvent_t t1) {
     if (a.mask_type == PA_MASK_ALIBI)
-        launch_256(prefill_kernel<D, BF16, I8, 2>, n_items, stream, t0, t1, a);
+        launch_256(prefill_kernel<D, BF16, I8, F8, 2>, n_items, stream, t0, t1, a);
     else if (a.mask_type == PA_MASK_CAUSAL)
-        launch_256(prefill_kernel<D, BF16, I8, 1>, n_items, stream, t0, t1, a);
+        launch_256(prefill_kernel<D, BF16, I8, F8, 1>, n_items, stream, t0, t1, a);
     else
-        launch_256(prefill_kernel<D, BF16, I8, 0>, n_items, stream, t0, t1, a);
+        launch_256(prefill_kernel<D, BF16, I8, F8, 0>, n_items, stream, t0, t1, a);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_d(const PrefillArgs& a, int n_items, bool bf16, bool i8, bool f8,
+                            hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+    if (f8) return bf16 ? launch_prefill_t<D, true, true, true>(a, n_items, stream, t0, t1)
+                        : launch_prefill_t<D, false, true, true>(a, n_items, stream, t0, t1);
+    if (i8) return bf16 ? launch_prefill_t<D, true, true, false>(a, n_items, stream, t0, t1)
+                        : launch_prefill_t<D, false, true, false>(a, n_items, stream, t0, t1);
+    return bf16 ? launch_prefill_t<D, true, false, false>(a, n_items, stream, t0, t1)
+                : launch_prefill_t<D, false, false, false>(a, n_items, stream, t0, t1);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, int n_items, int head_size, bool bf16, bool i8,
-                          hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+                          bool f8, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     if (n_items <= 0) return hipSuccess;
-    if (head_size == 128) {
-        if (i8) return bf16 ? launch_prefill_t<128, true, true>(a, n_items, stream, t0, t1)
-                            : launch_prefill_t<128, false, true>(a, n_items, stream, t0, t1);
-        return bf16 ? launch_prefill_t<128, true, false>(a, n_items, stream, t0, t1)
-                    : launch_prefill_t<128, false, false>(a, n_items, stream, t0, t1);
-    }
-    if (i8) return bf16 ? launch_prefill_t<64, true, true>(a, n_items, stream, t0, t1)
-                        : launch_prefill_t<64, false, true>(a, n_items, stream, t0, t1);
-    return bf16 ? launch_prefill_t<64, true, false>(a, n_items, stream, t0, t1)
-                : launch_prefill_t<64, false, false>(a, n_items, stream, t0, t1);
+    if (head_size == 128) return launch_prefill_d<128>(a, n_items, bf16, i8, f8, stream, t0, t1);
+    return launch_prefill_d<64>(a, n_items, bf16, i8, f8, stream, t0, t1);
 }
 
 }  // namespace pa

@@ -38,7 +38,8 @@ MASK_NONE = 0
 MASK_ALIBI = 3
 MASK_CAUSAL = 9
 
-_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
+_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
+           "f8": torch.float8_e4m3fn}
 
 
 @dataclass
@@ -47,7 +48,7 @@ class Workload:
     name: str
     index: int
     dtype: str                  # query / out dtype: "f16" | "bf16"
-    kv_dtype: str               # "f16" | "bf16" | "i8"
+    kv_dtype: str               # "f16" | "bf16" | "i8" | "f8"
     batch: int
     head_num: int
     kv_head_num: int
@@ -85,6 +86,10 @@ WORKLOADS = {
         "decode_int8_long", 5, "bf16", "i8", 32, 64, 8, 128, 128, "decode", 16384,
         MASK_NONE, 1.0 / math.sqrt(128.0), pool=("plus", 0.10)),
     # the INT8 long decode with per-token scales and offsets on K and V (same shapes)
+    # the INT8 long decode's shapes with a FLOAT8_E4M3FN cache and per-channel scales
+    "decode_fp8_long": Workload(
+        "decode_fp8_long", 7, "bf16", "f8", 32, 64, 8, 128, 128, "decode", 16384,
+        MASK_NONE, 1.0 / math.sqrt(128.0), pool=("plus", 0.10)),
     "decode_int8_pertoken_long": Workload(
         "decode_int8_pertoken_long", 6, "bf16", "i8", 32, 64, 8, 128, 128, "decode", 16384,
         MASK_NONE, 1.0 / math.sqrt(128.0), pool=("plus", 0.10), antiquant=(1, 1, True)),
@@ -105,6 +110,11 @@ def _normal(rng, shape, dtype):
 def _kv_pool(rng, shape, kv_dtype):
     if kv_dtype == "i8":
         return torch.from_numpy(rng.integers(-127, 128, size=shape, dtype=np.int8))
+    if kv_dtype == "f8":
+        # FLOAT8_E4M3FN codes of N(0, 64^2) values (clamped to the format's +-448), so
+        # that the codes span the format's exponent range; RNE by torch
+        x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(64.0)
+        return torch.from_numpy(np.clip(x, -448.0, 448.0)).to(torch.float8_e4m3fn)
     return _normal(rng, shape, kv_dtype)
 
 
@@ -161,6 +171,8 @@ def poison_unused(pool, used):
     mask = ~used
     if pool.dtype == torch.int8:
         pool[mask] = -128
+    elif pool.dtype == torch.float8_e4m3fn:
+        pool.view(torch.uint8)[mask] = 0x7F         # a NaN code
     else:
         pool[mask] = float("nan")
     return pool
@@ -215,7 +227,7 @@ def make_inputs(w, seed=None, poison=False, kv_lens=None, q_scale=1.0):
     tables = build_block_tables(rng, kvl, bs, num_blocks, width, w.table_padding)
     key_scale = value_scale = key_offset = value_offset = None
     kmode, vmode, offs = w.antiquant or (0, 0, False)
-    if w.kv_dtype == "i8" and w.antiquant is None:
+    if w.kv_dtype in ("i8", "f8") and w.antiquant is None:
         key_scale = torch.from_numpy(rng.uniform(0.005, 0.02, size=(Hkv, D)).astype(np.float32))
         value_scale = torch.from_numpy(rng.uniform(0.005, 0.02, size=(Hkv, D)).astype(np.float32))
     elif w.kv_dtype == "i8":
@@ -262,7 +274,7 @@ def make_random_case(seed, *, batch, head_num, kv_head_num, head_size, block_siz
     tables = build_block_tables(rng, kv_lens, bs, num_blocks, width, "minus_one")
     key_scale = value_scale = key_offset = value_offset = None
     kmode, vmode, offs = antiquant or (0, 0, False)
-    if kv_dtype == "i8" and antiquant is None:
+    if kv_dtype in ("i8", "f8") and antiquant is None:
         key_scale = torch.from_numpy(rng.uniform(0.005, 0.02, size=(Hkv, D)).astype(np.float32))
         value_scale = torch.from_numpy(rng.uniform(0.005, 0.02, size=(Hkv, D)).astype(np.float32))
     elif kv_dtype == "i8":

@@ -47,16 +47,22 @@ def gpu_run(inp, *, want_lse=True, out=None, lse=None, stream=None, keep_op=Fals
 
 def oracle_inputs(inp):
     key, value = inp["key"], inp["value"]
+    kv_format = None
     if key.dtype == torch.int8:
         k = key.numpy().astype(np.int64)
         v = value.numpy().astype(np.int64)
+    elif key.dtype == torch.float8_e4m3fn:
+        # byte codes: the oracle decodes them itself
+        k = key.view(torch.uint8).numpy().astype(np.int64)
+        v = value.view(torch.uint8).numpy().astype(np.int64)
+        kv_format = "e4m3fn"
     else:
         k = key.double().numpy()
         v = value.double().numpy()
     np64 = lambda name: inp[name].double().numpy() if inp.get(name) is not None else None
     aq = dict(ks=np64("key_scale"), vs=np64("value_scale"), ko=np64("key_offset"),
               vo=np64("value_offset"), kmode=inp.get("key_mode", 0),
-              vmode=inp.get("value_mode", 0))
+              vmode=inp.get("value_mode", 0), kv_format=kv_format)
     return k, v, aq, np64("slopes")
 
 
@@ -82,7 +88,8 @@ def oracle_run(inp, batches=None):
             q, k, v, table, ql, kl, inp["mask_type"], H, Hkv, inp["qk_scale"], slopes=sl,
             key_antiquant_scale=aq["ks"], value_antiquant_scale=aq["vs"],
             key_antiquant_offset=aq["ko"], value_antiquant_offset=aq["vo"],
-            key_antiquant_mode=aq["kmode"], value_antiquant_mode=aq["vmode"])
+            key_antiquant_mode=aq["kmode"], value_antiquant_mode=aq["vmode"],
+            kv_format=aq["kv_format"])
         return out, lse, np.arange(q.shape[0])
     q0 = np.concatenate([[0], np.cumsum(ql)])
     bs = k.shape[1]
@@ -90,6 +97,9 @@ def oracle_run(inp, batches=None):
     for b in batches:
         kb = oracle.gather_sequence(k, table[b], kl[b], bs)
         vb = oracle.gather_sequence(v, table[b], kl[b], bs)
+        if aq["kv_format"] == "e4m3fn":
+            kb = oracle.decode_e4m3fn(kb)
+            vb = oracle.decode_e4m3fn(vb)
         kb = _dequant(kb, b, aq["ks"], aq["ko"], aq["kmode"])
         vb = _dequant(vb, b, aq["vs"], aq["vo"], aq["vmode"])
         r = np.arange(q0[b], q0[b + 1])

@@ -65,8 +65,9 @@ class Case:
         self.slopes = desc([H], pa.PA_F32) if mask == pa.PA_MASK_ALIBI else None
         self.mask_type = mask
         self.H, self.Hkv, self.scale = H, Hkv, 1.0 / math.sqrt(D)
-        self.kscale = desc([Hkv, D], pa.PA_F32) if kv_dtype == pa.PA_I8 else None
-        self.vscale = desc([Hkv, D], pa.PA_F32) if kv_dtype == pa.PA_I8 else None
+        one_byte = kv_dtype in (pa.PA_I8, pa.PA_F8E4M3)
+        self.kscale = desc([Hkv, D], pa.PA_F32) if one_byte else None
+        self.vscale = desc([Hkv, D], pa.PA_F32) if one_byte else None
         self.out = desc([T, H, D], dtype)
         self.lse = desc([T, H], pa.PA_F32) if lse else None
         self.koff = self.voff = None
@@ -131,7 +132,7 @@ def _named_case(name):
     else:
         kv = [w.kv_seq_len] * w.batch
     ql = [1] * w.batch if w.seq_len == "decode" else [w.seq_len] * w.batch
-    dt = {"f16": pa.PA_F16, "bf16": pa.PA_BF16, "i8": pa.PA_I8}
+    dt = {"f16": pa.PA_F16, "bf16": pa.PA_BF16, "i8": pa.PA_I8, "f8": pa.PA_F8E4M3}
     c = Case(q_lens=ql, kv_lens=kv, H=w.head_num, Hkv=w.kv_head_num, D=w.head_size,
              bs=w.block_size, dtype=dt[w.dtype], kv_dtype=dt[w.kv_dtype], mask=w.mask_type,
              width=w.table_width)
@@ -416,6 +417,29 @@ def test_antiquant_checks():
     c.extended = True
     c.koff = c.voff = desc([2, 128], pa.PA_F32)
     _expect(c, pa.PA_ERR_PARAM_INVALID, "offsets")
+
+
+def test_fp8_cache_plans_and_checks():
+    """FLOAT8_E4M3FN K/V: per-channel scales required, no offsets, no per-token mode,
+    blockSize a multiple of 32."""
+    c = base(kv_dtype=pa.PA_F8E4M3, bs=32)
+    c.kscale = desc([2, 128], pa.PA_F32)
+    c.vscale = desc([2, 128], pa.PA_F32)
+    info = c.plan()
+    assert info["mode"] == "decode"
+    _check_decode_plan(info, [1, 1], [100, 37], 2, 4)
+    c = base(kv_dtype=pa.PA_F8E4M3, bs=32)
+    c.kscale = c.vscale = None
+    _expect(c, pa.PA_ERR_NULLPTR, "Scale")
+    c = base(kv_dtype=pa.PA_F8E4M3, bs=16)
+    c.kscale = desc([2, 128], pa.PA_F32)
+    c.vscale = desc([2, 128], pa.PA_F32)
+    _expect(c, pa.PA_ERR_PARAM_INVALID, "multiple of 32")
+    for kmode, vmode, offsets in ((1, 1, False), (0, 1, False), (0, 0, True)):
+        c = _i8_case(kmode, vmode, offsets)
+        c.key = desc(list(c.key.shape[:c.key.ndim]), pa.PA_F8E4M3)
+        c.value = desc(list(c.value.shape[:c.value.ndim]), pa.PA_F8E4M3)
+        _expect(c, pa.PA_ERR_PARAM_INVALID, "f8e4m3")
 
 
 def test_kv_head_num_zero_means_head_num():

@@ -41,6 +41,7 @@ SAMPLES = {  # sequences whose outputs the oracle checks one by one at full size
     "prefill_alibi_f16": [0, 5],
     "decode_int8_long": [0, 13, 31],
     "decode_int8_pertoken_long": [2, 19, 30],
+    "decode_fp8_long": [1, 16, 31],
 }
 
 
@@ -56,7 +57,7 @@ def test_named_workload_parity(name):
 
 
 @pytest.mark.parametrize("name", ["decode_bf16_batched", "decode_int8_long",
-                                  "decode_int8_pertoken_long"])
+                                  "decode_int8_pertoken_long", "decode_fp8_long"])
 def test_high_contrast_decode(name):
     """Queries x4 sharpen the softmax so the 2e-2 bf16 gate bites harder."""
     w = wl.WORKLOADS[name]
@@ -198,6 +199,38 @@ def test_prefill_antiquant_modes(aq, mask):
     out, lse = gpu_run(inp)
     ro, rl, rows = oracle_run(inp)
     compare(out, lse, ro, rl, rows, inp["query"].dtype, f"prefill antiquant {aq} {mask}")
+
+
+FP8_CASES = [
+    # (kind, dtype, D, H, Hkv, bs, q_lens, kv_lens, mask, env)
+    ("decode", "bf16", 128, 8, 2, 32, [1, 1, 1], [300, 45, 1], pa.PA_MASK_NONE, {}),
+    ("decode", "f16", 64, 8, 2, 64, [1, 1, 1], [97, 160, 33], pa.PA_MASK_ALIBI, {}),
+    ("decode", "bf16", 128, 8, 2, 32, [1, 1, 1], [1500, 257, 31], pa.PA_MASK_NONE,
+     {"PA_DECODE_CHUNK_TILES": "8"}),
+    ("decode", "bf16", 128, 32, 8, 64, [1, 1, 1], [700, 64, 2049], pa.PA_MASK_NONE,
+     {"PA_DECODE_WAVE_HEADS": "1"}),
+    ("prefill", "f16", 128, 8, 2, 32, [70, 1, 130], [200, 33, 130], pa.PA_MASK_CAUSAL, {}),
+    ("prefill", "bf16", 128, 8, 8, 32, [64, 100], [600, 100], pa.PA_MASK_ALIBI, {}),
+    ("prefill", "f16", 64, 4, 2, 64, [33, 90], [33, 200], pa.PA_MASK_NONE, {}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP8_CASES)))
+def test_fp8_cache(case, monkeypatch):
+    """FLOAT8_E4M3FN K/V with per-channel scales (unused slots hold NaN codes)."""
+    kind, dt, D, H, Hkv, bs, ql, kl, mask, env = FP8_CASES[case]
+    _say(f"[fp8] case {case}: {FP8_CASES[case]}")
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    inp = wl.make_random_case(600 + case, batch=len(kl), head_num=H, kv_head_num=Hkv,
+                              head_size=D, block_size=bs, q_lens=ql, kv_lens=kl, dtype=dt,
+                              kv_dtype="f8", mask_type=mask)
+    out, lse, op, ws = gpu_run(inp, keep_op=True)
+    info = pa.pa_op_describe(op)
+    op.destroy()
+    assert info["mode"] == kind
+    ro, rl, rows = oracle_run(inp)
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"fp8 case {case}")
 
 
 def test_decode_skips_sequences_without_query():
