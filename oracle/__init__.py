@@ -18,6 +18,8 @@ Sources (the pages this follows):
     key/value codes, and the
     softmax-LSE decomposition used by
     ring attention).
+  * The same pages' cache layout and length conventions for the KV-cache
+    append (append_kv_rows), whose API the pages do not print.
   * PrefixEncoder (Ascend Transformer Boost SelfAttention, calcType
     PREFIX_ENCODER), "Definition" and "Members" table (argument list,
     qkScale, maskType 3 = ALiBi compressed, 9 = causal, slopes per head,
@@ -42,6 +44,7 @@ from .attention import (
     attention_contiguous,
     paged_attention,
     merge_partials,
+    append_kv_rows,
 )
 
 __all__ = [

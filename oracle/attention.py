@@ -240,6 +240,31 @@ def _dequantize(x_b, b, scale, offset, mode):
     return dequantize_per_token(x_b, scale[b], off_row)
 
 
+def append_kv_rows(pool, new_rows, block_tables, seq_len, kv_seq_len):
+    """The cache after writing the new tokens' rows (KV-cache append).
+
+    aclnnFusedInferAttentionScoreV3, Constraints, paged attention scenario: token t
+    of sequence b lives in block table_row[t // blockSize], slot t % blockSize.
+    PrefixEncoder, Members: kvSeqLen counts the cached prefix plus the seqLen new
+    tokens, which are the sequence's last positions; the new tokens' rows are packed
+    sequence after sequence like the query.  Reading (no API on the pages): new token
+    i of sequence b goes to position kvSeqLen[b] - seqLen[b] + i.
+    pool: [numBlocks, blockSize, kvHeadNum, headSize]; new_rows: [nTokens, kvHeadNum,
+    headSize], same dtype.  Returns a new array; the input pool is not modified.
+    """
+    out = np.array(pool, copy=True)
+    new_rows = np.asarray(new_rows)
+    block_size = out.shape[1]
+    row = 0
+    for b in range(len(seq_len)):
+        ql, kl = int(seq_len[b]), int(kv_seq_len[b])
+        for i in range(ql):
+            t = kl - ql + i
+            out[int(block_tables[b][t // block_size]), t % block_size] = new_rows[row]
+            row += 1
+    return out
+
+
 def merge_partials(outs, lses):
     """Combine attention results computed over disjoint key ranges.
 

@@ -534,6 +534,53 @@ def test_fp8_equals_float_on_decoded_pool():
     _same(a[1], b[1])
 
 
+def test_append_worked_example():
+    """Two sequences, blockSize 2: sequence 0 has 3 cached + 2 new tokens (positions 3
+    and 4) in blocks [4, 1, 0], sequence 1 has 0 cached + 1 new token in block [2].
+    Position 3 is block 1 slot 1, position 4 is block 0 slot 0, sequence 1's token is
+    block 2 slot 0 (worked by hand); nothing else changes."""
+    pool = np.arange(5 * 2 * 1 * 2, dtype=np.int64).reshape(5, 2, 1, 2) * 10
+    new = np.array([[[-1, -2]], [[-3, -4]], [[-5, -6]]])
+    out = oracle.append_kv_rows(pool, new, [[4, 1, 0], [2, -1, -1]], [2, 1], [5, 1])
+    want = pool.copy()
+    want[1, 1, 0] = [-1, -2]
+    want[0, 0, 0] = [-3, -4]
+    want[2, 0, 0] = [-5, -6]
+    assert np.array_equal(out, want)
+    assert np.array_equal(pool, np.arange(20).reshape(5, 2, 1, 2) * 10)   # input untouched
+
+
+def test_append_then_gather_returns_new_rows_last():
+    """After an append, gathering a sequence gives its old prefix followed by its new
+    rows (gather_sequence is pinned separately), and no other slot changes."""
+    rng = np.random.default_rng([314, 97])
+    bs, Hkv, D = 4, 2, 3
+    q_lens, kv_lens = [3, 0, 5, 1], [7, 4, 5, 9]
+    need = [-(-k // bs) for k in kv_lens]
+    nb = sum(need) + 3
+    perm = rng.permutation(nb)
+    table = np.full((4, max(need)), -1)
+    pos = 0
+    for b in range(4):
+        table[b, :need[b]] = perm[pos:pos + need[b]]
+        pos += need[b]
+    pool = rng.standard_normal((nb, bs, Hkv, D))
+    new = rng.standard_normal((sum(q_lens), Hkv, D))
+    out = oracle.append_kv_rows(pool, new, table, q_lens, kv_lens)
+    row = 0
+    written = np.zeros((nb, bs), dtype=bool)
+    for b in range(4):
+        before = oracle.gather_sequence(pool, table[b], kv_lens[b], bs)
+        after = oracle.gather_sequence(out, table[b], kv_lens[b], bs)
+        keep = kv_lens[b] - q_lens[b]
+        assert np.array_equal(after[:keep], before[:keep])
+        assert np.array_equal(after[keep:], new[row:row + q_lens[b]])
+        for t in range(keep, kv_lens[b]):
+            written[table[b][t // bs], t % bs] = True
+        row += q_lens[b]
+    assert np.array_equal(out[~written], pool[~written])
+
+
 def test_empty_tensor_rules():
     """aclnnFusedInferAttentionScoreV4, Constraints, empty input: empty
     query/out returns empty; empty key/value gives out 0 and lse inf."""
