@@ -221,6 +221,42 @@ pa_status pa_paged_attention_get_workspace_size_ex(
 pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
                              void* stream);
 
+/*
+ * KV-cache append: write the new tokens' key/value rows into their cache blocks, the
+ * step before a prefill / prefix-encoder call.  The pages print no API for it; this one
+ * follows their cache layout and length conventions (aclnnFusedInferAttentionScoreV3,
+ * Constraints, paged attention scenario: token t of sequence b is in block
+ * blockTables[b][t / blockSize], slot t % blockSize; PrefixEncoder, Members: kvSeqLen
+ * counts the cached prefix plus the seqLen new tokens, which are the last positions).
+ * Reading: new token i of sequence b (row q0[b] + i of keyNew/valueNew, packed like the
+ * query) is written at position p = kvSeqLen[b] - seqLen[b] + i, so that an append
+ * followed by pa_paged_attention_get_workspace_size/pa_paged_attention with the same
+ * seqLen / kvSeqLen attends over the updated cache.  A byte copy: a one-byte cache
+ * receives the new tokens' codes as given (quantising them is the caller's step).
+ *
+ * keyNew, valueNew   device, [nTokens, kvHeadNum, headSize], the caches' dtype (f16,
+ *                    bf16, i8 or f8e4m3); last stride 1, other strides free (multiples
+ *                    of 16 bytes); headSize * element size a multiple of 16 bytes.
+ * keyCache, valueCache  device, [numBlocks, blockSize, kvHeadNum, headSize] (or its
+ *                    permuted BnNBsD view, or [numBlocks, blockSize, kvHeadNum*headSize]);
+ *                    written at the new tokens' slots only.
+ * blockTables        device, [batch, maxBlockNum] int32, maxBlockNum * blockSize >=
+ *                    max kvSeqLen.  Block ids are not validated (as for the attention
+ *                    call); the slots written must not be shared by two sequences.
+ * seqLen, kvSeqLen   HOST, [batch] int32, 0 <= seqLen[b] <= kvSeqLen[b],
+ *                    sum(seqLen) = nTokens.
+ * op                 out: handle (pa_op_destroy releases it); nTokens == 0 gives a no-op.
+ * Phase 1 makes no HIP call.  pa_kv_cache_append enqueues the copy on `stream` (NULL =
+ * the null stream); it may be run again, e.g. after the new rows were refilled in place.
+ * pa_paged_attention rejects an append op and pa_kv_cache_append an attention op
+ * (PA_ERR_PARAM_INVALID).  pa_op_set_timing_events applies to the copy kernel.
+ */
+pa_status pa_kv_cache_append_plan(const pa_tensor* keyNew, const pa_tensor* valueNew,
+                                  const pa_tensor* keyCache, const pa_tensor* valueCache,
+                                  const pa_tensor* blockTables, const pa_tensor* seqLen,
+                                  const pa_tensor* kvSeqLen, pa_op** op);
+pa_status pa_kv_cache_append(pa_op* op, void* stream);
+
 /* Release an operator handle (NULL is ignored).  Work already enqueued is unaffected: the
  * call blocks until the kernels of the op's last run have finished (they read the op's
  * work lists from its host buffer). */
@@ -235,11 +271,12 @@ pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop);
 
 /* Write a JSON description of the operator's plan into buf (NUL-terminated, cut at
  * cap - 1 bytes; buf may be NULL when cap is 0) and return the full length without the
- * NUL.  Keys: "mode" ("noop", "fill", "decode", "prefill"), "workspace_bytes",
+ * NUL.  Keys: "mode" ("noop", "fill", "decode", "prefill", "append"), "workspace_bytes",
  * "chunk_tiles", "partial_slots", and the work lists "decode_items"
  * [b, kvh, hg, t0, t1, slot, qrow, kvlen], "combine_items" [kvh, hg, slot0, nsplit, qrow],
  * "prefill_items" [b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads] (heads query heads from
- * h, 128/heads query rows from qbeg).  Host only, no HIP call.
+ * h, 128/heads query rows from qbeg), "append_items" [b, row0, pos0, count], "antiquant"
+ * [key mode, value mode, offsets given].  Host only, no HIP call.
  * For inspection and tests: not a stable interface.  op == NULL returns 0. */
 uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap);
 

@@ -31,7 +31,10 @@ from ._lib import (  # noqa: F401
     PaTensor,
     alloc_workspace,
     describe,
+    kv_cache_append,
     load,
+    pa_kv_cache_append,
+    pa_kv_cache_append_plan,
     pa_last_error,
     pa_op_describe,
     pa_op_destroy,

@@ -39,6 +39,8 @@ EXPORTED = (
     "pa_paged_attention_get_workspace_size",
     "pa_paged_attention_get_workspace_size_ex",
     "pa_paged_attention",
+    "pa_kv_cache_append_plan",
+    "pa_kv_cache_append",
     "pa_op_destroy",
     "pa_op_describe",
     "pa_op_set_timing_events",
@@ -96,6 +98,10 @@ def load():
     lib.pa_paged_attention.restype = ctypes.c_int
     lib.pa_paged_attention.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                        ctypes.c_void_p]
+    lib.pa_kv_cache_append_plan.restype = ctypes.c_int
+    lib.pa_kv_cache_append_plan.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pa_kv_cache_append.restype = ctypes.c_int
+    lib.pa_kv_cache_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.pa_op_destroy.restype = None
     lib.pa_op_destroy.argtypes = [ctypes.c_void_p]
     lib.pa_op_set_timing_events.restype = ctypes.c_int
@@ -238,6 +244,42 @@ def pa_paged_attention(workspace, workspace_size, op, stream=None):
     raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
     ptr = workspace.data_ptr() if workspace is not None and workspace.numel() > 0 else None
     _check(lib.pa_paged_attention(ptr, int(workspace_size), handle, raw))
+
+
+def pa_kv_cache_append_plan(key_new, value_new, key_cache, value_cache, block_tables, seq_len,
+                            kv_seq_len):
+    """Plan a KV-cache append (include/pagedattn.h).  Returns an Op."""
+    lib = load()
+    descs = [describe(key_new, device="cuda"), describe(value_new, device="cuda"),
+             describe(key_cache, device="cuda"), describe(value_cache, device="cuda"),
+             describe(block_tables, device="cuda"), describe(seq_len, device="cpu"),
+             describe(kv_seq_len, device="cpu")]
+    handle = ctypes.c_void_p(None)
+    _check(lib.pa_kv_cache_append_plan(*[_ref(d) for d in descs], ctypes.byref(handle)))
+    keep = (key_new, value_new, key_cache, value_cache, block_tables, seq_len, kv_seq_len)
+    return Op(handle.value, 0, keep)
+
+
+def pa_kv_cache_append(op, stream=None):
+    """Enqueue a planned KV-cache append on ``stream`` (None = torch's current stream)."""
+    lib = load()
+    handle = op.handle if isinstance(op, Op) else op
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+    _check(lib.pa_kv_cache_append(handle, raw))
+
+
+def kv_cache_append(key_new, value_new, key_cache, value_cache, block_tables, seq_len,
+                    kv_seq_len, stream=None):
+    """One-shot helper: plan, run, wait, free the plan."""
+    op = pa_kv_cache_append_plan(key_new, value_new, key_cache, value_cache, block_tables,
+                                 seq_len, kv_seq_len)
+    try:
+        pa_kv_cache_append(op, stream)
+    finally:
+        torch.cuda.synchronize(key_cache.device)
+        op.destroy()
 
 
 def pa_op_destroy(op):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 
-HIP_SOURCES = ["api.hip", "decode.hip", "prefill.hip", "fill.hip"]
+HIP_SOURCES = ["api.hip", "decode.hip", "prefill.hip", "fill.hip", "append.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

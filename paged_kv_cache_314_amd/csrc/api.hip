@@ -63,6 +63,9 @@ pa_status ensure_staging(pa_op* op) {
     } else if (p.mode == pa::Mode::kPrefill) {
         std::memcpy(base + p.off_items, p.prefill_items.data(),
                     p.prefill_items.size() * sizeof(pa::PrefillItem));
+    } else if (p.mode == pa::Mode::kAppend) {
+        std::memcpy(base + p.off_items, p.append_items.data(),
+                    p.append_items.size() * sizeof(pa::AppendItem));
     }
     return PA_OK;
 }
@@ -130,6 +133,8 @@ pa_status pa_paged_attention_get_workspace_size_ex(
 pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op, void* stream) {
     if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
     const pa::Plan& p = op->plan;
+    if (p.mode == pa::Mode::kAppend)
+        return fail(PA_ERR_PARAM_INVALID, "op is a KV-cache append plan: run it with pa_kv_cache_append");
     if (p.mode == pa::Mode::kNoop) return PA_OK;
     if (workspaceSize < p.workspace_bytes)
         return fail(PA_ERR_WORKSPACE_TOO_SMALL,
@@ -261,6 +266,71 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
     return e == hipSuccess ? PA_OK : hip_fail(e, "hipEventRecord(done)");
 }
 
+pa_status pa_kv_cache_append_plan(const pa_tensor* keyNew, const pa_tensor* valueNew,
+                                  const pa_tensor* keyCache, const pa_tensor* valueCache,
+                                  const pa_tensor* blockTables, const pa_tensor* seqLen,
+                                  const pa_tensor* kvSeqLen, pa_op** op) {
+    if (op == nullptr) return fail(PA_ERR_NULLPTR, "op must not be NULL");
+    *op = nullptr;
+    pa_op* h = new (std::nothrow) pa_op();
+    if (h == nullptr) return fail(PA_ERR_HOST_ALLOC, "cannot allocate the operator");
+    std::string err;
+    const pa_status st =
+        pa::plan_append(keyNew, valueNew, keyCache, valueCache, blockTables, seqLen, kvSeqLen, h->plan, err);
+    if (st != PA_OK) {
+        delete h;
+        return fail(st, err);
+    }
+    *op = h;
+    g_last_error.clear();
+    return PA_OK;
+}
+
+pa_status pa_kv_cache_append(pa_op* op, void* stream) {
+    if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
+    const pa::Plan& p = op->plan;
+    if (p.mode == pa::Mode::kNoop) return PA_OK;
+    if (p.mode != pa::Mode::kAppend)
+        return fail(PA_ERR_PARAM_INVALID, "op is not a KV-cache append plan");
+    pa_status st = ensure_staging(op);
+    if (st != PA_OK) return st;
+    hipError_t e;
+    if (op->done == nullptr) {
+        e = hipEventCreateWithFlags(&op->done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            op->done = nullptr;
+            return hip_fail(e, "hipEventCreateWithFlags");
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pa::AppendArgs a{};
+    a.items = reinterpret_cast<const pa::AppendItem*>(op->staging_dev + p.off_items);
+    a.knew = p.knew;
+    a.vnew = p.vnew;
+    a.kcache = const_cast<void*>(p.k);
+    a.vcache = const_cast<void*>(p.v);
+    a.table = p.table;
+    a.knew_tok_stride = p.knew_tok_stride;
+    a.knew_head_stride = p.knew_head_stride;
+    a.vnew_tok_stride = p.vnew_tok_stride;
+    a.vnew_head_stride = p.vnew_head_stride;
+    a.k_blk_stride = p.k_blk_stride;
+    a.k_slot_stride = p.k_slot_stride;
+    a.k_head_stride = p.k_head_stride;
+    a.v_blk_stride = p.v_blk_stride;
+    a.v_slot_stride = p.v_slot_stride;
+    a.v_head_stride = p.v_head_stride;
+    a.table_stride = p.table_stride;
+    a.kv_heads = p.kv_head_num;
+    a.row_chunks = p.head_size * p.elem_bytes / 16;
+    a.block_size = p.block_size;
+    a.elem_bytes = p.elem_bytes;
+    e = pa::launch_append(a, static_cast<int>(p.append_items.size()), s, op->t_start, op->t_stop);
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    e = hipEventRecord(op->done, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e, "hipEventRecord(done)");
+}
+
 void pa_op_destroy(pa_op* op) {
     if (op == nullptr) return;
     // kernels enqueued with this op may still read its work lists: wait for the last run
@@ -282,7 +352,7 @@ pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop) {
 uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
     if (op == nullptr) return 0;
     const pa::Plan& p = op->plan;
-    static const char* modes[] = {"noop", "fill", "decode", "prefill"};
+    static const char* modes[] = {"noop", "fill", "decode", "prefill", "append"};
     std::string s = "{\"mode\": \"";
     s += modes[static_cast<int>(p.mode)];
     s += "\", \"workspace_bytes\": " + std::to_string(p.workspace_bytes);
@@ -317,6 +387,13 @@ uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
              ", " + std::to_string(q.qlen) + ", " + std::to_string(q.kvlen) + ", " +
              std::to_string(q.qrow0) + ", " + std::to_string(q.ktiles) + ", " +
              std::to_string(q.heads) + "]";
+    }
+    s += "], \"append_items\": [";
+    for (size_t i = 0; i < p.append_items.size(); ++i) {
+        const pa::AppendItem& q = p.append_items[i];
+        if (i) s += ", ";
+        s += "[" + std::to_string(q.b) + ", " + std::to_string(q.row0) + ", " + std::to_string(q.pos0) +
+             ", " + std::to_string(q.count) + "]";
     }
     s += "]}";
     if (buf != nullptr && cap > 0) {

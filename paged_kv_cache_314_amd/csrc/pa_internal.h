@@ -22,7 +22,21 @@ constexpr int kComputeUnits = 256;
 constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
 
-enum class Mode : int32_t { kNoop = 0, kFill = 1, kDecode = 2, kPrefill = 3 };
+enum class Mode : int32_t { kNoop = 0, kFill = 1, kDecode = 2, kPrefill = 3, kAppend = 4 };
+
+// KV-cache append: new tokens per workgroup
+constexpr int kAppendRows = 16;
+
+// One append workgroup: `count` consecutive new tokens of sequence b, rows row0 .. of the
+// new-token tensors, positions pos0 .. in the sequence.
+struct AppendItem {
+    int32_t b;
+    int32_t row0;
+    int32_t pos0;
+    int32_t count;
+    int32_t pad[4];
+};
+static_assert(sizeof(AppendItem) == 32, "AppendItem layout");
 
 // One decode workgroup: a range of 32-token tiles of one sequence and
 //   heads == 1: one (kv head, head group), the four waves splitting the tile range, or
@@ -105,6 +119,14 @@ struct Plan {
     std::vector<DecodeItem> decode_items;
     std::vector<CombineItem> combine_items;
     std::vector<PrefillItem> prefill_items;
+    std::vector<AppendItem> append_items;
+
+    // KV-cache append: new-token tensors [nTokens, kvHeadNum, headSize] (strides in
+    // elements) and the caches written (k / v above are the caches, kvtype their dtype)
+    const void* knew = nullptr;
+    const void* vnew = nullptr;
+    int64_t knew_tok_stride = 0, knew_head_stride = 0, vnew_tok_stride = 0, vnew_head_stride = 0;
+    int32_t elem_bytes = 0;
     int32_t decode_chunk_tiles = 0;
     int32_t decode_wave_heads = 0;   // 1: items of 4 kv heads, one per wave
     int32_t partial_slots = 0;
@@ -114,6 +136,12 @@ struct Plan {
     uint64_t off_items = 0, off_combine = 0, items_bytes = 0;
     uint64_t off_part_o = 0, off_part_ml = 0, workspace_bytes = 0;
 };
+
+// KV-cache append planning (validation + work list).  On failure returns a status and
+// sets `err`.
+pa_status plan_append(const pa_tensor* keyNew, const pa_tensor* valueNew, const pa_tensor* keyCache,
+                      const pa_tensor* valueCache, const pa_tensor* blockTables,
+                      const pa_tensor* seqLen, const pa_tensor* kvSeqLen, Plan& p, std::string& err);
 
 // Validation + planning.  On failure returns a status and sets `err`.
 pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,

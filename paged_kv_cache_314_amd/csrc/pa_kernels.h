@@ -78,6 +78,22 @@ struct PrefillArgs {
     AntiquantArgs aq;
 };
 
+struct AppendArgs {
+    const AppendItem* items;
+    const void* knew;
+    const void* vnew;
+    void* kcache;
+    void* vcache;
+    const int32_t* table;
+    int64_t knew_tok_stride, knew_head_stride, vnew_tok_stride, vnew_head_stride;
+    int64_t k_blk_stride, k_slot_stride, k_head_stride;
+    int64_t v_blk_stride, v_slot_stride, v_head_stride, table_stride;
+    int32_t kv_heads;
+    int32_t row_chunks;     // headSize * element bytes / 16
+    int32_t block_size;
+    int32_t elem_bytes;
+};
+
 struct FillArgs {
     void* out;
     float* lse;
@@ -96,6 +112,9 @@ hipError_t launch_combine(const CombineArgs& a, int n_items, int head_size, bool
 hipError_t launch_prefill(const PrefillArgs& a, int n_items, int head_size, bool bf16, bool i8,
                           bool f8, hipStream_t stream, hipEvent_t t0 = nullptr,
                           hipEvent_t t1 = nullptr);
+
+hipError_t launch_append(const AppendArgs& a, int n_items, hipStream_t stream,
+                         hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // 256-thread launch of `kernel` over n workgroups, with timing events if given
 template <typename K, typename A>

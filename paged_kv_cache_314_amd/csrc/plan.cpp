@@ -668,6 +668,145 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
 
 }  // namespace
 
+namespace {
+
+// KV-cache append: the new tokens of sequence b (seqLen[b] rows of keyNew / valueNew,
+// packed in sequence order like the query) are its last positions,
+// p = kvSeqLen[b] - seqLen[b] + i, written to block blockTables[b][p / blockSize],
+// slot p % blockSize (aclnnFusedInferAttentionScoreV3, Constraints, paged attention
+// scenario: the cache layout; PrefixEncoder, Members: kvSeqLen counts the cached prefix
+// plus the new tokens).
+void plan_append_impl(const pa_tensor* keyNew, const pa_tensor* valueNew, const pa_tensor* keyCache,
+                      const pa_tensor* valueCache, const pa_tensor* blockTables,
+                      const pa_tensor* seqLen, const pa_tensor* kvSeqLen, Plan& p) {
+    REQUIRE(keyNew && valueNew && keyCache && valueCache && blockTables && seqLen && kvSeqLen,
+            PA_ERR_NULLPTR, "keyNew, valueNew, keyCache, valueCache, blockTables, seqLen and "
+                            "kvSeqLen are required");
+    for (auto [t, name] : {std::pair{keyNew, "keyNew"}, std::pair{valueNew, "valueNew"},
+                           std::pair{keyCache, "keyCache"}, std::pair{valueCache, "valueCache"}})
+        check_desc(t, name);
+    REQUIRE(keyNew->ndim == 3 && valueNew->ndim == 3, PA_ERR_PARAM_INVALID,
+            "keyNew / valueNew must be [nTokens, kvHeadNum, headSize]");
+    for (int i = 0; i < 3; ++i)
+        REQUIRE(keyNew->shape[i] == valueNew->shape[i], PA_ERR_PARAM_INVALID,
+                "keyNew and valueNew shapes differ");
+    const int64_t T = keyNew->shape[0], hkv = keyNew->shape[1], d = keyNew->shape[2];
+    p.mode = Mode::kAppend;
+    if (T == 0) {
+        p.mode = Mode::kNoop;
+        return;
+    }
+    REQUIRE(hkv > 0 && d > 0, PA_ERR_PARAM_INVALID, "kvHeadNum and headSize must be > 0");
+    REQUIRE(keyNew->dtype == keyCache->dtype && valueNew->dtype == valueCache->dtype &&
+                keyCache->dtype == valueCache->dtype,
+            PA_ERR_PARAM_INVALID, "new tokens and caches must share one dtype");
+    REQUIRE(keyCache->dtype == PA_F16 || keyCache->dtype == PA_BF16 || keyCache->dtype == PA_I8 ||
+                keyCache->dtype == PA_F8E4M3,
+            PA_ERR_PARAM_INVALID, "cache dtype must be f16, bf16, i8 or f8e4m3");
+    const int eb = elem_bytes(keyCache->dtype);
+    REQUIRE((d * eb) % 16 == 0, PA_ERR_PARAM_INVALID, "headSize * element size must be a multiple of 16 bytes");
+    REQUIRE(keyNew->stride[2] == 1 && valueNew->stride[2] == 1, PA_ERR_PARAM_INVALID,
+            "keyNew / valueNew last dimension must be contiguous");
+    const PoolView kc = pool_view(keyCache, "keyCache", hkv);
+    const PoolView vc = pool_view(valueCache, "valueCache", hkv);
+    REQUIRE(kc.d == d && vc.d == d && kc.slots == vc.slots && kc.blocks == vc.blocks, PA_ERR_PARAM_INVALID,
+            "caches must be [numBlocks, blockSize, kvHeadNum, headSize] matching the new tokens");
+    auto mult16 = [&](int64_t stride) { return (stride * eb) % 16 == 0; };
+    REQUIRE(mult16(keyNew->stride[0]) && mult16(keyNew->stride[1]) && mult16(valueNew->stride[0]) &&
+                mult16(valueNew->stride[1]) && mult16(kc.blk_stride) && mult16(kc.slot_stride) &&
+                mult16(kc.head_stride) && mult16(vc.blk_stride) && mult16(vc.slot_stride) &&
+                mult16(vc.head_stride),
+            PA_ERR_PARAM_INVALID, "strides must be multiples of 16 bytes");
+    REQUIRE(aligned16(keyNew->data) && aligned16(valueNew->data) && aligned16(keyCache->data) &&
+                aligned16(valueCache->data),
+            PA_ERR_PARAM_INVALID, "data must be 16-byte aligned");
+    REQUIRE(keyNew->data && valueNew->data && keyCache->data && valueCache->data, PA_ERR_NULLPTR,
+            "a tensor's data is NULL");
+    const int64_t bs = kc.slots;
+    REQUIRE(bs > 0 && bs <= 4096, PA_ERR_PARAM_INVALID, "blockSize must be in [1, 4096]");
+    REQUIRE((bs * std::max(kc.slot_stride, vc.slot_stride) + d) * eb < (int64_t(1) << 31),
+            PA_ERR_UNSUPPORTED, "a cache block must span less than 2 GiB");
+
+    check_desc(seqLen, "seqLen");
+    check_desc(kvSeqLen, "kvSeqLen");
+    REQUIRE(seqLen->dtype == PA_I32 && kvSeqLen->dtype == PA_I32 && seqLen->ndim == 1 &&
+                kvSeqLen->ndim == 1 && seqLen->shape[0] == kvSeqLen->shape[0] && seqLen->shape[0] > 0,
+            PA_ERR_PARAM_INVALID, "seqLen and kvSeqLen must be int32 [batch], batch > 0");
+    REQUIRE(seqLen->data && kvSeqLen->data, PA_ERR_NULLPTR, "seqLen/kvSeqLen data is NULL");
+    const int64_t B = seqLen->shape[0];
+    const int32_t* ql = static_cast<const int32_t*>(seqLen->data);
+    const int32_t* kl = static_cast<const int32_t*>(kvSeqLen->data);
+    check_desc(blockTables, "blockTables");
+    REQUIRE(blockTables->dtype == PA_I32 && blockTables->ndim == 2 && blockTables->shape[0] == B &&
+                (blockTables->stride[1] == 1 || blockTables->shape[1] <= 1),
+            PA_ERR_PARAM_INVALID, "blockTables must be int32 [batch, maxBlockNum], columns contiguous");
+    int64_t row = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t q = ql[b * seqLen->stride[0]], k = kl[b * kvSeqLen->stride[0]];
+        REQUIRE(q >= 0 && k >= q, PA_ERR_PARAM_INVALID,
+                "sequence " << b << ": need 0 <= seqLen (" << q << ") <= kvSeqLen (" << k << ")");
+        REQUIRE(blockTables->shape[1] * bs >= k, PA_ERR_PARAM_INVALID,
+                "blockTables has " << blockTables->shape[1] << " columns, sequence " << b << " needs "
+                                   << (k + bs - 1) / bs);
+        for (int32_t i = 0; i < q; i += kAppendRows) {
+            AppendItem it{};
+            it.b = static_cast<int32_t>(b);
+            it.row0 = static_cast<int32_t>(row + i);
+            it.pos0 = k - q + i;
+            it.count = std::min(kAppendRows, q - i);
+            p.append_items.push_back(it);
+        }
+        row += q;
+    }
+    REQUIRE(row == T, PA_ERR_PARAM_INVALID, "sum(seqLen) = " << row << " but keyNew has " << T << " rows");
+    REQUIRE(blockTables->data != nullptr, PA_ERR_NULLPTR, "blockTables data is NULL");
+
+    p.kvtype = static_cast<pa_dtype>(keyCache->dtype);
+    p.elem_bytes = eb;
+    p.batch = static_cast<int32_t>(B);
+    p.kv_head_num = static_cast<int32_t>(hkv);
+    p.head_size = static_cast<int32_t>(d);
+    p.block_size = static_cast<int32_t>(bs);
+    p.n_tokens = static_cast<int32_t>(T);
+    p.knew = keyNew->data;
+    p.vnew = valueNew->data;
+    p.knew_tok_stride = keyNew->stride[0];
+    p.knew_head_stride = keyNew->stride[1];
+    p.vnew_tok_stride = valueNew->stride[0];
+    p.vnew_head_stride = valueNew->stride[1];
+    p.k = keyCache->data;
+    p.v = valueCache->data;
+    p.k_blk_stride = kc.blk_stride;
+    p.k_slot_stride = kc.slot_stride;
+    p.k_head_stride = kc.head_stride;
+    p.v_blk_stride = vc.blk_stride;
+    p.v_slot_stride = vc.slot_stride;
+    p.v_head_stride = vc.head_stride;
+    p.table = static_cast<const int32_t*>(blockTables->data);
+    p.table_stride = blockTables->stride[0];
+    p.off_items = 0;
+    p.items_bytes = align256(p.append_items.size() * sizeof(AppendItem));
+    p.workspace_bytes = 0;
+}
+
+}  // namespace
+
+pa_status plan_append(const pa_tensor* keyNew, const pa_tensor* valueNew, const pa_tensor* keyCache,
+                      const pa_tensor* valueCache, const pa_tensor* blockTables,
+                      const pa_tensor* seqLen, const pa_tensor* kvSeqLen, Plan& p, std::string& err) {
+    try {
+        plan_append_impl(keyNew, valueNew, keyCache, valueCache, blockTables, seqLen, kvSeqLen, p);
+    } catch (const Fail& f) {
+        err = f.msg;
+        return f.status;
+    } catch (const std::bad_alloc&) {
+        err = "host allocation failed while planning";
+        return PA_ERR_HOST_ALLOC;
+    }
+    err.clear();
+    return PA_OK;
+}
+
 pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
                const pa_tensor* blockTables, const pa_tensor* mask, const pa_tensor* seqLen,
                const pa_tensor* kvSeqLen, const pa_tensor* slopes, int maskType,

@@ -442,6 +442,86 @@ def test_fp8_cache_plans_and_checks():
         _expect(c, pa.PA_ERR_PARAM_INVALID, "f8e4m3")
 
 
+class AppendCase:
+    """Descriptors for pa_kv_cache_append_plan (fake device pointers)."""
+
+    def __init__(self, *, q_lens, kv_lens, Hkv=2, D=128, bs=16, dtype=pa.PA_BF16, width=None):
+        T = int(sum(q_lens))
+        need = sum(-(-k // bs) for k in kv_lens)
+        W = max([-(-k // bs) for k in kv_lens] + [1]) if width is None else width
+        self.knew = desc([T, Hkv, D], dtype)
+        self.vnew = desc([T, Hkv, D], dtype)
+        self.kc = desc([need + 1, bs, Hkv, D], dtype)
+        self.vc = desc([need + 1, bs, Hkv, D], dtype)
+        self.table = desc([len(q_lens), W], pa.PA_I32)
+        self.seq_len, self._ql = host_i32(q_lens)
+        self.kv_seq_len, self._kl = host_i32(kv_lens)
+
+    def call(self):
+        lib = pa.load()
+        op = ctypes.c_void_p(None)
+        r = lambda d: ctypes.byref(d) if d is not None else None
+        st = lib.pa_kv_cache_append_plan(r(self.knew), r(self.vnew), r(self.kc), r(self.vc),
+                                         r(self.table), r(self.seq_len), r(self.kv_seq_len),
+                                         ctypes.byref(op))
+        return st, op.value
+
+
+def test_append_plan_covers_every_new_row_once():
+    q_lens, kv_lens = [40, 0, 1, 17], [100, 5, 1, 17]
+    c = AppendCase(q_lens=q_lens, kv_lens=kv_lens, bs=32)
+    st, op = c.call()
+    assert st == pa.PA_OK, pa.pa_last_error()
+    info = pa.pa_op_describe(op)
+    pa.pa_op_destroy(op)
+    assert info["mode"] == "append"
+    seen = {}
+    for b, row0, pos0, count in info["append_items"]:
+        assert 1 <= count <= 16
+        for i in range(count):
+            assert (row0 + i) not in seen
+            seen[row0 + i] = (b, pos0 + i)
+    row = 0
+    for b, (q, k) in enumerate(zip(q_lens, kv_lens)):
+        for i in range(q):
+            assert seen[row] == (b, k - q + i)
+            row += 1
+    assert len(seen) == sum(q_lens)
+
+
+def test_append_checks_and_op_kinds():
+    def expect(c, status, text):
+        st, op = c.call()
+        assert st == status and op is None, (st, pa.pa_last_error())
+        assert text in pa.pa_last_error()
+    expect(AppendCase(q_lens=[5, 1], kv_lens=[4, 3]), pa.PA_ERR_PARAM_INVALID, "seqLen")
+    c = AppendCase(q_lens=[2, 1], kv_lens=[40, 3])
+    c.vc = desc([20, 16, 2, 128], pa.PA_F16)
+    expect(c, pa.PA_ERR_PARAM_INVALID, "dtype")
+    expect(AppendCase(q_lens=[2, 1], kv_lens=[40, 3], width=2), pa.PA_ERR_PARAM_INVALID, "columns")
+    c = AppendCase(q_lens=[2, 1], kv_lens=[40, 3])
+    c.knew = desc([4, 2, 128], pa.PA_BF16)
+    expect(c, pa.PA_ERR_PARAM_INVALID, "shapes differ")
+    c = AppendCase(q_lens=[2, 1], kv_lens=[40, 3])
+    c.knew = c.vnew = desc([3, 256], pa.PA_BF16)
+    expect(c, pa.PA_ERR_PARAM_INVALID, "nTokens, kvHeadNum, headSize")
+    # an append op cannot run as attention, nor an attention op as an append
+    st, op = AppendCase(q_lens=[2], kv_lens=[9]).call()
+    assert st == pa.PA_OK
+    lib = pa.load()
+    assert lib.pa_paged_attention(None, 0, op, None) == pa.PA_ERR_PARAM_INVALID
+    assert "append" in pa.pa_last_error()
+    pa.pa_op_destroy(op)
+    st, _, aop = base().call()
+    assert st == pa.PA_OK
+    assert lib.pa_kv_cache_append(aop, None) == pa.PA_ERR_PARAM_INVALID
+    pa.pa_op_destroy(aop)
+    # no new tokens: a no-op plan
+    st, op = AppendCase(q_lens=[0, 0], kv_lens=[3, 0]).call()
+    assert st == pa.PA_OK and pa.pa_op_describe(op)["mode"] == "noop"
+    pa.pa_op_destroy(op)
+
+
 def test_kv_head_num_zero_means_head_num():
     c = base(H=4, Hkv=4)
     c.Hkv = 0

@@ -10,6 +10,8 @@ import sys
 
 import numpy as np
 import pytest
+
+import oracle
 import torch
 
 import paged_kv_cache_314_amd as pa
@@ -231,6 +233,72 @@ def test_fp8_cache(case, monkeypatch):
     assert info["mode"] == kind
     ro, rl, rows = oracle_run(inp)
     compare(out, lse, ro, rl, rows, inp["query"].dtype, f"fp8 case {case}")
+
+
+def _append_inputs(seed, kv_dtype, *, q_lens, kv_lens, bs, Hkv=2, D=128, layout="bnbsh"):
+    inp = wl.make_random_case(seed, batch=len(kv_lens), head_num=4 * Hkv, kv_head_num=Hkv,
+                              head_size=D, block_size=bs, q_lens=q_lens, kv_lens=kv_lens,
+                              dtype="bf16" if kv_dtype in ("i8", "f8") else kv_dtype,
+                              kv_dtype=kv_dtype, poison=False)
+    rng = np.random.default_rng([314, 2000 + seed])
+    T = int(sum(q_lens))
+    if kv_dtype == "i8":
+        draw = lambda: torch.from_numpy(rng.integers(-127, 128, size=(T, Hkv, D), dtype=np.int8))
+    elif kv_dtype == "f8":
+        draw = lambda: torch.from_numpy(np.clip(rng.standard_normal((T, Hkv, D)).astype(np.float32)
+                                                * 64, -448, 448)).to(torch.float8_e4m3fn)
+    else:
+        dt = torch.bfloat16 if kv_dtype == "bf16" else torch.float16
+        draw = lambda: torch.from_numpy(rng.standard_normal((T, Hkv, D)).astype(np.float32)).to(dt)
+    inp["key_new"], inp["value_new"] = draw(), draw()
+    if layout == "bnnbsd":
+        for k in ("key", "value"):
+            inp[k] = inp[k].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    return inp
+
+
+@pytest.mark.parametrize("kv_dtype,bs,layout", [("bf16", 16, "bnbsh"), ("f16", 128, "bnnbsd"),
+                                                ("i8", 32, "bnbsh"), ("f8", 64, "bnnbsd"),
+                                                ("bf16", 128, "bnbsh")])
+def test_kv_cache_append_bit_exact(kv_dtype, bs, layout):
+    """The cache after the append equals the oracle's, byte for byte."""
+    _say(f"[append] {kv_dtype} bs {bs} {layout}")
+    q_lens, kv_lens = [40, 0, 1, 300, 17], [100, 5, 1, 300, 17]
+    inp = _append_inputs(700 + bs, kv_dtype, q_lens=q_lens, kv_lens=kv_lens, bs=bs, layout=layout)
+    kc, vc = inp["key"].cuda(), inp["value"].cuda()
+    pa.kv_cache_append(inp["key_new"].cuda(), inp["value_new"].cuda(), kc, vc,
+                       inp["block_tables"].cuda(), inp["seq_len"], inp["kv_seq_len"])
+    # compare bytes: rows of [.., headSize * element size] uint8 in the logical layout
+    raw = lambda t: t.cpu().contiguous().view(torch.uint8).numpy()
+    for cache, pool, new in ((kc, inp["key"], inp["key_new"]), (vc, inp["value"], inp["value_new"])):
+        want = oracle.append_kv_rows(raw(pool), raw(new), inp["block_tables"].numpy(),
+                                     q_lens, kv_lens)
+        got = raw(cache)
+        assert got.shape == want.shape
+        assert np.array_equal(got, want)
+
+
+def test_append_then_prefill_attention():
+    """Append the new tokens, then attend with the same lengths: equals the oracle on the
+    oracle-appended cache (queries are the new tokens, the prefix-encoder step)."""
+    q_lens, kv_lens = [70, 1, 130], [200, 33, 130]
+    inp = _append_inputs(801, "bf16", q_lens=q_lens, kv_lens=kv_lens, bs=32, Hkv=2)
+    inp["mask_type"] = pa.PA_MASK_CAUSAL
+    kc, vc = inp["key"].cuda(), inp["value"].cuda()
+    pa.kv_cache_append(inp["key_new"].cuda(), inp["value_new"].cuda(), kc, vc,
+                       inp["block_tables"].cuda(), inp["seq_len"], inp["kv_seq_len"])
+    table = inp["block_tables"].numpy()
+    ref = dict(inp)
+    ref["key"] = torch.from_numpy(oracle.append_kv_rows(inp["key"].float().numpy(),
+                                                        inp["key_new"].float().numpy(),
+                                                        table, q_lens, kv_lens))
+    ref["value"] = torch.from_numpy(oracle.append_kv_rows(inp["value"].float().numpy(),
+                                                          inp["value_new"].float().numpy(),
+                                                          table, q_lens, kv_lens))
+    run = dict(inp, key=kc, value=vc)
+    out, lse = gpu_run(run)
+    ro, rl, rows = oracle_run(ref)
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, "append then prefill")
 
 
 def test_decode_skips_sequences_without_query():
