@@ -177,6 +177,86 @@ def cpu_baseline(inp, nbytes, flops, decode, budget_s):
                       f"step's work, {dt:.1f} s, fp64 NumPy, BLAS threads {threads}"}
 
 
+# ------------------------------------------------------------ KV-cache append
+
+def bench_append(args, w, dev):
+    """Time the KV-cache append of workload ``w`` (HBM-bound copy: the new rows are read
+    and written once; bytes = 2 x (K + V) x nTokens x kvHeadNum x headSize x element)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_314_amd as pa
+    from paged_kv_cache_314_amd import workloads as wl
+
+    inp = wl.make_inputs(w, poison=False)
+    kn, vn = inp["key_new"].to(dev), inp["value_new"].to(dev)
+    kc, vc = inp["key"].to(dev), inp["value"].to(dev)
+    if args.kv_layout == "bnnbsd":
+        kc = kc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        vc = vc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    table = inp["block_tables"].to(dev)
+    nbytes = 2 * 2 * kn.numel() * kn.element_size()
+    t_plan = time.perf_counter()
+    op = pa.pa_kv_cache_append_plan(kn, vn, kc, vc, table, inp["seq_len"], inp["kv_seq_len"])
+    plan_us = (time.perf_counter() - t_plan) * 1e6
+    info = pa.pa_op_describe(op)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pa.pa_kv_cache_append(op, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pa.pa_kv_cache_append(op, stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + stops:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for s_ev, e_ev in zip(starts, stops):
+        pa.pa_op_set_timing_events(op, s_ev, e_ev)
+        pa.pa_kv_cache_append(op, stream)
+    pa.pa_op_set_timing_events(op, None, None)
+    torch.cuda.synchronize()
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, stops)) / args.steps
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles(args.workload, "append"),
+            "kernel": "append_kernel", "kernel_us": kernel_ms * 1e3, "algorithmic_bytes": nbytes,
+            "algorithmic_flops": 0}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        raw = lambda t: t.contiguous().view(torch.uint8).numpy()
+        table_np = inp["block_tables"].numpy()
+        ql, kl = inp["seq_len"].tolist(), inp["kv_seq_len"].tolist()
+        tc = time.perf_counter()
+        oracle.append_kv_rows(raw(inp["key"]), raw(inp["key_new"]), table_np, ql, kl)
+        oracle.append_kv_rows(raw(inp["value"]), raw(inp["value_new"]), table_np, ql, kl)
+        dt = time.perf_counter() - tc
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        cpu = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole append (K and V, {len(ql)} sequences), {dt:.2f} s, "
+                         f"NumPy row copies (one thread; BLAS threads {threads} unused)"}
+    result = {
+        "metric": "decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), paged attention",
+        "value": nbytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "mode": "append", "batch": w.batch,
+                   "kv_head_num": w.kv_head_num, "head_size": w.head_size,
+                   "block_size": w.block_size, "kv_dtype": w.kv_dtype, "new_tokens": int(kn.shape[0]),
+                   "kv_layout": args.kv_layout, "parallelism": "single GPU",
+                   "work_items": len(info["append_items"])},
+        "plan_us": plan_us, "roofline": roof, "cpu_baseline": cpu,
+    }
+    op.destroy()
+    print(json.dumps(result), flush=True)
+
+
 # -------------------------------------------------------------------- main
 
 def main():
@@ -205,6 +285,8 @@ def main():
         return
 
     w = wl.WORKLOADS[args.workload]
+    if w.op == "append":
+        return bench_append(args, w, dev)
     decode = w.seq_len == "decode"
     kind = "decode" if decode else "prefill"
     inp = wl.make_inputs(w, poison=False)
@@ -262,7 +344,7 @@ def main():
         achieved = nbytes / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
-        dtype = "f16" if w.kv_dtype == "i8" else w.dtype
+        dtype = "f16" if w.kv_dtype in ("i8", "f8") else w.dtype   # one-byte caches run in f16
     else:
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"

@@ -3,7 +3,7 @@
     python -m paged_kv_cache_314_amd.counter_summary KIND WORKLOAD \\
         FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR COPY_MIB "<fetch cmd>" "<write cmd>"
 
-KIND is the kernel (decode_kernel | prefill_kernel). Each *_DIR is a `rocprofv3 --pmc ...
+KIND is the kernel (decode_kernel | prefill_kernel | append_kernel). Each *_DIR is a `rocprofv3 --pmc ...
 -d DIR -o run --output-format csv` output holding run_counter_collection.csv. The copy
 runs profile a plain device-to-device copy of COPY_MIB MiB (`bench.py --copy-probe`),
 which fixes the factor between each counter's KiB and the bytes actually moved.
@@ -23,6 +23,7 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_314_amd", "csrc")
 KERNEL_SOURCES = {
     "decode_kernel": ["decode.hip", "pa_device.h"],
     "prefill_kernel": ["prefill.hip", "pa_device.h"],
+    "append_kernel": ["append.hip", "pa_device.h"],
 }
 COPY_KERNEL = "copyBuffer"
 

@@ -64,6 +64,7 @@ class Workload:
     table_width: object = None  # None = max blocks needed
     table_padding: str = "minus_one"   # "minus_one" | "ids"
     antiquant: object = None    # int8 only: (key mode, value mode, offsets?); None = (0, 0, False)
+    op: str = "attention"       # "attention" | "append" (KV-cache append of the seqLen new tokens)
     extra: dict = field(default_factory=dict)
 
 
@@ -90,6 +91,11 @@ WORKLOADS = {
     "decode_fp8_long": Workload(
         "decode_fp8_long", 7, "bf16", "f8", 32, 64, 8, 128, 128, "decode", 16384,
         MASK_NONE, 1.0 / math.sqrt(128.0), pool=("plus", 0.10)),
+    # KV-cache append of the prefix + ALiBi prefill's new tokens (8 x 512 into 2560-token
+    # sequences, 32 kv heads, f16): the step before that prefill
+    "append_prefix_f16": Workload(
+        "append_prefix_f16", 8, "f16", "f16", 8, 32, 32, 128, 128, 512, 2560,
+        MASK_NONE, 1.0 / math.sqrt(128.0), op="append"),
     "decode_int8_pertoken_long": Workload(
         "decode_int8_pertoken_long", 6, "bf16", "i8", 32, 64, 8, 128, 128, "decode", 16384,
         MASK_NONE, 1.0 / math.sqrt(128.0), pool=("plus", 0.10), antiquant=(1, 1, True)),
@@ -235,6 +241,11 @@ def make_inputs(w, seed=None, poison=False, kv_lens=None, q_scale=1.0):
             rng, kmode, vmode, offs, Hkv, D, B, kvl)
     seq_len = torch.tensor(q_lens_fixed, dtype=torch.int32)
     kv_seq_len = torch.tensor(kvl, dtype=torch.int32)
+    extra = {}
+    if w.op == "append":
+        # the new tokens' K/V rows [nTokens, kvHeadNum, headSize]
+        extra["key_new"] = _kv_pool(rng, (n_tokens, Hkv, D), w.kv_dtype)
+        extra["value_new"] = _kv_pool(rng, (n_tokens, Hkv, D), w.kv_dtype)
     if poison:
         used = used_slots(tables, kv_seq_len, bs, num_blocks)
         poison_unused(key, used)
@@ -246,7 +257,7 @@ def make_inputs(w, seed=None, poison=False, kv_lens=None, q_scale=1.0):
         key_scale=key_scale, value_scale=value_scale,
         key_offset=key_offset, value_offset=value_offset, key_mode=kmode, value_mode=vmode,
         mask_type=w.mask_type, head_num=H, kv_head_num=Hkv,
-        qk_scale=float(w.qk_scale), want_lse=bool(w.lse),
+        qk_scale=float(w.qk_scale), want_lse=bool(w.lse), **extra,
     )
 
 

@@ -44,6 +44,7 @@ SAMPLES = {  # sequences whose outputs the oracle checks one by one at full size
     "decode_int8_long": [0, 13, 31],
     "decode_int8_pertoken_long": [2, 19, 30],
     "decode_fp8_long": [1, 16, 31],
+    "append_prefix_f16": None,
 }
 
 
@@ -51,6 +52,19 @@ SAMPLES = {  # sequences whose outputs the oracle checks one by one at full size
 def test_named_workload_parity(name):
     w = wl.WORKLOADS[name]
     _say(f"[parity] {name}")
+    if w.op == "append":
+        # the whole cache after the append, byte for byte against the oracle
+        inp = wl.make_inputs(w, poison=True)
+        kc, vc = inp["key"].cuda(), inp["value"].cuda()
+        pa.kv_cache_append(inp["key_new"].cuda(), inp["value_new"].cuda(), kc, vc,
+                           inp["block_tables"].cuda(), inp["seq_len"], inp["kv_seq_len"])
+        raw = lambda t: t.cpu().contiguous().view(torch.uint8).numpy()
+        ql, kl = inp["seq_len"].tolist(), inp["kv_seq_len"].tolist()
+        for cache, pool, new in ((kc, inp["key"], inp["key_new"]),
+                                 (vc, inp["value"], inp["value_new"])):
+            want = oracle.append_kv_rows(raw(pool), raw(new), inp["block_tables"].numpy(), ql, kl)
+            assert np.array_equal(raw(cache), want)
+        return
     inp = wl.make_inputs(w, poison=True)
     out, lse = gpu_run(inp, want_lse=True)
     ro, rl, rows = oracle_run(inp, SAMPLES[name])
