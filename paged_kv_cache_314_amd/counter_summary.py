@@ -37,13 +37,16 @@ def kernel_source_hash(kind):
     return h.hexdigest()[:16]
 
 
-def counter_values(outdir, counter, name_part):
-    """Per-dispatch values (KiB) of `counter` for kernels whose name contains name_part."""
+def counter_values(outdir, counter, name_parts):
+    """Per-dispatch values (KiB) of `counter` for kernels whose name contains one of
+    name_parts (a string or a tuple of strings)."""
+    if isinstance(name_parts, str):
+        name_parts = (name_parts,)
     path = os.path.join(outdir, "run_counter_collection.csv")
     vals = {}
     with open(path) as f:
         for r in csv.DictReader(f):
-            if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+            if r["Counter_Name"] != counter or not any(n in r["Kernel_Name"] for n in name_parts):
                 continue
             d = r["Dispatch_Id"]          # a counter may come in several rows per dispatch
             vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
@@ -58,7 +61,7 @@ def main(argv):
     # the largest copy dispatch is the probe (torch may launch small copies too)
     fetch_scale = copy_kib / max(cf)
     write_scale = copy_kib / max(cw)
-    part = f"::{kind}<"
+    part = (f"::{kind}<", f"::{kind}(")        # template or plain kernel
     fv = counter_values(fdir, "FETCH_SIZE", part)
     wv = counter_values(wdir, "WRITE_SIZE", part)
     if not fv or not wv:
