@@ -550,7 +550,10 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         // chunk = tiles one item gives each wave's share of work: about `target`
         // workgroups in all, and a multiple of 4 tiles.  Wave-per-head items are 4x
         // larger; with nearly equal sequence lengths one full round of resident
-        // workgroups (2 per CU) is best, uneven lengths need two rounds for balance.
+        // workgroups is best (uneven lengths need two rounds for balance): one workgroup
+        // per CU for one-byte caches with per-channel scales, whose 128-byte rows read
+        // with fewer concurrent streams keep more DRAM page locality; two per CU
+        // otherwise (the general-antiquant kernel needs them to hide its latency).
         int64_t max_tiles = 0, n_dec = 0;
         for (int64_t b = 0; b < B; ++b) {
             if (ql[b * qls] != 1) continue;
@@ -559,8 +562,11 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         }
         const bool even = n_dec > 0 &&
                           4 * max_tiles * n_dec * kvh_num * p.head_groups <= 5 * total_tiles;
-        const int target = env_int("PA_DECODE_TARGET_ITEMS",
-                                   wph ? (even ? 2 : 4) * kComputeUnits : 2048);
+        const bool lean_bytes = p.kvtype != PA_F16 && p.kvtype != PA_BF16 &&
+                                p.kmode == PA_ANTIQUANT_PER_CHANNEL &&
+                                p.vmode == PA_ANTIQUANT_PER_CHANNEL && p.koff == nullptr;
+        const int rounds = wph ? (even ? (lean_bytes ? 1 : 2) : 4) : 0;
+        const int target = env_int("PA_DECODE_TARGET_ITEMS", wph ? rounds * kComputeUnits : 2048);
         const int64_t per_item = (total_tiles + target - 1) / target;      // kv-head tiles
         int chunk = static_cast<int>(std::min<int64_t>(wph ? (per_item + 3) / 4 : per_item, 1 << 20));
         chunk = std::max(chunk, 8);          // short sequences: no split, no combine
