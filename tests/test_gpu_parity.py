@@ -315,6 +315,33 @@ def test_append_then_prefill_attention():
     compare(out, lse, ro, rl, rows, inp["query"].dtype, "append then prefill")
 
 
+LARGE_CASES = [
+    # (kind, dtype, kv_dtype, D, H, Hkv, bs, q_lens, kv_lens, mask)
+    ("decode", "bf16", None, 128, 64, 8, 128, [1, 1], [131072 + 17, 1], pa.PA_MASK_NONE),
+    ("decode", "bf16", "i8", 128, 64, 8, 256, [1, 1], [131072 + 100, 3], pa.PA_MASK_NONE),
+    ("prefill", "f16", None, 128, 4, 2, 1024, [300], [65536 + 300], pa.PA_MASK_ALIBI),
+    ("prefill", "bf16", None, 64, 8, 8, 4096, [257, 1], [9000, 5000], pa.PA_MASK_CAUSAL),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LARGE_CASES)))
+def test_large_sizes(case):
+    """Long sequences (131 k tokens decode, a 65 k-token prefix) and large blocks (up to
+    4096 slots) against the oracle."""
+    kind, dt, kvdt, D, H, Hkv, bs, ql, kl, mask = LARGE_CASES[case]
+    _say(f"[large] case {case}: {kind} {dt}/{kvdt} D{D} H{H}/{Hkv} bs{bs} q{ql} kv{kl}")
+    inp = wl.make_random_case(900 + case, batch=len(kl), head_num=H, kv_head_num=Hkv,
+                              head_size=D, block_size=bs, q_lens=ql, kv_lens=kl, dtype=dt,
+                              kv_dtype=kvdt, mask_type=mask, poison=False)
+    out, lse, op, ws = gpu_run(inp, keep_op=True)
+    info = pa.pa_op_describe(op)
+    op.destroy()
+    assert info["mode"] == kind
+    ro, rl, rows = oracle_run(inp)
+    st = compare(out, lse, ro, rl, rows, inp["query"].dtype, f"large case {case}")
+    _say(f"[large] case {case} {st}")
+
+
 def test_decode_skips_sequences_without_query():
     inp = wl.make_random_case(51, batch=4, head_num=4, kv_head_num=2, head_size=128,
                               block_size=16, q_lens=[1, 0, 1, 0], kv_lens=[100, 50, 0, 7],
