@@ -45,8 +45,8 @@
 //                          keeps P_j), and sum_j P_j sV_j oV_j is added to every O_d
 //   per-channel V offset   out_d = sV_d * (O_d / l + oV_d)
 // Per-token scales / offsets of a tile: lane l loads entry T + (l & 31) of the K (l < 32)
-// or V (l >= 32) tensor with the tile's K rows, and each lane picks its tokens' values
-// with cross-lane reads.
+// or V (l >= 32) tensor with the tile's K rows; the wave passes them through LDS and each
+// lane reads its tokens' values back as two 16-byte runs per tensor.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -94,6 +94,9 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     __shared__ float s_m[kDecodeWaves][kHeadPack];
     __shared__ float s_l[kDecodeWaves][kHeadPack];
     __shared__ float s_o[kDecodeWaves][kHeadPack][D];
+    // XQ: one tile's per-token values, per wave: scales at [lane], offsets at [64 + lane]
+    // (lanes 0..31 hold K's tokens, 32..63 V's)
+    __shared__ __attribute__((aligned(16))) float s_tok[kDecodeWaves][128];
 
     const DecodeItem it = a.items[blockIdx.x];
     const int lane = threadIdx.x & 63;
@@ -331,6 +334,36 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     // loads right after the transpose consumes V, so two tiles are always in flight.
     auto step = [&](Tile& t, const TileBase& cur, const TileBase& next) {
         const int T = cur.T;
+        // XQ: the scores of this lane are tokens 16m + 4qg + r (m, r < 4) of the tile, so
+        // after the lanes put their loaded values into the wave's LDS slots each lane reads
+        // its K and V values back as 16-byte runs (LDS work of one wave runs in order)
+        float tk_s[8], tk_o[8], pv_s[8], pv_o[8];
+        if constexpr (XQ) {
+            if (tok_loads) {
+                float* st = s_tok[wave];
+                st[lane] = t.ta;
+                if (tok_off) st[64 + lane] = t.tb;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int j = 16 * m + 4 * qg;
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 ks = ktok ? *reinterpret_cast<const f32x4*>(st + j) : z;
+                    const f32x4 ko = ktok && tok_off ? *reinterpret_cast<const f32x4*>(st + 64 + j) : z;
+                    const f32x4 vs = vtok ? *reinterpret_cast<const f32x4*>(st + 32 + j) : z;
+                    const f32x4 vo = vtok && tok_off ? *reinterpret_cast<const f32x4*>(st + 96 + j) : z;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        tk_s[4 * m + r] = ks[r];
+                        tk_o[4 * m + r] = ko[r];
+                        pv_s[4 * m + r] = vs[r];
+                        pv_o[4 * m + r] = vo[r];
+                    }
+                }
+            }
+        }
         // ---- S = K Q^T, scaled to log2 units, bias
         float s[8];
 #pragma unroll
@@ -363,27 +396,10 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
             for (int r = 0; r < 4; ++r) {
                 float x = c[r] * s_mul;
                 if constexpr (XQ) {
-                    if (ktok) {
-                        const int j = 16 * m + 4 * qg + r;      // token of this score in the tile
-                        const float sk = __shfl(t.ta, j);
-                        const float ok = tok_off ? __shfl(t.tb, j) : 0.0f;
-                        x = (x + ok * qsum) * sk;
-                    }
+                    if (ktok) x = (x + tk_o[4 * m + r] * qsum) * tk_s[4 * m + r];
                 }
                 if constexpr (ALIBI) x += slope2 * static_cast<float>(T + 16 * m + 4 * qg + r - pos);
                 s[4 * m + r] = x;
-            }
-        }
-        // per-token V values of this lane's 8 tokens (read before issue_k refills t)
-        float pv_s[8], pv_o[8];
-        if constexpr (XQ) {
-            if (vtok) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int j = 32 + 16 * (i >> 2) + 4 * qg + (i & 3);
-                    pv_s[i] = __shfl(t.ta, j);
-                    pv_o[i] = tok_off ? __shfl(t.tb, j) : 0.0f;
-                }
             }
         }
         issue_k(t, next);

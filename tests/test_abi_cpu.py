@@ -154,6 +154,25 @@ def test_plan_for_named_workloads(name):
         _check_prefill_plan(info, ql, kv, w.head_num, w.mask_type, w.head_num // w.kv_head_num)
 
 
+def test_single_round_prefill_pairs_heavy_with_light():
+    """When an XCD's list fits one round (33..64 workgroups for its 32 CUs), positions k
+    and k + 32 share a CU: the first 32 are the heaviest, heaviest first, and the rest
+    come lightest first, so each CU gets one heavy and one light item."""
+    info = _plan_named("prefill_causal_bf16")
+    items = info["prefill_items"]
+    assert len(items) == 512
+    for x in range(8):
+        lst = [it for it in items[x::8] if it[7] != 0]
+        assert 32 < len(lst) <= 64
+        w = [it[6] for it in lst]
+        first, second = w[:32], w[32:]
+        assert first == sorted(first, reverse=True)
+        assert second == sorted(second)
+        assert min(first) >= max(second)
+        # the causal 16-tile clusters: pairs (8, 1), (7, 2), (6, 3), (5, 4) key tiles
+        assert sorted(w[k] + w[k + 32] for k in range(len(lst) - 32)) == [9] * (len(lst) - 32)
+
+
 def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
     """Every (sequence, kv head, head group) is covered by tile ranges that partition
     [0, ceil(kvlen/32)) exactly once; split items own consecutive slots merged by one
