@@ -25,8 +25,10 @@
  *     elements).  The innermost dimension must be contiguous; see each argument.
  *   - "device" = HIP device memory (e.g. a torch CUDA tensor on ROCm);
  *     "host" = ordinary CPU memory.
- *   - The caller owns every tensor and the workspace.  The library never allocates
- *     device memory.  It owns the pa_op (host memory), released by pa_op_destroy.
+ *   - The caller owns every tensor and the workspace.  The library owns the pa_op and
+ *     allocates only for it: the op's work lists (a few KB, 32 bytes per workgroup) in
+ *     pinned host memory and, from its first execution, a device copy of them; both
+ *     are released by pa_op_destroy.
  *   - Tensors and the workspace must stay alive, and must not be written by others,
  *     until the work enqueued by pa_paged_attention has completed on the stream.
  *   - Block ids in blockTables are not validated (aclnnFusedInferAttentionScoreV3,
@@ -210,13 +212,18 @@ pa_status pa_paged_attention_get_workspace_size_ex(
  * context argument becomes a HIP stream.)  workspace: device memory of at least the
  * phase-1 size, 256-byte aligned, or NULL if that size is 0; its contents on entry do
  * not matter and are scratch afterwards (it holds split-KV partial results; the size is
- * 0 when no sequence is split).  The call returns once the work is enqueued; the first
- * call on an op allocates a small pinned, device-mapped host buffer for the op's work
- * lists, which the kernels read in place (no host-to-device copy per run).
+ * 0 when no sequence is split).  The call returns once the work is enqueued.  The first
+ * call on an op copies its work lists into a small device buffer of the op on `stream`
+ * and waits for `stream` once (every later call only enqueues); the op is then bound to
+ * that stream's device, and a call on another device returns PA_ERR_PARAM_INVALID.  If
+ * the first call is made while `stream` is being captured into a graph, the op instead
+ * reads its work lists from pinned host memory over the bus on every run (no copy, no
+ * wait, no device binding; about a microsecond more per kernel).
  * An op may be executed any number of times, on any stream of its device; two
  * executions must not share a workspace while both are in flight.
  * Returns PA_ERR_NULLPTR (op, or a needed workspace, is NULL), PA_ERR_WORKSPACE_TOO_SMALL,
- * PA_ERR_PARAM_INVALID (workspace not 256-byte aligned) or PA_ERR_HIP on failure.
+ * PA_ERR_PARAM_INVALID (workspace not 256-byte aligned, or another device than the
+ * first run's) or PA_ERR_HIP on failure.
  */
 pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
                              void* stream);
@@ -248,6 +255,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
  * op                 out: handle (pa_op_destroy releases it); nTokens == 0 gives a no-op.
  * Phase 1 makes no HIP call.  pa_kv_cache_append enqueues the copy on `stream` (NULL =
  * the null stream); it may be run again, e.g. after the new rows were refilled in place.
+ * Its work lists are handled as for pa_paged_attention (device copy made on the first run).
  * pa_paged_attention rejects an append op and pa_kv_cache_append an attention op
  * (PA_ERR_PARAM_INVALID).  pa_op_set_timing_events applies to the copy kernel.
  */
@@ -276,7 +284,8 @@ pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop);
  * [b, kvh, hg, t0, t1, slot, qrow, kvlen], "combine_items" [kvh, hg, slot0, nsplit, qrow],
  * "prefill_items" [b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads] (heads query heads from
  * h, 128/heads query rows from qbeg), "append_items" [b, row0, pos0, count], "antiquant"
- * [key mode, value mode, offsets given].  Host only, no HIP call.
+ * [key mode, value mode, offsets given], "work_lists" ("none" before the first run,
+ * then "device" or "host").  Host only, no HIP call.
  * For inspection and tests: not a stable interface.  op == NULL returns 0. */
 uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap);
 

@@ -16,6 +16,9 @@ struct pa_op {
     pa::Plan plan;
     void* staging = nullptr;        // pinned, device-mapped work lists (made on first run)
     unsigned char* staging_dev = nullptr;   // the same memory as seen by the GPU
+    unsigned char* lists_dev = nullptr;     // device copy of the work lists (first run)
+    int lists_device = -1;                  // the device holding lists_dev
+    const unsigned char* lists = nullptr;   // what the kernels read: lists_dev or staging_dev
     hipEvent_t done = nullptr;      // recorded after the last kernel of each run
     hipEvent_t t_start = nullptr;   // caller's timing events around the main kernel
     hipEvent_t t_stop = nullptr;
@@ -35,11 +38,59 @@ pa_status hip_fail(hipError_t e, const char* what) {
     return fail(PA_ERR_HIP, msg);
 }
 
-// Copy the host work lists into one pinned, device-mapped buffer.  Each workgroup reads
-// its own 32-byte item from it at start-up, so a run needs no host-to-device copy.
-pa_status ensure_staging(pa_op* op) {
+// The work lists: each workgroup reads its own 32-byte item at start-up, a dependent load
+// ahead of everything else it does, so they are read from device memory: the first run
+// copies them from a pinned host buffer into a small device buffer of the op, on the
+// caller's stream, and waits for that stream once.  A first run made under stream
+// capture cannot wait; that op then reads the pinned buffer in place over the bus
+// (about 1 us more per launch).  Kernels of later runs on another device are refused.
+pa_status make_host_lists(pa_op* op);
+
+pa_status ensure_staging(pa_op* op, hipStream_t stream) {
     const pa::Plan& p = op->plan;
-    if (op->staging != nullptr || p.items_bytes == 0) return PA_OK;
+    if (p.items_bytes == 0) return PA_OK;
+    if (op->lists != nullptr) {
+        if (op->lists_dev == nullptr) return PA_OK;
+        int dev = -1;
+        hipError_t e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        if (dev != op->lists_device)
+            return fail(PA_ERR_PARAM_INVALID, "op was first run on device " +
+                                                  std::to_string(op->lists_device) +
+                                                  ", not on device " + std::to_string(dev));
+        return PA_OK;
+    }
+    pa_status st = make_host_lists(op);
+    if (st != PA_OK) return st;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cap != hipStreamCaptureStatusNone) {
+        op->lists = op->staging_dev;
+        return PA_OK;
+    }
+    int dev = -1;
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    void* d = nullptr;
+    e = hipMalloc(&d, p.items_bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(work lists)");
+    e = hipMemcpyAsync(d, op->staging, p.items_bytes, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail(e, "copy of the work lists");
+    }
+    op->lists_dev = static_cast<unsigned char*>(d);
+    op->lists_device = dev;
+    op->lists = op->lists_dev;
+    return PA_OK;
+}
+
+// Copy the host work lists into one pinned, device-mapped buffer.
+pa_status make_host_lists(pa_op* op) {
+    const pa::Plan& p = op->plan;
+    if (op->staging != nullptr) return PA_OK;
     hipError_t e = hipHostMalloc(&op->staging, p.items_bytes, hipHostMallocMapped);
     if (e != hipSuccess) {
         op->staging = nullptr;
@@ -164,7 +215,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         return e == hipSuccess ? PA_OK : hip_fail(e, "fill kernel launch");
     }
 
-    pa_status st = ensure_staging(op);
+    pa_status st = ensure_staging(op, s);
     if (st != PA_OK) return st;
     if (op->done == nullptr) {
         e = hipEventCreateWithFlags(&op->done, hipEventDisableTiming);
@@ -174,7 +225,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         }
     }
     auto* ws = static_cast<unsigned char*>(workspace);
-    const unsigned char* lists = op->staging_dev;
+    const unsigned char* lists = op->lists;
     const float scale_log2 = p.qk_scale * 1.4426950408889634f;
 
     if (p.mode == pa::Mode::kDecode) {
@@ -292,7 +343,8 @@ pa_status pa_kv_cache_append(pa_op* op, void* stream) {
     if (p.mode == pa::Mode::kNoop) return PA_OK;
     if (p.mode != pa::Mode::kAppend)
         return fail(PA_ERR_PARAM_INVALID, "op is not a KV-cache append plan");
-    pa_status st = ensure_staging(op);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pa_status st = ensure_staging(op, s);
     if (st != PA_OK) return st;
     hipError_t e;
     if (op->done == nullptr) {
@@ -302,9 +354,8 @@ pa_status pa_kv_cache_append(pa_op* op, void* stream) {
             return hip_fail(e, "hipEventCreateWithFlags");
         }
     }
-    hipStream_t s = static_cast<hipStream_t>(stream);
     pa::AppendArgs a{};
-    a.items = reinterpret_cast<const pa::AppendItem*>(op->staging_dev + p.off_items);
+    a.items = reinterpret_cast<const pa::AppendItem*>(op->lists + p.off_items);
     a.knew = p.knew;
     a.vnew = p.vnew;
     a.kcache = const_cast<void*>(p.k);
@@ -338,6 +389,7 @@ void pa_op_destroy(pa_op* op) {
         (void)hipEventSynchronize(op->done);
         (void)hipEventDestroy(op->done);
     }
+    if (op->lists_dev != nullptr) (void)hipFree(op->lists_dev);
     if (op->staging != nullptr) (void)hipHostFree(op->staging);
     delete op;
 }
@@ -361,6 +413,8 @@ uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
     s += ", \"antiquant\": [" + std::to_string(p.kmode) + ", " + std::to_string(p.vmode) + ", " +
          std::to_string(p.koff != nullptr ? 1 : 0) + "]";
     s += ", \"partial_slots\": " + std::to_string(p.partial_slots);
+    s += std::string(", \"work_lists\": \"") +
+         (op->lists == nullptr ? "none" : (op->lists_dev != nullptr ? "device" : "host")) + "\"";
     s += ", \"decode_items\": [";
     for (size_t i = 0; i < p.decode_items.size(); ++i) {
         const pa::DecodeItem& d = p.decode_items[i];

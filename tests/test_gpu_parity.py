@@ -467,6 +467,75 @@ def test_two_dimensional_query_form():
     compare(out2.reshape(2, 4, 64), lse, ro, rl, rows, torch.float16, "2-D query")
 
 
+def test_work_lists_copied_once_and_reused_on_other_streams():
+    """The first run copies the op's work lists to the device; later runs of the same op
+    on other streams of the device read that copy and give bit-identical results."""
+    inp = wl.make_random_case(73, batch=3, head_num=8, kv_head_num=2, head_size=128,
+                              block_size=16, q_lens=[1, 1, 1], kv_lens=[5000, 40, 333],
+                              dtype="f16")
+    s = torch.cuda.Stream()
+    out, lse, op, ws = gpu_run(inp, stream=s, keep_op=True)
+    try:
+        info = pa.pa_op_describe(op)
+        assert info["work_lists"] == "device"
+        assert info["partial_slots"] > 0          # the split path and its combine ran
+        ro, rl, rows = oracle_run(inp)
+        compare(out, lse, ro, rl, rows, torch.float16, "first run, side stream")
+        ref_o, ref_l = out.clone(), lse.clone()
+        for stream in (None, torch.cuda.Stream(), s):
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    finally:
+        op.destroy()
+
+
+def test_first_run_under_graph_capture_reads_host_lists():
+    """An op whose first run is captured into a graph keeps its work lists in pinned host
+    memory (no copy or wait under capture); every replay matches the eager result."""
+    inp = wl.make_random_case(74, batch=2, head_num=8, kv_head_num=2, head_size=128,
+                              block_size=16, q_lens=[1, 1], kv_lens=[4100, 77], dtype="bf16")
+    ref_o, ref_l = gpu_run(inp)                  # another op, eager, device lists
+    from tests.harness import to_device
+    g = to_device(inp)
+    q = g["query"]
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((q.shape[0], g["head_num"]), float("nan"), dtype=torch.float32,
+                     device=q.device)
+    op = pa.pa_paged_attention_get_workspace_size_ex(
+        q, g["key"], g["value"], g["block_tables"], None, g["seq_len"], g["kv_seq_len"],
+        g["slopes"], g["mask_type"], g["head_num"], g["kv_head_num"], g["qk_scale"],
+        g["key_scale"], g["value_scale"], None, None, 0, 0, out, lse)
+    ws = pa.alloc_workspace(op.workspace_size, q.device)
+    assert pa.pa_op_describe(op)["work_lists"] == "none"
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    try:
+        with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+            pa.pa_paged_attention(ws, op.workspace_size, op, None)
+        assert pa.pa_op_describe(op)["work_lists"] == "host"
+        for r in range(3):
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {r}"
+            # the program's own eager work between replays
+            x = torch.randn(4096, device=q.device)
+            assert torch.isfinite(x.sum()).item()
+        # an eager run of the same op after the replays reads the same host lists
+        out.fill_(float("nan"))
+        pa.pa_paged_attention(ws, op.workspace_size, op, None)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o)
+    finally:
+        graph.reset()
+        op.destroy()
+
+
 def test_runs_on_a_side_stream():
     inp = wl.make_random_case(72, batch=2, head_num=8, kv_head_num=2, head_size=128,
                               block_size=16, q_lens=[1, 1], kv_lens=[700, 33], dtype="bf16")
