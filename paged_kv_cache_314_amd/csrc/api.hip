@@ -304,6 +304,9 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.table_stride = p.table_stride;
         a.group = p.group;
         a.block_size = p.block_size;
+        a.block_shift = -1;
+        for (int sh = 0; sh < 31; ++sh)
+            if ((1 << sh) == p.block_size) a.block_shift = sh;
         a.mask_type = p.mask_type;
         a.scale_is_f32 = p.scale_type == PA_F32;
         a.scale_log2 = scale_log2;

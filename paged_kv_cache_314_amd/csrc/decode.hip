@@ -661,39 +661,68 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
 // Merge the nsplit partials of one (sequence, kv head, head group) in slot order.
 template <int D, bool BF16>
 __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
-    const CombineItem it = a.items[blockIdx.x];
+    // one thread per output element: item blockIdx.x / per_item, element
+    // (blockIdx.x % per_item) * 256 + threadIdx.x of its geff x D block
+    const int per_item = a.blocks_per_item;
+    const CombineItem it = a.items[blockIdx.x / per_item];
     const int geff = a.group < kHeadPack ? a.group : kHeadPack;
-    for (int e = threadIdx.x; e < geff * D; e += blockDim.x) {
-        const int h = e / D, d = e - (e / D) * D;
-        const int hlocal = it.hg * kHeadPack + h;
-        if (hlocal >= a.group) continue;
-        // unrolled so that the partials' loads of several splits are in flight together;
-        // the sums still run in ascending split order
-        const float* ml = a.part_ml + 2 * (static_cast<int64_t>(it.slot0) * geff + h);
-        const float* po = a.part_o + (static_cast<int64_t>(it.slot0) * geff + h) * D + d;
-        const int64_t ml_step = 2 * geff, o_step = static_cast<int64_t>(geff) * D;
-        float M = -INFINITY;
+    const int e = (blockIdx.x % per_item) * 256 + threadIdx.x;
+    if (e >= geff * D) return;
+    const int h = e / D, d = e - (e / D) * D;
+    const int hlocal = it.hg * kHeadPack + h;
+    if (hlocal >= a.group) return;
+    const float* ml = a.part_ml + 2 * (static_cast<int64_t>(it.slot0) * geff + h);
+    const float* po = a.part_o + (static_cast<int64_t>(it.slot0) * geff + h) * D + d;
+    const int64_t ml_step = 2 * geff, o_step = static_cast<int64_t>(geff) * D;
+    const int ns = it.nsplit;
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    constexpr int kMaxLoaded = 8;
+    if (ns <= kMaxLoaded) {
+        // every split's (m, l, o) is loaded before any is used: one memory round trip
+        float pm[kMaxLoaded], pl[kMaxLoaded], pv[kMaxLoaded];
+#pragma unroll
+        for (int s = 0; s < kMaxLoaded; ++s) {
+            if (s < ns) {
+                pm[s] = ml[s * ml_step];
+                pl[s] = ml[s * ml_step + 1];
+                pv[s] = po[s * o_step];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kMaxLoaded; ++s)
+            if (s < ns) M = fmaxf(M, pm[s]);
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int s = 0; s < kMaxLoaded; ++s) {
+                if (s < ns) {
+                    const float f = fast_exp2(pm[s] - M);
+                    L += pl[s] * f;
+                    O += pv[s] * f;
+                }
+            }
+        }
+    } else {
+        // the same sums in the same (ascending) split order, two passes
 #pragma unroll 8
-        for (int s = 0; s < it.nsplit; ++s) M = fmaxf(M, ml[s * ml_step]);
-        float L = 0.0f, O = 0.0f;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * ml_step]);
         if (M != -INFINITY) {
 #pragma unroll 4
-            for (int s = 0; s < it.nsplit; ++s) {
+            for (int s = 0; s < ns; ++s) {
                 const float f = fast_exp2(ml[s * ml_step] - M);
                 L += ml[s * ml_step + 1] * f;
                 O += po[s * o_step] * f;
             }
         }
-        const int out_head = it.kvh * a.group + hlocal;
-        const float val = (L > 0.0f) ? O / L : 0.0f;
-        uint16_t* orow = static_cast<uint16_t*>(a.out) +
-                         static_cast<int64_t>(it.qrow) * a.out_tok_stride +
-                         static_cast<int64_t>(out_head) * a.out_head_stride;
-        orow[d] = static_cast<uint16_t>(f32_to_half<BF16>(val));
-        if (d == 0 && a.lse != nullptr) {
-            a.lse[static_cast<int64_t>(it.qrow) * a.lse_tok_stride + out_head] =
-                (L > 0.0f) ? (M + fast_log2(L)) * kLn2 : INFINITY;
-        }
+    }
+    const int out_head = it.kvh * a.group + hlocal;
+    const float val = (L > 0.0f) ? O / L : 0.0f;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) +
+                     static_cast<int64_t>(it.qrow) * a.out_tok_stride +
+                     static_cast<int64_t>(out_head) * a.out_head_stride;
+    orow[d] = static_cast<uint16_t>(f32_to_half<BF16>(val));
+    if (d == 0 && a.lse != nullptr) {
+        a.lse[static_cast<int64_t>(it.qrow) * a.lse_tok_stride + out_head] =
+            (L > 0.0f) ? (M + fast_log2(L)) * kLn2 : INFINITY;
     }
 }
 
@@ -736,7 +765,11 @@ hipError_t launch_decode_d(const DecodeArgs& a, int n_items, bool bf16, bool i8,
 
 template <int D, bool BF16>
 hipError_t launch_combine_t(const CombineArgs& a, int n_items, hipStream_t stream) {
-    hipLaunchKernelGGL((combine_kernel<D, BF16>), dim3(n_items), dim3(256), 0, stream, a);
+    CombineArgs c = a;
+    const int geff = a.group < kHeadPack ? a.group : kHeadPack;
+    c.blocks_per_item = (geff * D + 255) / 256;
+    hipLaunchKernelGGL((combine_kernel<D, BF16>), dim3(n_items * c.blocks_per_item), dim3(256), 0,
+                       stream, c);
     return hipGetLastError();
 }
 

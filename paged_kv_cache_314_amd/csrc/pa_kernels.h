@@ -54,6 +54,7 @@ struct CombineArgs {
     float* lse;
     int64_t out_tok_stride, out_head_stride, lse_tok_stride;
     int32_t group;
+    int32_t blocks_per_item;   // workgroups per combine item (set at launch)
 };
 
 struct PrefillArgs {
@@ -72,6 +73,7 @@ struct PrefillArgs {
     int64_t v_blk_stride, v_slot_stride, v_head_stride, table_stride;
     int32_t group;
     int32_t block_size;
+    int32_t block_shift;    // log2(block_size) when it is a power of two, else -1
     int32_t mask_type;
     int32_t scale_is_f32;
     float scale_log2;

@@ -360,22 +360,19 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     auto vswz = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
     using gvoid = __attribute__((address_space(1))) void;
     using lvoid = __attribute__((address_space(3))) void;
-    auto token_addr = [&](const char* pool, int64_t blk_bytes, int64_t slot_bytes, int tok) {
-        const int blk = tok / bs;
-        return pool + ctab[blk] * blk_bytes + (tok - blk * bs) * slot_bytes;
-    };
+    const int bshift = a.block_shift;
     // one 16-key group: base = uniform address of source row 0, src[i] = the lane's
     // source row (relative) of load i, dst = LDS row 0 of the group
     auto issue_group = [&](const char* base, int64_t slot_bytes, uint16_t* dst, int ld,
                            const int (&src)[NL], bool is_k) {
+        uint64_t bi = reinterpret_cast<uintptr_t>(base);
+        asm volatile("" : "+s"(bi));
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int r = RPI * i + lrow;                       // LDS row in the group
             const int pos = lch ^ (is_k ? kswz(r) : vswz(r));   // the lane's slot holds
             uint32_t off = static_cast<uint32_t>(src[i] * slot_bytes) + 16u * pos;
             asm volatile("" : "+v"(off));
-            uint64_t bi = reinterpret_cast<uintptr_t>(base);
-            asm volatile("" : "+s"(bi));
             __builtin_amdgcn_global_load_lds(
                 reinterpret_cast<const gvoid*>(bi + off),
                 reinterpret_cast<lvoid*>(reinterpret_cast<uintptr_t>(dst + RPI * i * ld)), 16, 0, 0);
@@ -401,10 +398,20 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         // loop-invariant offsets
 #pragma unroll
         for (int i = 0; i < NL; ++i) src[i] += lrow;
-        issue_group(token_addr(kpool, kblk_bytes, kslot_bytes, gb), kslot_bytes,
-                    s_k[buf] + 16 * wave * KLD, KLD, src, true);
-        issue_group(token_addr(vpool, vblk_bytes, vslot_bytes, gb), vslot_bytes,
-                    s_v[buf] + 16 * wave * VLD, VLD, src, false);
+        // block and slot of token gb, shared by K and V: a shift for power-of-two block
+        // sizes (a wave-uniform branch), else a division; offsets inside a block fit 32
+        // bits (the planner bounds a block's span), block ids are taken as non-negative
+        const int blk = bshift >= 0 ? (gb >> bshift)
+                                    : static_cast<int>(static_cast<uint32_t>(gb) /
+                                                       static_cast<uint32_t>(bs));
+        const uint32_t slot = static_cast<uint32_t>(gb - blk * bs);
+        const uint64_t e = static_cast<uint32_t>(ctab[blk]);
+        const char* kb = kpool + e * static_cast<uint64_t>(kblk_bytes) +
+                         slot * static_cast<uint32_t>(kslot_bytes);
+        const char* vb = vpool + e * static_cast<uint64_t>(vblk_bytes) +
+                         slot * static_cast<uint32_t>(vslot_bytes);
+        issue_group(kb, kslot_bytes, s_k[buf] + 16 * wave * KLD, KLD, src, true);
+        issue_group(vb, vslot_bytes, s_v[buf] + 16 * wave * VLD, VLD, src, false);
     };
 
     // element offset of 16-byte chunk c of K / V tile row r
