@@ -361,57 +361,75 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     using gvoid = __attribute__((address_space(1))) void;
     using lvoid = __attribute__((address_space(3))) void;
     const int bshift = a.block_shift;
-    // one 16-key group: base = uniform address of source row 0, src[i] = the lane's
-    // source row (relative) of load i, dst = LDS row 0 of the group
-    auto issue_group = [&](const char* base, int64_t slot_bytes, uint16_t* dst, int ld,
-                           const int (&src)[NL], bool is_k) {
+    // lane byte offset of load i (source row src relative to the group's base token):
+    // the row's slot offset plus the lane's swizzled 16-byte chunk
+    auto lane_off = [&](int i, int src, uint32_t slot_bytes, bool is_k) {
+        const int r = RPI * i + lrow;                       // LDS row in the group
+        const int pos = lch ^ (is_k ? kswz(r) : vswz(r));   // the lane's slot holds
+        return static_cast<uint32_t>(src) * slot_bytes + 16u * pos;
+    };
+    const uint32_t kslot32 = static_cast<uint32_t>(kslot_bytes);
+    const uint32_t vslot32 = static_cast<uint32_t>(vslot_bytes);
+    // offsets of a full tile (source row = LDS row) are the same for every tile
+    uint32_t koff_full[NL], voff_full[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        koff_full[i] = lane_off(i, RPI * i + lrow, kslot32, true);
+        voff_full[i] = lane_off(i, RPI * i + lrow, vslot32, false);
+    }
+    // one 16-key group: base = uniform address of the group's first token, off[i] = the
+    // lane's byte offset of load i, dst = LDS row 0 of the group
+    auto issue_group = [&](const char* base, uint16_t* dst, int ld, const uint32_t (&off)[NL]) {
         uint64_t bi = reinterpret_cast<uintptr_t>(base);
         asm volatile("" : "+s"(bi));
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int r = RPI * i + lrow;                       // LDS row in the group
-            const int pos = lch ^ (is_k ? kswz(r) : vswz(r));   // the lane's slot holds
-            uint32_t off = static_cast<uint32_t>(src[i] * slot_bytes) + 16u * pos;
-            asm volatile("" : "+v"(off));
+            // opaque 32-bit lane offset: the load then takes the scalar-base +
+            // 32-bit-offset form with no per-load address arithmetic
+            uint32_t o = off[i];
+            asm volatile("" : "+v"(o));
             __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const gvoid*>(bi + off),
+                reinterpret_cast<const gvoid*>(bi + o),
                 reinterpret_cast<lvoid*>(reinterpret_cast<uintptr_t>(dst + RPI * i * ld)), 16, 0, 0);
         }
     };
     auto load_tile_direct = [&](int buf, int t) {
         const int j0 = t * BN;
         const int g0 = j0 + 16 * wave;
-        int src[NL];
         int gb = g0;
-        if (j0 + BN <= kvlen) {
-#pragma unroll
-            for (int i = 0; i < NL; ++i) src[i] = RPI * i;
-        } else {
-            // tail tile (wave-uniform branch): clamp rows to kvlen - 1
-            asm volatile("" ::: "memory");
-            const int last = kvlen - 1;
-            gb = g0 <= last ? g0 : last;
-#pragma unroll
-            for (int i = 0; i < NL; ++i) src[i] = min(RPI * i + lrow, last - gb) - lrow;
-        }
-        // src[i] + lrow is the source row; fold lrow in here so the common case keeps
-        // loop-invariant offsets
-#pragma unroll
-        for (int i = 0; i < NL; ++i) src[i] += lrow;
         // block and slot of token gb, shared by K and V: a shift for power-of-two block
         // sizes (a wave-uniform branch), else a division; offsets inside a block fit 32
         // bits (the planner bounds a block's span), block ids are taken as non-negative
-        const int blk = bshift >= 0 ? (gb >> bshift)
-                                    : static_cast<int>(static_cast<uint32_t>(gb) /
-                                                       static_cast<uint32_t>(bs));
-        const uint32_t slot = static_cast<uint32_t>(gb - blk * bs);
-        const uint64_t e = static_cast<uint32_t>(ctab[blk]);
-        const char* kb = kpool + e * static_cast<uint64_t>(kblk_bytes) +
-                         slot * static_cast<uint32_t>(kslot_bytes);
-        const char* vb = vpool + e * static_cast<uint64_t>(vblk_bytes) +
-                         slot * static_cast<uint32_t>(vslot_bytes);
-        issue_group(kb, kslot_bytes, s_k[buf] + 16 * wave * KLD, KLD, src, true);
-        issue_group(vb, vslot_bytes, s_v[buf] + 16 * wave * VLD, VLD, src, false);
+        auto bases = [&](const char*& kb, const char*& vb) {
+            const int blk = bshift >= 0 ? (gb >> bshift)
+                                        : static_cast<int>(static_cast<uint32_t>(gb) /
+                                                           static_cast<uint32_t>(bs));
+            const uint32_t slot = static_cast<uint32_t>(gb - blk * bs);
+            const uint64_t e = static_cast<uint32_t>(ctab[blk]);
+            kb = kpool + e * static_cast<uint64_t>(kblk_bytes) + slot * kslot32;
+            vb = vpool + e * static_cast<uint64_t>(vblk_bytes) + slot * vslot32;
+        };
+        const char *kb, *vb;
+        if (j0 + BN <= kvlen) {
+            bases(kb, vb);
+            issue_group(kb, s_k[buf] + 16 * wave * KLD, KLD, koff_full);
+            issue_group(vb, s_v[buf] + 16 * wave * VLD, VLD, voff_full);
+        } else {
+            // tail tile (wave-uniform branch): rows past kvlen re-read row kvlen - 1
+            asm volatile("" ::: "memory");
+            const int last = kvlen - 1;
+            gb = g0 <= last ? g0 : last;
+            uint32_t ko[NL], vo[NL];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int src = min(RPI * i + lrow, last - gb);
+                ko[i] = lane_off(i, src, kslot32, true);
+                vo[i] = lane_off(i, src, vslot32, false);
+            }
+            bases(kb, vb);
+            issue_group(kb, s_k[buf] + 16 * wave * KLD, KLD, ko);
+            issue_group(vb, s_v[buf] + 16 * wave * VLD, VLD, vo);
+        }
     };
 
     // element offset of 16-byte chunk c of K / V tile row r
@@ -433,6 +451,16 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
     }
 
+    // LDS byte addresses of the lane's K operand reads in buffer 0 (row qcol, chunk
+    // 2 ks + g2); rows 32.. of the tile share the swizzle of rows 0..31
+    constexpr uint32_t kKBufBytes = BN * KLD * 2;
+    using lds_u32x4 = const __attribute__((address_space(3))) u32x4*;
+    uint32_t kaddr[KS];
+#pragma unroll
+    for (int ks_i = 0; ks_i < KS; ++ks_i)
+        kaddr[ks_i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_k[0])) +
+                      2u * kpos(qcol, 2 * ks_i + g2);
+
     // ---- stage 1: S^T = K Q^T for the K tile in s_k[buf] (plus the ALiBi term)
     auto qk = [&](int buf, f32x16 (&sacc)[2]) {
 #pragma unroll
@@ -440,13 +468,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.0f;
         }
-        const uint16_t* ks = s_k[buf];
+        // the lane's read addresses in buffer 0 are loop-invariant (kaddr); buffer 1 is
+        // one uniform add away, the second 32-key half an immediate offset
+        const uint32_t boff = static_cast<uint32_t>(buf) * kKBufBytes;
 #pragma unroll
         for (int ks_i = 0; ks_i < KS; ++ks_i) {
+            // opaque sum, so that the second half's offset folds into the read
+            uint32_t ka = kaddr[ks_i] + boff;
+            asm volatile("" : "+v"(ka));
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const u32x4 kop = *reinterpret_cast<const u32x4*>(
-                    ks + kpos(mt * 32 + qcol, 2 * ks_i + g2));
+                const u32x4 kop = *reinterpret_cast<lds_u32x4>(
+                    static_cast<uintptr_t>(ka + mt * 32 * KLD * 2));
                 sacc[mt] = mfma32x32x16<MBF>(kop, qhi[ks_i], sacc[mt]);
                 if constexpr (I8) sacc[mt] = mfma32x32x16<false>(kop, qlo[ks_i], sacc[mt]);
             }
