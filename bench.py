@@ -3,10 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--copy-probe MiB]
 
-A step is one execute of the planned operator (pa_paged_attention): the upload of
-the work lists plus every kernel of the path, over one batch of seeded synthetic
-inputs already resident in HBM.  The plan (phase 1) is made once before timing;
-its host time is reported as ``plan_us``.  Prints ONE JSON line.
+A step is one execute of the planned operator (pa_paged_attention): every kernel of
+the path over one batch of seeded synthetic inputs already resident in HBM.  The plan
+(phase 1) is made once before timing; its host time is reported as ``plan_us``; the
+op's first execute (inside the warmup) copies its work lists to the device.  Without
+--warmup, the untimed warmup runs for WARMUP_SECONDS (at least 10 steps) so that the
+GPU clock has ramped up; the count run is reported as "warmup".  Prints ONE JSON line.
 
 Default workload: causal prefill, bf16, B=4, seqLen=kvSeqLen=512, H=32, Hkv=8,
 D=128, blockSize=128 ("prefill_causal_bf16").  --workload picks another of the
@@ -31,13 +33,19 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense MFMA, published
+# default warmup length: MFMA-heavy kernels run several percent slower during the first
+# tens of milliseconds on an idle GPU (measured: ALiBi prefix prefill 218 us per step
+# after 10 warmup steps, 193 us after 300)
+WARMUP_SECONDS = 0.5
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed warmup steps; default: as many as fill %.1f s (at least 10), "
+                         "so that the GPU clock has ramped up before timing" % WARMUP_SECONDS)
     ap.add_argument("--workload", default="prefill_causal_bf16")
     ap.add_argument("--kv-layout", choices=["bnbsh", "bnnbsd"], default="bnbsh",
                     help="K/V pool memory layout: (block, slot, kv head, d) as the workload "
@@ -111,7 +119,8 @@ def traffic_from_profiles(workload, kind):
 
 def cpu_baseline(inp, nbytes, flops, decode, budget_s):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
-    whole sequences, one after another, until the time budget is spent."""
+    whole sequences, one after another (starting again at the first after the last),
+    until the time budget is spent."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -151,7 +160,9 @@ def cpu_baseline(inp, nbytes, flops, decode, budget_s):
         total_units += ql[b] * kl[b] if not decode else kl[b]
     t0 = time.perf_counter()
     nseq = 0
-    for b in range(len(ql)):
+    # whole sequences in order, wrapping round to the first one, until the budget is spent
+    for i in range(1 << 30):
+        b = i % len(ql)
         kb = oracle.gather_sequence(k, table[b], kl[b], bs)
         vb = oracle.gather_sequence(v, table[b], kl[b], bs)
         if fp8:
@@ -173,8 +184,28 @@ def cpu_baseline(inp, nbytes, flops, decode, budget_s):
     else:
         value, unit = flops * frac / dt / 1e12, "TFLOP/s"
     return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
-            "sample": f"{nseq} of {len(ql)} sequences (all heads), {frac:.3f} of the "
-                      f"step's work, {dt:.1f} s, fp64 NumPy, BLAS threads {threads}"}
+            "sample": f"{nseq} sequences (all heads) taken in order from the step's "
+                      f"{len(ql)}, {frac:.3f} times the step's work, {dt:.1f} s, fp64 NumPy, "
+                      f"BLAS threads {threads}"}
+
+
+def warmup(args, step):
+    """Run the untimed warmup steps: exactly --warmup W if given, else at least 10 and
+    until WARMUP_SECONDS have passed.  Returns the number run."""
+    import torch
+    if args.warmup >= 0:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return args.warmup
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= WARMUP_SECONDS:
+            return n
 
 
 # ------------------------------------------------------------ KV-cache append
@@ -201,9 +232,7 @@ def bench_append(args, w, dev):
     plan_us = (time.perf_counter() - t_plan) * 1e6
     info = pa.pa_op_describe(op)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        pa.pa_kv_cache_append(op, stream)
-    torch.cuda.synchronize()
+    args.warmup = warmup(args, lambda: pa.pa_kv_cache_append(op, stream))
     t0 = time.perf_counter()
     for _ in range(args.steps):
         pa.pa_kv_cache_append(op, stream)
@@ -311,9 +340,7 @@ def main():
     info = pa.pa_op_describe(op)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
-        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
-    torch.cuda.synchronize()
+    args.warmup = warmup(args, lambda: pa.pa_paged_attention(ws, op.workspace_size, op, stream))
 
     # timed region: K whole steps
     torch.cuda.synchronize()
