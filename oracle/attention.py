@@ -13,7 +13,7 @@ Notation follows the pages:
   lse    [nTokens, headNum], natural log    (aclnnFusedInferAttentionScoreV3,
                                              Constraints: softmaxLse)
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * query head h uses kv head h // (headNum / kvHeadNum);
   * the seqLen new queries of a sequence are its LAST seqLen positions, so
     query i sits at absolute position p_i = kvSeqLen - seqLen + i

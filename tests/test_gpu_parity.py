@@ -363,6 +363,9 @@ PREFILL_CASES = [
     ("bf16", "i8", 128, 4, 2, 64, [150, 33], [700, 33], pa.PA_MASK_CAUSAL),
     ("f16", "i8", 64, 2, 2, 32, [65], [2000], pa.PA_MASK_ALIBI),
     ("f16", None, 128, 3, 3, 16, [1, 2, 0, 66], [5, 2, 9, 66], pa.PA_MASK_NONE),
+    # block sizes that are not powers of two: the tile loads find the block by division
+    ("f16", None, 128, 4, 1, 80, [300, 77], [1000, 400], pa.PA_MASK_ALIBI),
+    ("bf16", None, 64, 2, 2, 48, [257, 64], [1500, 64], pa.PA_MASK_CAUSAL),
 ]
 
 
