@@ -18,7 +18,9 @@ Throughput: prefill workloads report algorithmic TFLOP/s (4*D flops per visible
 (query, key) pair, exact causal count); decode workloads report algorithmic GB/s
 (K/V bytes of the valid tokens + Q + out + lse + used block-table entries +
 antiquant scales).  ``roofline`` covers the main kernel alone, timed with HIP
-events recorded on its launch stream around each launch.
+events recorded on its launch stream around each launch (mean, and p10 / median / p90),
+back to back (warm caches) and, under ``roofline.cold``, after a 1 GiB read before each
+launch (cold caches).
 """
 
 import argparse
@@ -37,6 +39,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense MFMA, published
 # tens of milliseconds on an idle GPU (measured: ALiBi prefix prefill 218 us per step
 # after 10 warmup steps, 193 us after 300)
 WARMUP_SECONDS = 0.5
+FLUSH_MIB = 1024                 # cache flush before each cold launch (256 MB MALL + L2s)
 
 
 def parse():
@@ -365,6 +368,24 @@ def main():
     kms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
     kernel_ms = sum(kms) / len(kms)
 
+    # the same kernel from cold caches: a read of a FLUSH_MIB buffer (larger than the
+    # 256 MB Infinity Cache and the L2s together) runs on the stream before each launch
+    nc = min(args.steps, 20)
+    flush = torch.ones(FLUSH_MIB << 18, dtype=torch.float32, device=dev)
+    cstarts = [torch.cuda.Event(enable_timing=True) for _ in range(nc)]
+    cstops = [torch.cuda.Event(enable_timing=True) for _ in range(nc)]
+    for e in cstarts + cstops:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for s_ev, e_ev in zip(cstarts, cstops):
+        flush.sum()
+        pa.pa_op_set_timing_events(op, s_ev, e_ev)
+        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+    pa.pa_op_set_timing_events(op, None, None)
+    torch.cuda.synchronize()
+    cold_ms = sum(s.elapsed_time(e) for s, e in zip(cstarts, cstops)) / nc
+    del flush
+
     if decode:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
@@ -383,6 +404,13 @@ def main():
     roof["traffic"] = traffic_from_profiles(args.workload, kind)
     roof["kernel"] = f"{kind}_kernel"
     roof["kernel_us"] = kernel_ms * 1e3
+    qs = sorted(kms)
+    pick = lambda f: qs[int(round(f * (len(qs) - 1)))] * 1e3
+    roof["kernel_us_p10_median_p90"] = [pick(0.1), pick(0.5), pick(0.9)]
+    work = nbytes / 1e9 if decode else flops / 1e12
+    roof["cold"] = {"kernel_us": cold_ms * 1e3, "achieved": work / (cold_ms * 1e-3),
+                    "frac": work / (cold_ms * 1e-3) / roof["peak"], "launches": nc,
+                    "flush": f"read of {FLUSH_MIB} MiB before each launch"}
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
 
