@@ -506,7 +506,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     //      their first key) are re-based, which rescales O and l.  Afterwards every
     //      score is <= slack, so exp2 of it is safe to round to 16 bits.
     //      The key of sacc[mt][r] is j0 + 4*g2 + dj, dj = 32mt + 8(r/4) + r%4.
-    auto scores = [&](f32x16 (&sacc)[2], int j0, bool need_mask) {
+    auto scores = [&](f32x16 (&sacc)[2], int j0, bool need_mask, bool first) {
         const float mo = (m_ref == -INFINITY) ? 0.0f : m_ref;
         float base = -mo;
         if constexpr (alibi) base += slope2 * static_cast<float>(j0 - pos);
@@ -543,8 +543,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             const float alpha = grow ? fast_exp2(m_ref - (mo + up)) : 1.0f;
             m_ref = grow ? mo + up : m_ref;
             l_run *= alpha;
+            // on the wave's first tile O is still zero: nothing to rescale
+            if (!first) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -611,7 +614,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             f32x16 sacc[2];
             u32x4 pop[4];
             qk(t & 1, sacc);
-            scores(sacc, t * BN, need_mask(t));
+            scores(sacc, t * BN, need_mask(t), t == t_act);   // tiles run from t_act down
             probs(sacc, pop);
             pv(pop, t & 1);
         }
