@@ -411,6 +411,15 @@ def main():
     roof["cold"] = {"kernel_us": cold_ms * 1e3, "achieved": work / (cold_ms * 1e-3),
                     "frac": work / (cold_ms * 1e-3) / roof["peak"], "launches": nc,
                     "flush": f"read of {FLUSH_MIB} MiB before each launch"}
+    if not decode:
+        # the same launch against the HBM roof: a prefill whose flops per algorithmic
+        # byte fall below the ridge (2.5 PFLOP/s / 8 TB/s = 312.5) is bound by HBM first
+        ai = flops / nbytes
+        hbm = nbytes / (kernel_ms * 1e-3) / 1e9
+        roof["hbm_view"] = {"achieved": hbm, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": hbm / PEAK_HBM_GBS, "flop_per_byte": ai,
+                            "ridge_flop_per_byte": peak * 1e12 / (PEAK_HBM_GBS * 1e9),
+                            "roof_tflops": min(peak, ai * PEAK_HBM_GBS / 1e3)}
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
 
