@@ -353,9 +353,24 @@ def main():
     ref_out = out.clone()
     ref_lse = lse.clone() if lse is not None else None
 
-    # timed region (right after the warmup): K whole steps, captured once into a HIP
-    # graph and replayed as one launch (no host work between steps); the captured
-    # executes hold no memset
+    # main-kernel duration: HIP events recorded around each launch on its stream, taken
+    # first after the warmup (the GPU's clock drifts under long runs of back-to-back
+    # launches; rocprofv3's kernel averages of the same command are taken in this state)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + stops:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for s_ev, e_ev in zip(starts, stops):
+        pa.pa_op_set_timing_events(op, s_ev, e_ev)
+        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+    pa.pa_op_set_timing_events(op, None, None)
+    torch.cuda.synchronize()
+    kms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
+    kernel_ms = sum(kms) / len(kms)
+
+    # timed region: K whole steps, captured once into a HIP graph and replayed as one
+    # launch (no host work between steps); the captured executes hold no memset
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         cap = torch.cuda.current_stream()
@@ -378,20 +393,6 @@ def main():
         pa.pa_paged_attention(ws, op.workspace_size, op, stream)
     torch.cuda.synchronize()
     ms_per_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # main-kernel duration: HIP events recorded around each launch on its stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for e in starts + stops:
-        e.record(stream)
-    torch.cuda.synchronize()
-    for s_ev, e_ev in zip(starts, stops):
-        pa.pa_op_set_timing_events(op, s_ev, e_ev)
-        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
-    pa.pa_op_set_timing_events(op, None, None)
-    torch.cuda.synchronize()
-    kms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
-    kernel_ms = sum(kms) / len(kms)
 
     # the same kernel from cold caches: a read of a FLUSH_MIB buffer (larger than the
     # 256 MB Infinity Cache and the L2s together) runs on the stream before each launch
