@@ -596,11 +596,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // Key tiles are visited from the last one down: under a causal mask (and even more
-    // with ALiBi, whose bias grows towards the diagonal) the first tile then holds the
-    // row maxima, so later tiles rarely re-base the running sums.  Tile t is staged in
-    // s_k[t % 2] / s_v[t % 2].  A wave works on tiles 0 .. t_act (the rows it owns see
-    // no key of a higher tile); tiles on the diagonal or past kvlen are masked.
+    // A wave works on tiles 0 .. t_act (the rows it owns see no key of a higher tile);
+    // tiles on the diagonal or past kvlen are masked.
     const int T = it.ktiles - 1;
     const int t_act = !wave_live ? -1
                     : (!causal ? T : (wave_pmax < 0 ? -1 : min(T, wave_pmax / BN)));
@@ -608,41 +605,55 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         return (t * BN + BN > kvlen) || (causal && t * BN + BN - 1 > wave_pmin);
     };
 
-    // one stage per iteration: tile t - 1 loads while tile t is computed
-    auto compute = [&](int t) {
+    // Visiting order.  The first P tiles hold only keys before the new tokens (key j <
+    // kvlen - seqLen is visible to every query row), and the workgroups of all query
+    // tiles of a head need them: they are visited first, from tile P - 1 down to 0, so
+    // that those workgroups (placed side by side on one XCD) stream the same K/V tiles
+    // at the same time and share them through the L2.  Then the item's own diagonal
+    // tiles, from T down to P.  Step k visits tile tile_of(k); its buffer is k % 2.
+    // Either part runs from the keys nearest the queries downwards, so the first tile of
+    // each part holds (with ALiBi, whose bias grows towards the diagonal) the row maxima
+    // and later tiles rarely re-base the running sums.
+    const int shift_keys = kvlen - qlen;
+    const int P = (!causal) ? T + 1 : (shift_keys > 0 ? min(shift_keys / BN, T + 1) : 0);
+    auto tile_of = [&](int k) { return k < P ? P - 1 - k : T - (k - P); };
+    // the wave's first computed step (O and l are zero before it)
+    const int k_first = (P > 0) ? 0 : T - t_act;
+    auto compute = [&](int t, int buf, bool first) {
         if (t <= t_act) {
             f32x16 sacc[2];
             u32x4 pop[4];
-            qk(t & 1, sacc);
-            scores(sacc, t * BN, need_mask(t), t == t_act);   // tiles run from t_act down
+            qk(buf, sacc);
+            scores(sacc, t * BN, need_mask(t), first);
             probs(sacc, pop);
-            pv(pop, t & 1);
+            pv(pop, buf);
         }
     };
     if constexpr (DIRECT) {
-        // the loads into s_*[(t-1) % 2] start after the barrier that follows every read
-        // of that buffer's previous tile (t + 1); vmcnt(0) + barrier publish them
-        if (T >= 0) load_tile_direct(T & 1, T);
-        for (int t = T; t >= 0; --t) {
+        // the loads into buffer (k+1) % 2 start after the barrier that follows every read
+        // of that buffer's previous tile (step k - 1); vmcnt(0) + barrier publish them
+        if (T >= 0) load_tile_direct(0, tile_of(0));
+        for (int k = 0; k <= T; ++k) {
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
-            if (t >= 1) load_tile_direct((t - 1) & 1, t - 1);
-            compute(t);
+            if (k < T) load_tile_direct((k + 1) & 1, tile_of(k + 1));
+            compute(tile_of(k), k & 1, k == k_first);
         }
     } else {
         if (T >= 0) {
-            load_k(T);
-            load_v(T);
+            load_k(tile_of(0));
+            load_v(tile_of(0));
         }
-        for (int t = T; t >= 0; --t) {
-            store_k(t & 1);
-            store_v(t & 1, t);
+        for (int k = 0; k <= T; ++k) {
+            const int t = tile_of(k);
+            store_k(k & 1);
+            store_v(k & 1, t);
             __syncthreads();
-            if (t >= 1) {
-                load_k(t - 1);
-                load_v(t - 1);
+            if (k < T) {
+                load_k(tile_of(k + 1));
+                load_v(tile_of(k + 1));
             }
-            compute(t);
+            compute(t, k & 1, k == k_first);
         }
     }
 
