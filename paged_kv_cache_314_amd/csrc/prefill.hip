@@ -44,6 +44,7 @@ namespace {
 
 constexpr int BN = kPrefillBN;          // 64 keys per tile
 constexpr float kRescaleSlack = 8.0f;   // log2 units a row max may exceed its reference
+constexpr float kNegligible = 32.0f;    // log2 units below the reference: weight < 2^-32
 // s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -506,6 +507,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     //      their first key) are re-based, which rescales O and l.  Afterwards every
     //      score is <= slack, so exp2 of it is safe to round to 16 bits.
     //      The key of sacc[mt][r] is j0 + 4*g2 + dj, dj = 32mt + 8(r/4) + r%4.
+    //      Returns true (ALiBi, 16-bit K/V) when every score of the tile, in every row of the
+    //      wave, lies more than kNegligible below the row's reference: each weight is then
+    //      below 2^-32 of the reference key's, so the tile's P and P V are skipped (its
+    //      share of l and O stays below 2^-32 per key, under fp32 rounding of the sums).
     auto scores = [&](f32x16 (&sacc)[2], int j0, bool need_mask, bool first) {
         const float mo = (m_ref == -INFINITY) ? 0.0f : m_ref;
         float base = -mo;
@@ -538,6 +543,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
         tmax = max_halves(tmax);
         const bool grow = (tmax > kRescaleSlack) || (m_ref == -INFINITY && tmax > -INFINITY);
+        bool negligible = false;
+        if constexpr (alibi && !I8) negligible = !__any(grow || tmax >= -kNegligible);
         if (__any(grow)) {
             const float up = grow ? tmax : 0.0f;
             const float alpha = grow ? fast_exp2(m_ref - (mo + up)) : 1.0f;
@@ -554,6 +561,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 for (int r = 0; r < 16; ++r) sacc[mt][r] -= up;
             }
         }
+        return negligible;
     };
 
     // ---- P = exp2(scores), packed as the P^T operands (k-step kt holds keys
@@ -624,9 +632,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             f32x16 sacc[2];
             u32x4 pop[4];
             qk(buf, sacc);
-            scores(sacc, t * BN, need_mask(t), first);
-            probs(sacc, pop);
-            pv(pop, buf);
+            if (!scores(sacc, t * BN, need_mask(t), first)) {
+                probs(sacc, pop);
+                pv(pop, buf);
+            }
         }
     };
     if constexpr (DIRECT) {
