@@ -21,9 +21,10 @@ Throughput: prefill workloads report algorithmic TFLOP/s (4*D flops per visible
 (query, key) pair, exact causal count); decode workloads report algorithmic GB/s
 (K/V bytes of the valid tokens + Q + out + lse + used block-table entries +
 antiquant scales).  ``roofline`` covers the main kernel alone, timed with HIP
-events recorded on its launch stream around each launch (mean, and p10 / median / p90),
-back to back (warm caches) and, under ``roofline.cold``, after a 1 GiB read before each
-launch (cold caches).
+events recorded on its launch stream around each of K launches made right after the
+warmup (mean, and p10 / median / p90), back to back (warm caches) and, under
+``roofline.cold``, after a 1 GiB read before each launch (cold caches); prefill is
+also given against the HBM roof under ``roofline.hbm_view``.
 """
 
 import argparse
