@@ -381,6 +381,24 @@ def test_prefill_random(case):
     compare(out, lse, ro, rl, rows, inp["query"].dtype, f"prefill case {case}")
 
 
+# ----------------------------------------------- steep ALiBi: negligible tiles skipped
+
+@pytest.mark.parametrize("dt,D", [("f16", 128), ("bf16", 64)])
+def test_steep_alibi_long_prefix(dt, D):
+    """Slopes of 1 over a 3000-token prefix: nearly every prefix tile lies more than 32
+    log2 units below its rows' reference, so the kernel skips its P and P V; out and
+    lse must still match the full computation of the oracle."""
+    _say(f"[steep alibi] {dt} D={D}")
+    inp = wl.make_random_case(950 + D, batch=2, head_num=4, kv_head_num=2, head_size=D,
+                              block_size=64, q_lens=[200, 70], kv_lens=[3200, 3070],
+                              dtype=dt, mask_type=pa.PA_MASK_ALIBI)
+    inp["slopes"] = torch.full((4,), 1.0, dtype=torch.float32)
+    inp["slopes"][3] = 0.004          # one shallow head: its tiles are all computed
+    out, lse = gpu_run(inp)
+    ro, rl, rows = oracle_run(inp)
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"steep alibi {dt} D={D}")
+
+
 # ----------------------------------------------------------- unusual qkScale
 
 SCALE_KINDS = {
