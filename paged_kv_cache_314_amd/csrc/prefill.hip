@@ -613,20 +613,25 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         return (t * BN + BN > kvlen) || (causal && t * BN + BN - 1 > wave_pmin);
     };
 
-    // Visiting order.  The first P tiles hold only keys before the new tokens (key j <
-    // kvlen - seqLen is visible to every query row), and the workgroups of all query
-    // tiles of a head need them: they are visited first, from tile P - 1 down to 0, so
-    // that those workgroups (placed side by side on one XCD) stream the same K/V tiles
-    // at the same time and share them through the L2.  Then the item's own diagonal
-    // tiles, from T down to P.  Step k visits tile tile_of(k); its buffer is k % 2.
-    // Either part runs from the keys nearest the queries downwards, so the first tile of
-    // each part holds (with ALiBi, whose bias grows towards the diagonal) the row maxima
-    // and later tiles rarely re-base the running sums.
+    // Visiting order.  Step k visits tile tile_of(k); its buffer is k % 2.
+    //  - First the item's last tile T, the one nearest its queries: under a causal mask
+    //    (and even more with ALiBi, whose bias grows towards the diagonal) it holds the
+    //    row maxima, so later tiles rarely re-base the running sums, and under ALiBi the
+    //    tiles far from the queries are then recognised as negligible at once.
+    //  - Then the P tiles that hold only keys before the new tokens (key j < kvlen -
+    //    seqLen is visible to every query row), from P - 1 down to 0: the workgroups of
+    //    all query tiles of a head need them and run side by side on one XCD, so they
+    //    stream these tiles at nearly the same time and share them through the L2.
+    //  - Then the rest of the item's diagonal tiles, from T - 1 down to P.
+    // Without a mask every tile is visible to every row: T down to 0.
     const int shift_keys = kvlen - qlen;
-    const int P = (!causal) ? T + 1 : (shift_keys > 0 ? min(shift_keys / BN, T + 1) : 0);
-    auto tile_of = [&](int k) { return k < P ? P - 1 - k : T - (k - P); };
-    // the wave's first computed step (O and l are zero before it)
-    const int k_first = (P > 0) ? 0 : T - t_act;
+    const int P = (!causal) ? 0 : (shift_keys > 0 ? min(shift_keys / BN, T) : 0);
+    auto tile_of = [&](int k) {
+        return k == 0 ? T : (k <= P ? P - k : T - (k - P));
+    };
+    // the wave's first computed step (O and l are zero before it); a live wave sees
+    // every prefix tile (t_act >= P)
+    const int k_first = (t_act == T) ? 0 : (P > 0 ? 1 : T - t_act);
     auto compute = [&](int t, int buf, bool first) {
         if (t <= t_act) {
             f32x16 sacc[2];
