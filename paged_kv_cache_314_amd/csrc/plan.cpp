@@ -225,7 +225,7 @@ std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items) {
     // equal-weight pairs).  Longer lists keep the cluster order, which is what lets the
     // query tiles of one (sequence, head block) share its K/V tiles through the L2.
     constexpr size_t kCusPerXcd = kComputeUnits / kXcds;
-    if (env_int("PA_PREFILL_PAIR", 1) != 0) {
+    if (env_flag("PA_PREFILL_PAIR", true)) {
         for (auto& l : lists) {
             if (l.size() <= kCusPerXcd || l.size() > 2 * kCusPerXcd) continue;
             std::stable_sort(l.begin(), l.end(), [](const PrefillItem& x, const PrefillItem& y) {
@@ -694,7 +694,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                              if (x.ktiles != y.ktiles) return x.ktiles > y.ktiles;
                              return head_desc && x.h > y.h;
                          });
-        if (env_int("PA_PREFILL_XCD_ORDER", 1) != 0) p.prefill_items = xcd_order(p.prefill_items);
+        if (env_flag("PA_PREFILL_XCD_ORDER", true)) p.prefill_items = xcd_order(p.prefill_items);
         p.off_items = 0;
         p.items_bytes = align256(p.prefill_items.size() * sizeof(PrefillItem));
         p.workspace_bytes = 0;

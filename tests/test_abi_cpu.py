@@ -154,6 +154,19 @@ def test_plan_for_named_workloads(name):
         _check_prefill_plan(info, ql, kv, w.head_num, w.mask_type, w.head_num // w.kv_head_num)
 
 
+def test_alibi_prefill_items_longest_then_highest_head(monkeypatch):
+    """Before the XCD placement, ALiBi prefill items run longest first and, among equal
+    lengths, highest head first (the usual slopes fall with the head index, and steep
+    heads skip most of their negligible tiles); the XCD placement keeps every item."""
+    monkeypatch.setenv("PA_PREFILL_XCD_ORDER", "0")
+    items = _plan_named("prefill_alibi_f16")["prefill_items"]
+    keys = [(-it[6], -it[1]) for it in items]
+    assert keys == sorted(keys)
+    monkeypatch.delenv("PA_PREFILL_XCD_ORDER")
+    placed = [it for it in _plan_named("prefill_alibi_f16")["prefill_items"] if it[7] != 0]
+    assert sorted(map(tuple, placed)) == sorted(map(tuple, items))
+
+
 def test_single_round_prefill_pairs_heavy_with_light():
     """When an XCD's list fits one round (33..64 workgroups for its 32 CUs), positions k
     and k + 32 share a CU: the first 32 are the heaviest, heaviest first, and the rest
