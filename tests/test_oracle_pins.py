@@ -619,3 +619,39 @@ def test_merge_partials_equals_unsplit():
     out, lse = oracle.merge_partials(outs, lses)
     _same(out, full[0])
     _same(lse, full[1])
+
+
+def test_merge_partials_skips_chunks_a_row_cannot_see():
+    """Causal split where some chunks lie wholly past a row's position: those
+    partials are empty (out 0, lse +inf, the empty-row convention) and must drop
+    out of the merge; rows that see no key at all stay out 0 / lse +inf.  The
+    merge must still reproduce the unsplit result (softmaxLse decomposition,
+    aclnnFusedInferAttentionScoreV3, Constraints)."""
+    rng = np.random.default_rng([314, 91])
+    kv, nq, H, D = 29, 31, 2, 5          # positions -2 .. 28: rows 0 and 1 see no key
+    q = rng.standard_normal((nq, H, D))
+    k = rng.standard_normal((kv, H, D))
+    v = rng.standard_normal((kv, H, D))
+    pos = oracle.query_positions(nq, kv)
+    full = oracle.attention_contiguous(q, k, v, pos, MASK_CAUSAL, 0.6, H, H)
+    cuts = [0, 10, 26, 27, 29]
+    outs, lses = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, l = oracle.attention_contiguous(q, k[a:b], v[a:b], pos - a, MASK_CAUSAL, 0.6, H, H)
+        outs.append(o)
+        lses.append(l)
+    # the chunks past a row's position really are empty partials for that row
+    assert np.all(np.isinf(lses[3][: nq - 2]) & (lses[3][: nq - 2] > 0))   # p <= 26
+    assert np.all(outs[3][: nq - 2] == 0.0)
+    assert np.all(np.isinf(lses[2][: nq - 3]))                             # p <= 25
+    assert np.all(np.isfinite(lses[2][nq - 3:]))
+    out, lse = oracle.merge_partials(outs, lses)
+    assert np.all(np.isfinite(out))
+    assert np.all(out[:2] == 0.0) and np.all(lse[:2] == np.inf)
+    _same(out, full[0])
+    _same(lse, full[1])
+    # a single live partial merged with empty ones is returned unchanged
+    live = np.isfinite(lses[0])
+    o1, l1 = oracle.merge_partials([outs[0], np.zeros_like(outs[0])],
+                                   [lses[0], np.full_like(lses[0], np.inf)])
+    assert np.array_equal(o1[live], outs[0][live]) and np.array_equal(l1[live], lses[0][live])
