@@ -1,30 +1,34 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--copy-probe MiB]
+                    [--kv-layout bnbsh|bnnbsd] [--no-cpu-baseline] [--copy-probe MiB]
 
-A step is one execute of the planned operator (pa_paged_attention): every kernel of
-the path over one batch of seeded synthetic inputs already resident in HBM.  The K
-timed steps are captured into one HIP graph and replayed as a single launch (the
-replay is checked bit for bit against the eager result); the same K steps launched
-one by one from the host are reported as ``ms_per_step_eager``.  The plan
-(phase 1) is made once before timing; its host time is reported as ``plan_us``; the
-op's first execute (inside the warmup) copies its work lists to the device.  Without
---warmup, the untimed warmup runs for WARMUP_SECONDS (at least 10 steps) so that the
-GPU clock has ramped up; the count run is reported as "warmup".  Prints ONE JSON line.
+A step is one execute of the planned operator (pa_paged_attention): the copy of its
+work lists into the workspace and every kernel of the path, over one batch of seeded
+synthetic inputs already resident in HBM.  The K timed steps are captured into one HIP
+graph and replayed as a single launch (the replay is checked bit for bit against the
+eager result); the same K steps launched one by one from the host are reported as
+``ms_per_step_eager``.  Without --warmup, the untimed warmup runs for WARMUP_SECONDS
+(at least 10 steps) so that the GPU clock has ramped up.  Prints ONE JSON line.
 
-Default workload: causal prefill, bf16, B=4, seqLen=kvSeqLen=512, H=32, Hkv=8,
-D=128, blockSize=128 ("prefill_causal_bf16").  --workload picks another of the
-named workloads in paged_kv_cache_314_amd.workloads.
+Default (no --workload): the metric on the largest single-GPU configurations.  The
+headline ``value`` is the batched decode (bf16, B=64, kvSeqLen ~ U[1024, 8192], H=32,
+Hkv=8, D=128, blockSize=128, lse; "decode_bf16_batched") in GB/s; the same line
+carries, under ``workloads``, the ALiBi prefix prefill (fp16, B=8, 512 new tokens over
+2560, H=Hkv=32; "prefill_alibi_f16") in TFLOP/s and the long INT8-KV decode (B=32,
+kvSeqLen=16384, H=64, Hkv=8; "decode_int8_long") in GB/s in both cache layouts, each
+with its own roofline and CPU baseline.  --workload NAME measures one named workload.
 
 Throughput: prefill workloads report algorithmic TFLOP/s (4*D flops per visible
 (query, key) pair, exact causal count); decode workloads report algorithmic GB/s
 (K/V bytes of the valid tokens + Q + out + lse + used block-table entries +
-antiquant scales).  ``roofline`` covers the main kernel alone, timed with HIP
-events recorded on its launch stream around each of K launches made right after the
+antiquant scales).  ``roofline`` covers the op's kernels (decode: the decode kernel and
+the split-KV combine; prefill: the prefill kernel), timed with HIP events attached to
+the first kernel's dispatch and the last one's, over K executes made right after the
 warmup (mean, and p10 / median / p90), back to back (warm caches) and, under
-``roofline.cold``, after a 1 GiB read before each launch (cold caches); prefill is
-also given against the HBM roof under ``roofline.hbm_view``.
+``roofline.cold``, after a 1 GiB read before each execute (cold caches); prefill is
+also given against the HBM roof under ``roofline.hbm_view``, and with the MFMA work
+the kernel executed (from rocprofv3 counters) under ``roofline.executed``.
 """
 
 import argparse
@@ -53,7 +57,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=-1,
                     help="untimed warmup steps; default: as many as fill %.1f s (at least 10), "
                          "so that the GPU clock has ramped up before timing" % WARMUP_SECONDS)
-    ap.add_argument("--workload", default="prefill_causal_bf16")
+    ap.add_argument("--workload", default=None,
+                    help="measure one named workload (default: the batched decode as the "
+                         "headline, with the ALiBi prefix prefill and the long INT8-KV decode "
+                         "in both cache layouts in the same line)")
     ap.add_argument("--kv-layout", choices=["bnbsh", "bnnbsd"], default="bnbsh",
                     help="K/V pool memory layout: (block, slot, kv head, d) as the workload "
                          "defines it, or (block, kv head, slot, d) passed as a strided view")
@@ -104,11 +111,10 @@ def algorithmic_counts(inp):
     return nbytes, flops
 
 
-def traffic_from_profiles(workload, kind):
-    """HBM bytes per launch measured with rocprofv3 counters, if a summary for this
-    workload exists and was taken on the current kernel source; else None."""
+def counters_from_profiles(workload, kernel):
+    """The rocprofv3 counter summary of ``kernel`` on ``workload`` under profiles/, if
+    one exists and was taken on the current kernel sources; else None."""
     from paged_kv_cache_314_amd.counter_summary import kernel_source_hash
-    kernel = f"{kind}_kernel"
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
     if not os.path.exists(path):
         return None
@@ -119,7 +125,20 @@ def traffic_from_profiles(workload, kind):
         return None
     if d.get("source_sha256_16") != kernel_source_hash(kernel):
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
+
+
+def traffic_from_profiles(workload, kernels):
+    """HBM bytes per execute measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE),
+    summed over ``kernels``, if every summary exists and was taken on the current
+    kernel sources; else None."""
+    total = 0.0
+    for k in kernels:
+        d = counters_from_profiles(workload, k)
+        if d is None or d.get("hbm_bytes_per_launch") is None:
+            return None
+        total += d["hbm_bytes_per_launch"]
+    return total
 
 
 # ------------------------------------------------------------ cpu baseline
@@ -186,14 +205,16 @@ def cpu_baseline(inp, nbytes, flops, decode, budget_s):
     dt = time.perf_counter() - t0
     frac = done_units / total_units if total_units else 1.0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cores = len(os.sched_getaffinity(0))
     if decode:
         value, unit = nbytes * frac / dt / 1e9, "GB/s"
     else:
         value, unit = flops * frac / dt / 1e12, "TFLOP/s"
-    return {"value": value, "unit": unit, "cores": int(threads), "kind": "oracle",
+    return {"value": value, "unit": unit, "cores": int(min(threads, cores)), "kind": "oracle",
+            "host_cores": cores, "blas_threads": int(threads),
             "sample": f"{nseq} sequences (all heads) taken in order from the step's "
-                      f"{len(ql)}, {frac:.3f} times the step's work, {dt:.1f} s, fp64 NumPy, "
-                      f"BLAS threads {threads}"}
+                      f"{len(ql)}, {frac:.3f} times the step's work, {dt:.1f} s, fp64 NumPy "
+                      f"(BLAS threads {threads} on {cores} host cores)"}
 
 
 def warmup(args, step):
@@ -234,12 +255,17 @@ def bench_append(args, w, dev):
         vc = vc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     table = inp["block_tables"].to(dev)
     nbytes = 2 * 2 * kn.numel() * kn.element_size()
+    pa.load()
+    first = pa.pa_kv_cache_append_plan(kn, vn, kc, vc, table, inp["seq_len"], inp["kv_seq_len"])
+    first.destroy()
     t_plan = time.perf_counter()
     op = pa.pa_kv_cache_append_plan(kn, vn, kc, vc, table, inp["seq_len"], inp["kv_seq_len"])
     plan_us = (time.perf_counter() - t_plan) * 1e6
     info = pa.pa_op_describe(op)
     stream = torch.cuda.current_stream()
-    args.warmup = warmup(args, lambda: pa.pa_kv_cache_append(op, stream))
+    ws = pa.alloc_workspace(op.workspace_size, dev)
+    run = lambda st: pa.pa_kv_cache_append(ws, op.workspace_size, op, st)
+    args.warmup = warmup(args, lambda: run(stream))
     # kernel events first after the warmup, then the graph-timed steps, then eager (as
     # for the attention workloads)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -249,7 +275,7 @@ def bench_append(args, w, dev):
     torch.cuda.synchronize()
     for s_ev, e_ev in zip(starts, stops):
         pa.pa_op_set_timing_events(op, s_ev, e_ev)
-        pa.pa_kv_cache_append(op, stream)
+        run(stream)
     pa.pa_op_set_timing_events(op, None, None)
     torch.cuda.synchronize()
     kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, stops)) / args.steps
@@ -258,7 +284,7 @@ def bench_append(args, w, dev):
     with torch.cuda.graph(graph):
         cap = torch.cuda.current_stream()
         for _ in range(args.steps):
-            pa.pa_kv_cache_append(op, cap)
+            run(cap)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     graph.replay()
@@ -269,12 +295,13 @@ def bench_append(args, w, dev):
     del graph, ref_k, ref_v
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        pa.pa_kv_cache_append(op, stream)
+        run(stream)
     torch.cuda.synchronize()
     ms_per_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profiles(args.workload, "append"),
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic_from_profiles(args.workload, ["append_kernel"]),
             "kernel": "append_kernel", "kernel_us": kernel_ms * 1e3, "algorithmic_bytes": nbytes,
             "algorithmic_flops": 0}
     cpu = None
@@ -296,6 +323,7 @@ def bench_append(args, w, dev):
         dt = time.perf_counter() - tc
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
         cpu = {"value": reps * nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "host_cores": len(os.sched_getaffinity(0)), "blas_threads": int(threads),
                "sample": f"the whole append (K and V, {len(ql)} sequences) {reps} times, "
                          f"{dt:.1f} s, NumPy row copies (one thread; BLAS threads {threads} "
                          f"unused)"}
@@ -344,43 +372,114 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": max(args.steps, 1)}))
         return
 
-    w = wl.WORKLOADS[args.workload]
-    if w.op == "append":
-        return bench_append(args, w, dev)
+    if args.workload is not None and wl.WORKLOADS[args.workload].op == "append":
+        return bench_append(args, wl.WORKLOADS[args.workload], dev)
+    if args.workload is not None:
+        r = measure(args, args.workload, args.kv_layout, dev,
+                    None if args.no_cpu_baseline else args.cpu_seconds)
+        print(json.dumps(headline(args, r)), flush=True)
+        return
+    # default: the batched decode is the headline; the ALiBi prefix prefill and the long
+    # INT8-KV decode (both cache layouts) ride along in the same line
+    cpu = lambda t: None if args.no_cpu_baseline else t
+    head = measure(args, HEADLINE, "bnbsh", dev, cpu(args.cpu_seconds))
+    line = headline(args, head)
+    line["workloads"] = {}
+    for name, layout in ALSO:
+        r = measure(args, name, layout, dev, cpu(SECONDARY_CPU_SECONDS))
+        key = name if layout == "bnbsh" else f"{name}@{layout}"
+        line["workloads"][key] = {k: r[k] for k in (
+            "value", "unit", "ms_per_step", "ms_per_step_eager", "dtype", "config", "plan_us",
+            "plan_us_first", "roofline", "cpu_baseline")}
+    print(json.dumps(line), flush=True)
+
+
+HEADLINE = "decode_bf16_batched"
+ALSO = [("prefill_alibi_f16", "bnbsh"), ("decode_int8_long", "bnbsh"),
+        ("decode_int8_long", "bnnbsd")]
+SECONDARY_CPU_SECONDS = 5.0
+
+
+def headline(args, r):
+    """The driver's JSON line for one measured workload ``r``."""
+    return {
+        "metric": "decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), paged attention",
+        "value": r["value"],
+        "unit": r["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": r["warmup"],
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "launch": "one HIP graph of the K steps",
+        "ms_per_step_eager": r["ms_per_step_eager"],
+        "dtype": r["dtype"],
+        "data": "synthetic",
+        "config": r["config"],
+        "plan_us": r["plan_us"],
+        "plan_us_first": r["plan_us_first"],
+        "roofline": r["roofline"],
+        "cpu_baseline": r["cpu_baseline"],
+    }
+
+
+def measure(args, name, layout, dev, cpu_seconds):
+    """Plan, warm up and time workload ``name`` (K graph-replayed steps, K eager steps,
+    K event-timed executes warm and up to 20 cold); returns its figures."""
+    import torch
+
+    import paged_kv_cache_314_amd as pa
+    from paged_kv_cache_314_amd import workloads as wl
+
+    w = wl.WORKLOADS[name]
     decode = w.seq_len == "decode"
     kind = "decode" if decode else "prefill"
     inp = wl.make_inputs(w, poison=False)
     nbytes, flops = algorithmic_counts(inp)
     g = {key: (val.to(dev) if isinstance(val, torch.Tensor) and key not in ("seq_len", "kv_seq_len")
                else val) for key, val in inp.items()}
-    if args.kv_layout == "bnnbsd":
+    if layout == "bnnbsd":
         for key in ("key", "value"):
             g[key] = g[key].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     out = torch.empty_like(g["query"])
     lse = (torch.empty((out.shape[0], w.head_num), dtype=torch.float32, device=dev)
            if w.lse else None)
 
+    def plan():
+        return pa.pa_paged_attention_get_workspace_size_ex(
+            g["query"], g["key"], g["value"], g["block_tables"], None, g["seq_len"],
+            g["kv_seq_len"], g["slopes"], g["mask_type"], g["head_num"], g["kv_head_num"],
+            g["qk_scale"], g["key_scale"], g["value_scale"], g.get("key_offset"),
+            g.get("value_offset"), g.get("key_mode", 0), g.get("value_mode", 0), out, lse)
+
+    # phase 1 twice: the first call (library already loaded) may take a fresh pinned
+    # buffer for the work lists; the second, warm one is what a serving loop pays per step
+    pa.load()
     t_plan = time.perf_counter()
-    op = pa.pa_paged_attention_get_workspace_size_ex(
-        g["query"], g["key"], g["value"], g["block_tables"], None, g["seq_len"],
-        g["kv_seq_len"], g["slopes"], g["mask_type"], g["head_num"], g["kv_head_num"],
-        g["qk_scale"], g["key_scale"], g["value_scale"], g.get("key_offset"),
-        g.get("value_offset"), g.get("key_mode", 0), g.get("value_mode", 0), out, lse)
+    first = plan()
+    plan_us_first = (time.perf_counter() - t_plan) * 1e6
+    first.destroy()
+    t_plan = time.perf_counter()
+    op = plan()
     plan_us = (time.perf_counter() - t_plan) * 1e6
     ws = pa.alloc_workspace(op.workspace_size, dev)
     info = pa.pa_op_describe(op)
     stream = torch.cuda.current_stream()
+    run = lambda st: pa.pa_paged_attention(ws, op.workspace_size, op, st)
 
-    args.warmup = warmup(args, lambda: pa.pa_paged_attention(ws, op.workspace_size, op, stream))
+    n_warm = warmup(args, lambda: run(stream))
 
     # the warmup's result: every later execute must reproduce it bit for bit
     torch.cuda.synchronize()
     ref_out = out.clone()
     ref_lse = lse.clone() if lse is not None else None
 
-    # main-kernel duration: HIP events recorded around each launch on its stream, taken
-    # first after the warmup (the GPU's clock drifts under long runs of back-to-back
-    # launches; rocprofv3's kernel averages of the same command are taken in this state)
+    # kernel duration: HIP events attached to the dispatch of the op's first kernel and
+    # its last one, taken first after the warmup (the GPU's clock drifts under long runs
+    # of back-to-back launches; rocprofv3's kernel averages of the same command are taken
+    # in this state)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for e in starts + stops:
@@ -388,19 +487,19 @@ def main():
     torch.cuda.synchronize()
     for s_ev, e_ev in zip(starts, stops):
         pa.pa_op_set_timing_events(op, s_ev, e_ev)
-        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+        run(stream)
     pa.pa_op_set_timing_events(op, None, None)
     torch.cuda.synchronize()
     kms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
     kernel_ms = sum(kms) / len(kms)
 
     # timed region: K whole steps, captured once into a HIP graph and replayed as one
-    # launch (no host work between steps); the captured executes hold no memset
+    # launch (no host work between steps)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         cap = torch.cuda.current_stream()
         for _ in range(args.steps):
-            pa.pa_paged_attention(ws, op.workspace_size, op, cap)
+            run(cap)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     graph.replay()
@@ -408,19 +507,19 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     if not torch.equal(out, ref_out) or (lse is not None and not torch.equal(lse, ref_lse)):
-        raise RuntimeError("graph replay of the execute differs from the eager result")
+        raise RuntimeError(f"{name}: graph replay of the execute differs from the eager result")
     del graph
 
     # the same K steps launched one by one from the host (reported beside the graph)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+        run(stream)
     torch.cuda.synchronize()
     ms_per_step_eager = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # the same kernel from cold caches: a read of a FLUSH_MIB buffer (larger than the
-    # 256 MB Infinity Cache and the L2s together) runs on the stream before each launch
+    # the same kernels from cold caches: a read of a FLUSH_MIB buffer (larger than the
+    # 256 MB Infinity Cache and the L2s together) runs on the stream before each execute
     nc = min(args.steps, 20)
     flush = torch.ones(FLUSH_MIB << 18, dtype=torch.float32, device=dev)
     cstarts = [torch.cuda.Event(enable_timing=True) for _ in range(nc)]
@@ -431,12 +530,14 @@ def main():
     for s_ev, e_ev in zip(cstarts, cstops):
         flush.sum()
         pa.pa_op_set_timing_events(op, s_ev, e_ev)
-        pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+        run(stream)
     pa.pa_op_set_timing_events(op, None, None)
     torch.cuda.synchronize()
     cold_ms = sum(s.elapsed_time(e) for s, e in zip(cstarts, cstops)) / nc
     del flush
 
+    has_combine = len(info["combine_items"]) > 0
+    kernels = [f"{kind}_kernel"] + (["combine_kernel"] if has_combine else [])
     if decode:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
@@ -452,8 +553,9 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
         dtype = w.dtype
-    roof["traffic"] = traffic_from_profiles(args.workload, kind)
-    roof["kernel"] = f"{kind}_kernel"
+    roof["traffic"] = traffic_from_profiles(name if layout == "bnbsh" else f"{name}@{layout}",
+                                            kernels)
+    roof["kernel"] = "+".join(kernels)
     roof["kernel_us"] = kernel_ms * 1e3
     qs = sorted(kms)
     pick = lambda f: qs[int(round(f * (len(qs) - 1)))] * 1e3
@@ -461,7 +563,7 @@ def main():
     work = nbytes / 1e9 if decode else flops / 1e12
     roof["cold"] = {"kernel_us": cold_ms * 1e3, "achieved": work / (cold_ms * 1e-3),
                     "frac": work / (cold_ms * 1e-3) / roof["peak"], "launches": nc,
-                    "flush": f"read of {FLUSH_MIB} MiB before each launch"}
+                    "flush": f"read of {FLUSH_MIB} MiB before each execute"}
     if not decode:
         # the same launch against the HBM roof: a prefill whose flops per algorithmic
         # byte fall below the ridge (2.5 PFLOP/s / 8 TB/s = 312.5) is bound by HBM first
@@ -471,43 +573,39 @@ def main():
                             "frac": hbm / PEAK_HBM_GBS, "flop_per_byte": ai,
                             "ridge_flop_per_byte": peak * 1e12 / (PEAK_HBM_GBS * 1e9),
                             "roof_tflops": min(peak, ai * PEAK_HBM_GBS / 1e3)}
+        # the MFMA work the kernel executed (it skips the P V of tiles whose weights are
+        # negligible under ALiBi, and adds the rank-1 bias products), from counters
+        sq = counters_from_profiles(name, "prefill_kernel")
+        if sq is not None and sq.get("mfma_flops_per_launch"):
+            ex = sq["mfma_flops_per_launch"]
+            roof["executed"] = {"flops": ex, "algorithmic_flops": flops, "ratio": ex / flops,
+                                "achieved": ex / (kernel_ms * 1e-3) / 1e12,
+                                "frac": ex / (kernel_ms * 1e-3) / 1e12 / peak,
+                                "mfma_busy_frac": sq.get("mfma_busy_frac"),
+                                "source": "rocprofv3 SQ counters under profiles/"}
+        else:
+            roof["executed"] = None
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, nbytes, flops, decode, args.cpu_seconds)
-
-    result = {
-        "metric": "decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), paged attention",
-        "value": value,
-        "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "launch": "one HIP graph of the K steps",
-        "ms_per_step_eager": ms_per_step_eager,
-        "dtype": dtype,
-        "data": "synthetic",
+    if cpu_seconds is not None:
+        cpu = cpu_baseline(inp, nbytes, flops, decode, cpu_seconds)
+    op.destroy()
+    return {
+        "value": value, "unit": unit, "warmup": n_warm, "ms_per_step": ms_per_step,
+        "ms_per_step_eager": ms_per_step_eager, "dtype": dtype, "plan_us": plan_us,
+        "plan_us_first": plan_us_first, "roofline": roof, "cpu_baseline": cpu,
         "config": {
-            "workload": args.workload, "mode": kind, "batch": w.batch,
+            "workload": name, "mode": kind, "batch": w.batch,
             "head_num": w.head_num, "kv_head_num": w.kv_head_num, "head_size": w.head_size,
             "block_size": w.block_size, "q_dtype": w.dtype, "kv_dtype": w.kv_dtype,
-            "mask_type": w.mask_type, "lse": w.lse, "kv_layout": args.kv_layout,
+            "mask_type": w.mask_type, "lse": w.lse, "kv_layout": layout,
             "parallelism": "single GPU",
             "work_items": len(info["decode_items"]) + len(info["prefill_items"]),
             "combine_items": len(info["combine_items"]),
         },
-        "plan_us": plan_us,
-        "roofline": roof,
-        "cpu_baseline": cpu,
     }
-    op.destroy()
-    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

@@ -16,19 +16,24 @@
  * Two-phase call, as the pages' operator APIs (PrefixEncoder, Definition; the
  * "GetWorkspaceSize then execute" pattern of aclnnFusedInferAttentionScoreV3/V4):
  *   1. pa_paged_attention_get_workspace_size(...) validates every argument, plans the
- *      work and returns the device workspace size plus an operator handle.  It makes no
- *      HIP call and touches no device memory.
- *   2. pa_paged_attention(workspace, size, op, stream) enqueues the kernels on `stream`.
+ *      work for the current device and returns the device workspace size plus an
+ *      operator handle.  It touches no device memory; its HIP calls are device queries
+ *      (the current device's compute-unit count) and, on a host with a device, a pinned
+ *      host buffer for the op's work lists (taken from a pool that pa_op_destroy
+ *      refills, so steady-state planning allocates nothing).
+ *   2. pa_paged_attention(workspace, size, op, stream) enqueues the copy of the work
+ *      lists into the workspace and the kernels on `stream`; it allocates nothing and
+ *      never waits.
  *
  * Conventions shared by every entry point
  *   - Tensors are described by pa_tensor (data pointer, dtype, shape, strides in
  *     elements).  The innermost dimension must be contiguous; see each argument.
  *   - "device" = HIP device memory (e.g. a torch CUDA tensor on ROCm);
  *     "host" = ordinary CPU memory.
- *   - The caller owns every tensor and the workspace.  The library owns the pa_op and
- *     allocates only for it: the op's work lists (a few KB, 32 bytes per workgroup) in
- *     pinned host memory and, from its first execution, a device copy of them; both
- *     are released by pa_op_destroy.
+ *   - The caller owns every tensor and the workspace; the library never allocates device
+ *     memory.  The library owns the pa_op: its plan and a pinned host copy of its work
+ *     lists (32 or 48 bytes per workgroup), which each execute copies into the head of
+ *     the workspace before its kernels run.
  *   - Tensors and the workspace must stay alive, and must not be written by others,
  *     until the work enqueued by pa_paged_attention has completed on the stream.
  *   - Block ids in blockTables are not validated (aclnnFusedInferAttentionScoreV3,
@@ -211,19 +216,17 @@ pa_status pa_paged_attention_get_workspace_size_ex(
  * stream).  (PrefixEncoder, Definition: AtbSelfAttentionPrefixEncoder; the pages'
  * context argument becomes a HIP stream.)  workspace: device memory of at least the
  * phase-1 size, 256-byte aligned, or NULL if that size is 0; its contents on entry do
- * not matter and are scratch afterwards (it holds split-KV partial results; the size is
- * 0 when no sequence is split).  The call returns once the work is enqueued.  The first
- * call on an op copies its work lists into a small device buffer of the op on `stream`
- * and waits for `stream` once (every later call only enqueues); the op is then bound to
- * that stream's device, and a call on another device returns PA_ERR_PARAM_INVALID.  If
- * the first call is made while `stream` is being captured into a graph, the op instead
- * reads its work lists from pinned host memory over the bus on every run (no copy, no
- * wait, no device binding; about a microsecond more per kernel).
- * An op may be executed any number of times, on any stream of its device; two
+ * not matter and are scratch afterwards.  It holds the op's work lists (copied in by an
+ * asynchronous host-to-device copy from the op's pinned buffer, enqueued on `stream`
+ * ahead of the kernels) and, when sequences are split, the split-KV partial results.
+ * The call only enqueues: no allocation, no wait, so it may be captured into a graph
+ * (the copy becomes a graph node that reads the op's pinned buffer on every replay;
+ * such a graph must not be replayed after pa_op_destroy).
+ * An op may be executed any number of times, on any stream of any device; two
  * executions must not share a workspace while both are in flight.
  * Returns PA_ERR_NULLPTR (op, or a needed workspace, is NULL), PA_ERR_WORKSPACE_TOO_SMALL,
- * PA_ERR_PARAM_INVALID (workspace not 256-byte aligned, or another device than the
- * first run's) or PA_ERR_HIP on failure.
+ * PA_ERR_PARAM_INVALID (workspace not 256-byte aligned) or PA_ERR_HIP on failure (also
+ * for an op planned on a host without a HIP device, which holds no pinned lists).
  */
 pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
                              void* stream);
@@ -252,40 +255,74 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
  *                    call); the slots written must not be shared by two sequences.
  * seqLen, kvSeqLen   HOST, [batch] int32, 0 <= seqLen[b] <= kvSeqLen[b],
  *                    sum(seqLen) = nTokens.
+ * workspaceSize      out: device workspace bytes pa_kv_cache_append needs (its work list,
+ *                    16 new tokens per 32-byte item; 0 for a no-op).
  * op                 out: handle (pa_op_destroy releases it); nTokens == 0 gives a no-op.
- * Phase 1 makes no HIP call.  pa_kv_cache_append enqueues the copy on `stream` (NULL =
- * the null stream); it may be run again, e.g. after the new rows were refilled in place.
- * Its work lists are handled as for pa_paged_attention (device copy made on the first run).
+ * Planning is done as for pa_paged_attention_get_workspace_size (same HIP calls).
+ * pa_kv_cache_append enqueues the copy of the work list into `workspace` (256-byte
+ * aligned device memory of at least workspaceSize bytes, scratch afterwards) and the
+ * copy kernel on `stream` (NULL = the null stream); it allocates nothing and never waits,
+ * and may be run again, e.g. after the new rows were refilled in place.
  * pa_paged_attention rejects an append op and pa_kv_cache_append an attention op
  * (PA_ERR_PARAM_INVALID).  pa_op_set_timing_events applies to the copy kernel.
  */
 pa_status pa_kv_cache_append_plan(const pa_tensor* keyNew, const pa_tensor* valueNew,
                                   const pa_tensor* keyCache, const pa_tensor* valueCache,
                                   const pa_tensor* blockTables, const pa_tensor* seqLen,
-                                  const pa_tensor* kvSeqLen, pa_op** op);
-pa_status pa_kv_cache_append(pa_op* op, void* stream);
+                                  const pa_tensor* kvSeqLen, uint64_t* workspaceSize,
+                                  pa_op** op);
+pa_status pa_kv_cache_append(void* workspace, uint64_t workspaceSize, pa_op* op, void* stream);
 
-/* Release an operator handle (NULL is ignored).  Work already enqueued is unaffected: the
- * call blocks until the kernels of the op's last run have finished (they read the op's
- * work lists from its host buffer). */
+/* Release an operator handle (NULL is ignored).  Work already enqueued is unaffected and
+ * the call does not wait for it: the op's pinned work-list buffer goes back to the
+ * library's pool and is handed to a new op only after the copies enqueued from it have
+ * run. */
 void pa_op_destroy(pa_op* op);
 
+/* Plan options: overrides of the planner's automatic choices, for tuning and tests.
+ * Process-wide; they apply to ops planned after the call.  value -1 restores the
+ * automatic choice (the default for every option).
+ *   PA_OPT_DECODE_CHUNK_TILES   32-token tiles per decode work item (1 .. 2^20)
+ *   PA_OPT_DECODE_TARGET_ITEMS  decode workgroups the split aims for (1 .. 2^20)
+ *   PA_OPT_DECODE_WAVE_HEADS    0 / 1: decode items of four kv heads, one per wave
+ *   PA_OPT_PREFILL_PAIR         0 / 1: heavy + light prefill items sharing a CU
+ *   PA_OPT_PREFILL_XCD_ORDER    0 / 1: prefill items grouped per XCD
+ *   PA_OPT_COMPUTE_UNITS        compute units to plan for (1 .. 2^20; default: the
+ *                               current device's, 256 when no device can be queried)
+ * The decode options change how sequences are split, and with it the order of the
+ * floating-point sums: results stay within the stated tolerances but their bits
+ * change.  The determinism promise (same call, same inputs -> same bits) holds for
+ * ops planned with the same options on the same device.  Returns PA_ERR_PARAM_INVALID
+ * for an unknown option or a value out of range. */
+enum {
+    PA_OPT_DECODE_CHUNK_TILES = 1,
+    PA_OPT_DECODE_TARGET_ITEMS = 2,
+    PA_OPT_DECODE_WAVE_HEADS = 3,
+    PA_OPT_PREFILL_PAIR = 4,
+    PA_OPT_PREFILL_XCD_ORDER = 5,
+    PA_OPT_COMPUTE_UNITS = 6
+};
+pa_status pa_set_plan_option(int option, int32_t value);
+/* The option's current value (-1: automatic, or an unknown option). */
+int32_t pa_get_plan_option(int option);
+
 /* Instrumentation: start and stop are hipEvent_t handles (or NULL to clear), created with
- * timing enabled.  While set, each pa_paged_attention on this op attaches them to the
- * dispatch of its main kernel (the decode kernel or the prefill kernel), so that
- * hipEventElapsedTime(start, stop) is that kernel's own duration.  The events stay owned
- * by the caller.  Host only; returns PA_ERR_NULLPTR if op is NULL. */
+ * timing enabled.  While set, each execute of this op attaches start to the dispatch of
+ * its main kernel (the decode, prefill or append kernel) and stop to its last kernel
+ * (the split-KV combine when there is one), so that hipEventElapsedTime(start, stop) is
+ * the duration of the op's kernels, without the copy of the work lists.  The events
+ * stay owned by the caller.  Host only; returns PA_ERR_NULLPTR if op is NULL. */
 pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop);
 
 /* Write a JSON description of the operator's plan into buf (NUL-terminated, cut at
  * cap - 1 bytes; buf may be NULL when cap is 0) and return the full length without the
  * NUL.  Keys: "mode" ("noop", "fill", "decode", "prefill", "append"), "workspace_bytes",
- * "chunk_tiles", "partial_slots", and the work lists "decode_items"
+ * "items_bytes" (the work lists at the head of the workspace), "compute_units" (planned
+ * for), "chunk_tiles", "partial_slots", and the work lists "decode_items"
  * [b, kvh, hg, t0, t1, slot, qrow, kvlen], "combine_items" [kvh, hg, slot0, nsplit, qrow],
  * "prefill_items" [b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads] (heads query heads from
  * h, 128/heads query rows from qbeg), "append_items" [b, row0, pos0, count], "antiquant"
- * [key mode, value mode, offsets given], "work_lists" ("none" before the first run,
- * then "device" or "host").  Host only, no HIP call.
+ * [key mode, value mode, offsets given].  Host only, no HIP call.
  * For inspection and tests: not a stable interface.  op == NULL returns 0. */
 uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap);
 

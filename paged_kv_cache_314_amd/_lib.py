@@ -25,6 +25,8 @@ PA_ERR_HOST_ALLOC = 6
 PA_F16, PA_BF16, PA_I8, PA_F32, PA_I32, PA_F8E4M3 = 1, 2, 3, 4, 5, 6
 PA_MASK_NONE, PA_MASK_ALIBI, PA_MASK_CAUSAL = 0, 3, 9
 PA_ANTIQUANT_PER_CHANNEL, PA_ANTIQUANT_PER_TOKEN = 0, 1
+(PA_OPT_DECODE_CHUNK_TILES, PA_OPT_DECODE_TARGET_ITEMS, PA_OPT_DECODE_WAVE_HEADS,
+ PA_OPT_PREFILL_PAIR, PA_OPT_PREFILL_XCD_ORDER, PA_OPT_COMPUTE_UNITS) = range(1, 7)
 
 _DTYPE_CODE = {
     torch.float16: PA_F16,
@@ -44,6 +46,8 @@ EXPORTED = (
     "pa_op_destroy",
     "pa_op_describe",
     "pa_op_set_timing_events",
+    "pa_set_plan_option",
+    "pa_get_plan_option",
     "pa_status_string",
     "pa_last_error",
     "pa_version",
@@ -99,9 +103,15 @@ def load():
     lib.pa_paged_attention.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                        ctypes.c_void_p]
     lib.pa_kv_cache_append_plan.restype = ctypes.c_int
-    lib.pa_kv_cache_append_plan.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pa_kv_cache_append_plan.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_uint64),
+                                            ctypes.POINTER(ctypes.c_void_p)]
     lib.pa_kv_cache_append.restype = ctypes.c_int
-    lib.pa_kv_cache_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_kv_cache_append.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.pa_set_plan_option.restype = ctypes.c_int
+    lib.pa_set_plan_option.argtypes = [ctypes.c_int, ctypes.c_int32]
+    lib.pa_get_plan_option.restype = ctypes.c_int32
+    lib.pa_get_plan_option.argtypes = [ctypes.c_int]
     lib.pa_op_destroy.restype = None
     lib.pa_op_destroy.argtypes = [ctypes.c_void_p]
     lib.pa_op_set_timing_events.restype = ctypes.c_int
@@ -254,20 +264,24 @@ def pa_kv_cache_append_plan(key_new, value_new, key_cache, value_cache, block_ta
              describe(key_cache, device="cuda"), describe(value_cache, device="cuda"),
              describe(block_tables, device="cuda"), describe(seq_len, device="cpu"),
              describe(kv_seq_len, device="cpu")]
+    ws = ctypes.c_uint64(0)
     handle = ctypes.c_void_p(None)
-    _check(lib.pa_kv_cache_append_plan(*[_ref(d) for d in descs], ctypes.byref(handle)))
+    _check(lib.pa_kv_cache_append_plan(*[_ref(d) for d in descs], ctypes.byref(ws),
+                                       ctypes.byref(handle)))
     keep = (key_new, value_new, key_cache, value_cache, block_tables, seq_len, kv_seq_len)
-    return Op(handle.value, 0, keep)
+    return Op(handle.value, int(ws.value), keep)
 
 
-def pa_kv_cache_append(op, stream=None):
-    """Enqueue a planned KV-cache append on ``stream`` (None = torch's current stream)."""
+def pa_kv_cache_append(workspace, workspace_size, op, stream=None):
+    """Enqueue a planned KV-cache append on ``stream`` (None = torch's current stream).
+    ``workspace`` is a uint8 CUDA tensor of at least ``workspace_size`` bytes, or None."""
     lib = load()
     handle = op.handle if isinstance(op, Op) else op
     if stream is None:
         stream = torch.cuda.current_stream()
     raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
-    _check(lib.pa_kv_cache_append(handle, raw))
+    ptr = workspace.data_ptr() if workspace is not None and workspace.numel() > 0 else None
+    _check(lib.pa_kv_cache_append(ptr, int(workspace_size), handle, raw))
 
 
 def kv_cache_append(key_new, value_new, key_cache, value_cache, block_tables, seq_len,
@@ -276,7 +290,8 @@ def kv_cache_append(key_new, value_new, key_cache, value_cache, block_tables, se
     op = pa_kv_cache_append_plan(key_new, value_new, key_cache, value_cache, block_tables,
                                  seq_len, kv_seq_len)
     try:
-        pa_kv_cache_append(op, stream)
+        ws = alloc_workspace(op.workspace_size, key_cache.device)
+        pa_kv_cache_append(ws, op.workspace_size, op, stream)
     finally:
         torch.cuda.synchronize(key_cache.device)
         op.destroy()
@@ -289,8 +304,37 @@ def pa_op_destroy(op):
         load().pa_op_destroy(op)
 
 
+def pa_set_plan_option(option, value):
+    """Override a planner choice process-wide (PA_OPT_*; -1 restores automatic)."""
+    _check(load().pa_set_plan_option(int(option), int(value)))
+
+
+def pa_get_plan_option(option):
+    return int(load().pa_get_plan_option(int(option)))
+
+
+class plan_options:
+    """Context manager setting plan options for the ops planned inside it:
+    ``with plan_options({PA_OPT_DECODE_CHUNK_TILES: 8}): ...``."""
+
+    def __init__(self, values):
+        self.values = dict(values)
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.values.items():
+            self.saved[k] = pa_get_plan_option(k)
+            pa_set_plan_option(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            pa_set_plan_option(k, v)
+        return False
+
+
 def pa_op_set_timing_events(op, start, stop):
-    """Record torch.cuda.Event ``start``/``stop`` around the op's main kernel (None clears).
+    """Record torch.cuda.Event ``start``/``stop`` around the op's kernels (None clears).
     Events must have been recorded once (torch creates them lazily)."""
     handle = op.handle if isinstance(op, Op) else op
     s = start.cuda_event if start is not None else None

@@ -3,24 +3,32 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "pa_internal.h"
 #include "pa_kernels.h"
 #include "pagedattn.h"
 
+// A pinned host buffer holding an op's work lists, with the event recorded after the last
+// kernel that read a copy of them.  Buffers are drawn from a pool in phase 1 and given
+// back by pa_op_destroy, so steady-state planning allocates nothing.
+struct HostLists {
+    void* ptr = nullptr;
+    uint64_t bytes = 0;
+    hipEvent_t done = nullptr;
+};
+
 struct pa_op {
     pa::Plan plan;
-    void* staging = nullptr;        // pinned, device-mapped work lists (made on first run)
-    unsigned char* staging_dev = nullptr;   // the same memory as seen by the GPU
-    unsigned char* lists_dev = nullptr;     // device copy of the work lists (first run)
-    int lists_device = -1;                  // the device holding lists_dev
-    const unsigned char* lists = nullptr;   // what the kernels read: lists_dev or staging_dev
-    hipEvent_t done = nullptr;      // recorded after the last kernel of each run
-    hipEvent_t t_start = nullptr;   // caller's timing events around the main kernel
+    HostLists lists;                // pinned copy of the plan's work lists (made in phase 1)
+    bool planned_without_device = false;
+    hipEvent_t t_start = nullptr;   // caller's timing events around the op's kernels
     hipEvent_t t_stop = nullptr;
 };
 
@@ -38,73 +46,122 @@ pa_status hip_fail(hipError_t e, const char* what) {
     return fail(PA_ERR_HIP, msg);
 }
 
-// The work lists: each workgroup reads its own 32-byte item at start-up, a dependent load
-// ahead of everything else it does, so they are read from device memory: the first run
-// copies them from a pinned host buffer into a small device buffer of the op, on the
-// caller's stream, and waits for that stream once.  A first run made under stream
-// capture cannot wait; that op then reads the pinned buffer in place over the bus
-// (about 1 us more per launch).  Kernels of later runs on another device are refused.
-pa_status make_host_lists(pa_op* op);
+// ---------------------------------------------------------------- plan options
 
-pa_status ensure_staging(pa_op* op, hipStream_t stream) {
-    const pa::Plan& p = op->plan;
-    if (p.items_bytes == 0) return PA_OK;
-    if (op->lists != nullptr) {
-        if (op->lists_dev == nullptr) return PA_OK;
-        int dev = -1;
-        hipError_t e = hipStreamGetDevice(stream, &dev);
-        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
-        if (dev != op->lists_device)
-            return fail(PA_ERR_PARAM_INVALID, "op was first run on device " +
-                                                  std::to_string(op->lists_device) +
-                                                  ", not on device " + std::to_string(dev));
-        return PA_OK;
+constexpr int kNumOptions = PA_OPT_COMPUTE_UNITS + 1;
+std::atomic<int32_t> g_options[kNumOptions] = {};   // 0 = automatic (the stored value is v + 1)
+
+int32_t option(int opt) { return g_options[opt].load(std::memory_order_relaxed) - 1; }
+
+// compute units of the current device (cached per device); 256, a full MI355X, when no
+// device can be queried (planning on a host without a GPU)
+int32_t device_compute_units() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int32_t> cache[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return 256;
     }
-    pa_status st = make_host_lists(op);
-    if (st != PA_OK) return st;
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    hipError_t e = hipStreamIsCapturing(stream, &cap);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
-    if (cap != hipStreamCaptureStatusNone) {
-        op->lists = op->staging_dev;
-        return PA_OK;
+    if (dev < kMaxDevices) {
+        const int32_t c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
     }
-    int dev = -1;
-    e = hipStreamGetDevice(stream, &dev);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
-    void* d = nullptr;
-    e = hipMalloc(&d, p.items_bytes);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(work lists)");
-    e = hipMemcpyAsync(d, op->staging, p.items_bytes, hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+pa::PlanConfig plan_config() {
+    pa::PlanConfig c;
+    c.compute_units = option(PA_OPT_COMPUTE_UNITS) > 0 ? option(PA_OPT_COMPUTE_UNITS)
+                                                       : device_compute_units();
+    c.decode_chunk_tiles = option(PA_OPT_DECODE_CHUNK_TILES);
+    c.decode_target_items = option(PA_OPT_DECODE_TARGET_ITEMS);
+    c.decode_wave_heads = option(PA_OPT_DECODE_WAVE_HEADS);
+    c.prefill_pair = option(PA_OPT_PREFILL_PAIR);
+    c.prefill_xcd_order = option(PA_OPT_PREFILL_XCD_ORDER);
+    return c;
+}
+
+// ------------------------------------------------------- pinned work-list buffers
+
+std::mutex g_pool_mu;
+std::vector<HostLists> g_pool;      // given back by pa_op_destroy
+constexpr size_t kPoolKeep = 64;    // buffers kept for reuse
+
+// A pinned buffer of at least `bytes` whose previous user's kernels have finished.
+pa_status acquire_lists(uint64_t bytes, HostLists& out) {
+    {
+        std::lock_guard<std::mutex> lock(g_pool_mu);
+        for (size_t i = 0; i < g_pool.size(); ++i) {
+            HostLists& c = g_pool[i];
+            if (c.bytes < bytes) continue;
+            const hipError_t q = hipEventQuery(c.done);
+            if (q == hipErrorNotReady) continue;
+            (void)hipGetLastError();
+            out = c;
+            g_pool.erase(g_pool.begin() + static_cast<std::ptrdiff_t>(i));
+            return PA_OK;
+        }
+    }
+    HostLists c;
+    c.bytes = std::max<uint64_t>(4096, bytes);
+    hipError_t e = hipHostMalloc(&c.ptr, c.bytes, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work lists)");
+    e = hipEventCreateWithFlags(&c.done, hipEventDisableTiming);
     if (e != hipSuccess) {
-        (void)hipFree(d);
-        return hip_fail(e, "copy of the work lists");
+        (void)hipHostFree(c.ptr);
+        return hip_fail(e, "hipEventCreateWithFlags");
     }
-    op->lists_dev = static_cast<unsigned char*>(d);
-    op->lists_device = dev;
-    op->lists = op->lists_dev;
+    out = c;
     return PA_OK;
 }
 
-// Copy the host work lists into one pinned, device-mapped buffer.
+void release_lists(HostLists& c) {
+    if (c.ptr == nullptr) return;
+    HostLists drop;
+    {
+        std::lock_guard<std::mutex> lock(g_pool_mu);
+        g_pool.push_back(c);
+        if (g_pool.size() > kPoolKeep) {
+            // free the oldest buffer whose last reader has finished
+            for (size_t i = 0; i < g_pool.size(); ++i) {
+                if (hipEventQuery(g_pool[i].done) == hipErrorNotReady) continue;
+                drop = g_pool[i];
+                g_pool.erase(g_pool.begin() + static_cast<std::ptrdiff_t>(i));
+                break;
+            }
+            (void)hipGetLastError();
+        }
+    }
+    if (drop.ptr != nullptr) {
+        (void)hipEventDestroy(drop.done);
+        (void)hipHostFree(drop.ptr);
+    }
+    c = HostLists{};
+}
+
+// Write the plan's work lists into the op's pinned buffer (phase 1).  Without a usable
+// HIP device (planning on a host without a GPU) the op is left without one; its execute
+// then fails.
 pa_status make_host_lists(pa_op* op) {
     const pa::Plan& p = op->plan;
-    if (op->staging != nullptr) return PA_OK;
-    hipError_t e = hipHostMalloc(&op->staging, p.items_bytes, hipHostMallocMapped);
-    if (e != hipSuccess) {
-        op->staging = nullptr;
-        return hip_fail(e, "hipHostMalloc(work lists)");
+    if (p.items_bytes == 0) return PA_OK;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+        (void)hipGetLastError();
+        op->planned_without_device = true;
+        return PA_OK;
     }
-    void* dev = nullptr;
-    e = hipHostGetDevicePointer(&dev, op->staging, 0);
-    if (e != hipSuccess) {
-        (void)hipHostFree(op->staging);
-        op->staging = nullptr;
-        return hip_fail(e, "hipHostGetDevicePointer(work lists)");
-    }
-    op->staging_dev = static_cast<unsigned char*>(dev);
-    auto* base = static_cast<unsigned char*>(op->staging);
+    pa_status st = acquire_lists(p.items_bytes, op->lists);
+    if (st != PA_OK) return st;
+    auto* base = static_cast<unsigned char*>(op->lists.ptr);
     std::memset(base, 0, p.items_bytes);
     if (p.mode == pa::Mode::kDecode) {
         std::memcpy(base + p.off_items, p.decode_items.data(),
@@ -119,6 +176,27 @@ pa_status make_host_lists(pa_op* op) {
                     p.append_items.size() * sizeof(pa::AppendItem));
     }
     return PA_OK;
+}
+
+// Checks shared by the execute calls; on success the work lists are enqueued for copy
+// into the head of the workspace.
+pa_status stage_lists(pa_op* op, unsigned char* ws, uint64_t ws_size, hipStream_t s) {
+    const pa::Plan& p = op->plan;
+    if (ws_size < p.workspace_bytes)
+        return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                    "workspace of " + std::to_string(ws_size) + " bytes, need " +
+                        std::to_string(p.workspace_bytes));
+    if (p.workspace_bytes > 0 && ws == nullptr) return fail(PA_ERR_NULLPTR, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(PA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
+    if (p.items_bytes == 0) return PA_OK;
+    if (op->lists.ptr == nullptr)
+        return fail(PA_ERR_HIP, op->planned_without_device
+                                    ? "the op was planned without a HIP device: plan it again"
+                                    : "the op has no work lists");
+    const hipError_t e = hipMemcpyAsync(ws + p.off_items, op->lists.ptr, p.items_bytes,
+                                        hipMemcpyHostToDevice, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e, "copy of the work lists into the workspace");
 }
 
 pa::AntiquantArgs antiquant_args(const pa::Plan& p) {
@@ -167,13 +245,19 @@ pa_status pa_paged_attention_get_workspace_size_ex(
     pa_op* h = new (std::nothrow) pa_op();
     if (h == nullptr) return fail(PA_ERR_HOST_ALLOC, "cannot allocate the operator");
     std::string err;
-    const pa_status st = pa::plan(query, key, value, blockTables, mask, seqLen, kvSeqLen, slopes,
-                                  maskType, headNum, kvHeadNum, qkScale, keyAntiquantScale,
-                                  valueAntiquantScale, keyAntiquantOffset, valueAntiquantOffset,
-                                  keyAntiquantMode, valueAntiquantMode, attnOut, lse, h->plan, err);
+    pa_status st = pa::plan(query, key, value, blockTables, mask, seqLen, kvSeqLen, slopes,
+                            maskType, headNum, kvHeadNum, qkScale, keyAntiquantScale,
+                            valueAntiquantScale, keyAntiquantOffset, valueAntiquantOffset,
+                            keyAntiquantMode, valueAntiquantMode, attnOut, lse, plan_config(),
+                            h->plan, err);
     if (st != PA_OK) {
         delete h;
         return fail(st, err);
+    }
+    st = make_host_lists(h);
+    if (st != PA_OK) {
+        delete h;
+        return st;
     }
     *workspaceSize = h->plan.workspace_bytes;
     *op = h;
@@ -187,15 +271,10 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
     if (p.mode == pa::Mode::kAppend)
         return fail(PA_ERR_PARAM_INVALID, "op is a KV-cache append plan: run it with pa_kv_cache_append");
     if (p.mode == pa::Mode::kNoop) return PA_OK;
-    if (workspaceSize < p.workspace_bytes)
-        return fail(PA_ERR_WORKSPACE_TOO_SMALL,
-                    "workspace of " + std::to_string(workspaceSize) + " bytes, need " +
-                        std::to_string(p.workspace_bytes));
-    if (p.workspace_bytes > 0 && workspace == nullptr)
-        return fail(PA_ERR_NULLPTR, "workspace is NULL");
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return fail(PA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    auto* ws = static_cast<unsigned char*>(workspace);
+    pa_status st = stage_lists(op, ws, workspaceSize, s);
+    if (st != PA_OK) return st;
     const bool bf16 = p.qtype == PA_BF16;
     const bool f8 = p.kvtype == PA_F8E4M3;
     const bool i8 = p.kvtype == PA_I8 || f8;      // one-byte K/V
@@ -215,17 +294,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         return e == hipSuccess ? PA_OK : hip_fail(e, "fill kernel launch");
     }
 
-    pa_status st = ensure_staging(op, s);
-    if (st != PA_OK) return st;
-    if (op->done == nullptr) {
-        e = hipEventCreateWithFlags(&op->done, hipEventDisableTiming);
-        if (e != hipSuccess) {
-            op->done = nullptr;
-            return hip_fail(e, "hipEventCreateWithFlags");
-        }
-    }
-    auto* ws = static_cast<unsigned char*>(workspace);
-    const unsigned char* lists = op->lists;
+    const unsigned char* lists = ws;
     const float scale_log2 = p.qk_scale * 1.4426950408889634f;
 
     if (p.mode == pa::Mode::kDecode) {
@@ -240,8 +309,8 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.slopes = p.slopes;
         a.kscale = p.kscale;
         a.vscale = p.vscale;
-        a.part_o = p.workspace_bytes ? reinterpret_cast<float*>(ws + p.off_part_o) : nullptr;
-        a.part_ml = p.workspace_bytes ? reinterpret_cast<float*>(ws + p.off_part_ml) : nullptr;
+        a.part_o = p.partial_slots ? reinterpret_cast<float*>(ws + p.off_part_o) : nullptr;
+        a.part_ml = p.partial_slots ? reinterpret_cast<float*>(ws + p.off_part_ml) : nullptr;
         a.q_tok_stride = p.q_tok_stride;
         a.q_head_stride = p.q_head_stride;
         a.out_tok_stride = p.out_tok_stride;
@@ -261,10 +330,12 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.scale_log2 = scale_log2;
         a.wave_heads = p.decode_wave_heads;
         a.aq = antiquant_args(p);
+        // timing events: start with the decode kernel, stop after the last kernel
+        const bool combine = !p.combine_items.empty();
         e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, f8,
-                              s, op->t_start, op->t_stop);
+                              s, op->t_start, combine ? nullptr : op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-        if (!p.combine_items.empty()) {
+        if (combine) {
             pa::CombineArgs c{};
             c.items = reinterpret_cast<const pa::CombineItem*>(lists + p.off_combine);
             c.part_o = a.part_o;
@@ -275,7 +346,8 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
             c.out_head_stride = p.out_head_stride;
             c.lse_tok_stride = p.lse_tok_stride;
             c.group = p.group;
-            e = pa::launch_combine(c, static_cast<int>(p.combine_items.size()), p.head_size, bf16, s);
+            e = pa::launch_combine(c, static_cast<int>(p.combine_items.size()), p.head_size, bf16, s,
+                                   op->t_stop);
             if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
         }
     } else {
@@ -315,50 +387,54 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
                                s, op->t_start, op->t_stop);
         if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
     }
-    // the kernels read the op's work lists from host memory until they finish
-    e = hipEventRecord(op->done, s);
+    // the copy of the work lists above reads the op's pinned buffer: mark its last use
+    if (op->lists.done == nullptr) return PA_OK;
+    e = hipEventRecord(op->lists.done, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "hipEventRecord(done)");
 }
 
 pa_status pa_kv_cache_append_plan(const pa_tensor* keyNew, const pa_tensor* valueNew,
                                   const pa_tensor* keyCache, const pa_tensor* valueCache,
                                   const pa_tensor* blockTables, const pa_tensor* seqLen,
-                                  const pa_tensor* kvSeqLen, pa_op** op) {
-    if (op == nullptr) return fail(PA_ERR_NULLPTR, "op must not be NULL");
-    *op = nullptr;
+                                  const pa_tensor* kvSeqLen, uint64_t* workspaceSize,
+                                  pa_op** op) {
+    if (op != nullptr) *op = nullptr;
+    if (workspaceSize == nullptr || op == nullptr)
+        return fail(PA_ERR_NULLPTR, "workspaceSize and op must not be NULL");
+    *workspaceSize = 0;
     pa_op* h = new (std::nothrow) pa_op();
     if (h == nullptr) return fail(PA_ERR_HOST_ALLOC, "cannot allocate the operator");
     std::string err;
-    const pa_status st =
+    pa_status st =
         pa::plan_append(keyNew, valueNew, keyCache, valueCache, blockTables, seqLen, kvSeqLen, h->plan, err);
     if (st != PA_OK) {
         delete h;
         return fail(st, err);
     }
+    st = make_host_lists(h);
+    if (st != PA_OK) {
+        delete h;
+        return st;
+    }
+    *workspaceSize = h->plan.workspace_bytes;
     *op = h;
     g_last_error.clear();
     return PA_OK;
 }
 
-pa_status pa_kv_cache_append(pa_op* op, void* stream) {
+pa_status pa_kv_cache_append(void* workspace, uint64_t workspaceSize, pa_op* op, void* stream) {
     if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
     const pa::Plan& p = op->plan;
     if (p.mode == pa::Mode::kNoop) return PA_OK;
     if (p.mode != pa::Mode::kAppend)
         return fail(PA_ERR_PARAM_INVALID, "op is not a KV-cache append plan");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    pa_status st = ensure_staging(op, s);
+    auto* ws = static_cast<unsigned char*>(workspace);
+    pa_status st = stage_lists(op, ws, workspaceSize, s);
     if (st != PA_OK) return st;
     hipError_t e;
-    if (op->done == nullptr) {
-        e = hipEventCreateWithFlags(&op->done, hipEventDisableTiming);
-        if (e != hipSuccess) {
-            op->done = nullptr;
-            return hip_fail(e, "hipEventCreateWithFlags");
-        }
-    }
     pa::AppendArgs a{};
-    a.items = reinterpret_cast<const pa::AppendItem*>(op->lists + p.off_items);
+    a.items = reinterpret_cast<const pa::AppendItem*>(ws + p.off_items);
     a.knew = p.knew;
     a.vnew = p.vnew;
     a.kcache = const_cast<void*>(p.k);
@@ -381,20 +457,34 @@ pa_status pa_kv_cache_append(pa_op* op, void* stream) {
     a.elem_bytes = p.elem_bytes;
     e = pa::launch_append(a, static_cast<int>(p.append_items.size()), s, op->t_start, op->t_stop);
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
-    e = hipEventRecord(op->done, s);
+    if (op->lists.done == nullptr) return PA_OK;
+    e = hipEventRecord(op->lists.done, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "hipEventRecord(done)");
 }
 
 void pa_op_destroy(pa_op* op) {
     if (op == nullptr) return;
-    // kernels enqueued with this op may still read its work lists: wait for the last run
-    if (op->done != nullptr) {
-        (void)hipEventSynchronize(op->done);
-        (void)hipEventDestroy(op->done);
-    }
-    if (op->lists_dev != nullptr) (void)hipFree(op->lists_dev);
-    if (op->staging != nullptr) (void)hipHostFree(op->staging);
+    // the pinned work lists go back to the pool; they are handed out again only once the
+    // copies enqueued by this op's executes have run (their event has completed)
+    release_lists(op->lists);
     delete op;
+}
+
+pa_status pa_set_plan_option(int option, int32_t value) {
+    if (option < PA_OPT_DECODE_CHUNK_TILES || option > PA_OPT_COMPUTE_UNITS)
+        return fail(PA_ERR_PARAM_INVALID, "unknown plan option " + std::to_string(option));
+    const bool flag = option == PA_OPT_DECODE_WAVE_HEADS || option == PA_OPT_PREFILL_PAIR ||
+                      option == PA_OPT_PREFILL_XCD_ORDER;
+    if (value < -1 || (flag && value > 1) || (!flag && value > (1 << 20)) || (!flag && value == 0))
+        return fail(PA_ERR_PARAM_INVALID, "value " + std::to_string(value) +
+                                              " out of range for plan option " + std::to_string(option));
+    g_options[option].store(value + 1, std::memory_order_relaxed);
+    return PA_OK;
+}
+
+int32_t pa_get_plan_option(int option) {
+    if (option < PA_OPT_DECODE_CHUNK_TILES || option > PA_OPT_COMPUTE_UNITS) return -1;
+    return ::option(option);
 }
 
 pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop) {
@@ -416,8 +506,8 @@ uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
     s += ", \"antiquant\": [" + std::to_string(p.kmode) + ", " + std::to_string(p.vmode) + ", " +
          std::to_string(p.koff != nullptr ? 1 : 0) + "]";
     s += ", \"partial_slots\": " + std::to_string(p.partial_slots);
-    s += std::string(", \"work_lists\": \"") +
-         (op->lists == nullptr ? "none" : (op->lists_dev != nullptr ? "device" : "host")) + "\"";
+    s += ", \"items_bytes\": " + std::to_string(p.items_bytes);
+    s += ", \"compute_units\": " + std::to_string(p.compute_units);
     s += ", \"decode_items\": [";
     for (size_t i = 0; i < p.decode_items.size(); ++i) {
         const pa::DecodeItem& d = p.decode_items[i];

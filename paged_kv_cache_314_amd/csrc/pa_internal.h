@@ -16,11 +16,23 @@ constexpr int kDecodeTile = 32;
 constexpr int kHeadPack = 16;
 // Waves per decode workgroup.
 constexpr int kDecodeWaves = 4;
-// Compute units of the target GPU (MI355X), for sizing work lists.
-constexpr int kComputeUnits = 256;
+// Compute units per XCD (accelerator complex die) of gfx950: a full MI355X has 8 XCDs
+// of 32 CUs; a partitioned one shows fewer whole XCDs.
+constexpr int kCusPerXcd = 32;
 // Prefill: query rows per workgroup and keys per step.
 constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
+
+// What the planner sizes work for, and the overrides of its automatic choices (a value
+// < 0 means automatic).  Set by the C ABI from the current device and pa_set_plan_option.
+struct PlanConfig {
+    int32_t compute_units = 256;        // of the device the op will run on
+    int32_t decode_chunk_tiles = -1;    // 32-token tiles per decode work item
+    int32_t decode_target_items = -1;   // decode workgroups the planner aims for
+    int32_t decode_wave_heads = -1;     // 0 / 1: items of four kv heads, one per wave
+    int32_t prefill_pair = -1;          // 0 / 1: heavy + light prefill items per CU
+    int32_t prefill_xcd_order = -1;     // 0 / 1: XCD-ordered prefill list
+};
 
 enum class Mode : int32_t { kNoop = 0, kFill = 1, kDecode = 2, kPrefill = 3, kAppend = 4 };
 
@@ -115,7 +127,7 @@ struct Plan {
     int64_t v_blk_stride = 0, v_slot_stride = 0, v_head_stride = 0;
     int64_t table_stride = 0;
 
-    // work lists (copied into the workspace by phase 2)
+    // work lists (phase 2 copies them into the head of the workspace)
     std::vector<DecodeItem> decode_items;
     std::vector<CombineItem> combine_items;
     std::vector<PrefillItem> prefill_items;
@@ -130,9 +142,10 @@ struct Plan {
     int32_t decode_chunk_tiles = 0;
     int32_t decode_wave_heads = 0;   // 1: items of 4 kv heads, one per wave
     int32_t partial_slots = 0;
+    int32_t compute_units = 0;       // the device size the lists were made for
 
-    // work lists live in pinned host memory owned by the op (offsets into it); the
-    // device workspace holds only the split-KV partials (256-aligned offsets)
+    // device workspace: the work lists in its first items_bytes (offsets off_items,
+    // off_combine), then the split-KV partials (off_part_o, off_part_ml); all 256-aligned
     uint64_t off_items = 0, off_combine = 0, items_bytes = 0;
     uint64_t off_part_o = 0, off_part_ml = 0, workspace_bytes = 0;
 };
@@ -143,7 +156,7 @@ pa_status plan_append(const pa_tensor* keyNew, const pa_tensor* valueNew, const 
                       const pa_tensor* valueCache, const pa_tensor* blockTables,
                       const pa_tensor* seqLen, const pa_tensor* kvSeqLen, Plan& p, std::string& err);
 
-// Validation + planning.  On failure returns a status and sets `err`.
+// Validation + planning for the device described by `cfg`.  On failure returns a status and sets `err`.
 pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* value,
                const pa_tensor* blockTables, const pa_tensor* mask,
                const pa_tensor* seqLen, const pa_tensor* kvSeqLen, const pa_tensor* slopes,
@@ -151,6 +164,7 @@ pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                const pa_tensor* keyAntiquantScale, const pa_tensor* valueAntiquantScale,
                const pa_tensor* keyAntiquantOffset, const pa_tensor* valueAntiquantOffset,
                int keyAntiquantMode, int valueAntiquantMode,
-               const pa_tensor* attnOut, const pa_tensor* lse, Plan& p, std::string& err);
+               const pa_tensor* attnOut, const pa_tensor* lse, const PlanConfig& cfg, Plan& p,
+               std::string& err);
 
 }  // namespace pa

@@ -156,22 +156,9 @@ PoolView pool_view(const pa_tensor* t, const char* name, int64_t kv_heads) {
     return v;
 }
 
-int env_int(const char* name, int fallback) {
-    const char* s = std::getenv(name);
-    if (s == nullptr || *s == 0) return fallback;
-    char* end = nullptr;
-    long v = std::strtol(s, &end, 10);
-    if (end == s || v <= 0 || v > (1 << 20)) return fallback;
-    return static_cast<int>(v);
-}
-
-// 0 / 1 switch from the environment (unset or unparsable: fallback)
-bool env_flag(const char* name, bool fallback) {
-    const char* s = std::getenv(name);
-    if (s == nullptr || *s == 0) return fallback;
-    if (s[0] == '0' && s[1] == 0) return false;
-    if (s[0] == '1' && s[1] == 0) return true;
-    return fallback;
+// a 0 / 1 override (< 0: the automatic choice)
+bool pick(int32_t override_value, bool automatic) {
+    return override_value < 0 ? automatic : override_value != 0;
 }
 
 uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
@@ -183,8 +170,10 @@ uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 // tile through that L2 instead of each fetching it from HBM.  Clusters go to the least
 // loaded XCD, heaviest first; the per-XCD lists are padded to equal length with no-op
 // items (heads == 0) so that list x, entry k lands at position 8 * k + x.
-std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items) {
-    constexpr int kXcds = 8;
+std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const PlanConfig& cfg) {
+    const int kXcds = cfg.compute_units % kCusPerXcd == 0
+                          ? std::max(1, std::min(8, cfg.compute_units / kCusPerXcd)) : 1;
+    const size_t cus_per_xcd = static_cast<size_t>(cfg.compute_units / kXcds);
     struct Cluster { int64_t work = 0; std::vector<PrefillItem> members; };
     std::vector<Cluster> clusters;
     {
@@ -208,7 +197,7 @@ std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items) {
     std::stable_sort(clusters.begin(), clusters.end(),
                      [](const Cluster& x, const Cluster& y) { return x.work > y.work; });
     std::vector<std::vector<PrefillItem>> lists(kXcds);
-    int64_t load[kXcds] = {};
+    std::vector<int64_t> load(kXcds, 0);
     for (const Cluster& c : clusters) {
         int x = 0;
         for (int i = 1; i < kXcds; ++i)
@@ -224,14 +213,13 @@ std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items) {
     // (measured: the causal 512-token, 4-sequence GQA workload runs 16% faster than with
     // equal-weight pairs).  Longer lists keep the cluster order, which is what lets the
     // query tiles of one (sequence, head block) share its K/V tiles through the L2.
-    constexpr size_t kCusPerXcd = kComputeUnits / kXcds;
-    if (env_flag("PA_PREFILL_PAIR", true)) {
+    if (pick(cfg.prefill_pair, true)) {
         for (auto& l : lists) {
-            if (l.size() <= kCusPerXcd || l.size() > 2 * kCusPerXcd) continue;
+            if (l.size() <= cus_per_xcd || l.size() > 2 * cus_per_xcd) continue;
             std::stable_sort(l.begin(), l.end(), [](const PrefillItem& x, const PrefillItem& y) {
                 return x.ktiles > y.ktiles;
             });
-            std::reverse(l.begin() + kCusPerXcd, l.end());
+            std::reverse(l.begin() + cus_per_xcd, l.end());
         }
     }
     size_t len = 0;
@@ -248,8 +236,9 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                int32_t headNum, int32_t kvHeadNum, float qkScale,
                const pa_tensor* keyScale, const pa_tensor* valueScale,
                const pa_tensor* keyOffset, const pa_tensor* valueOffset, int kmode, int vmode,
-               const pa_tensor* attnOut, const pa_tensor* lse, Plan& p) {
+               const pa_tensor* attnOut, const pa_tensor* lse, const PlanConfig& cfg, Plan& p) {
     // -- required descriptors (aclnnFusedInferAttentionScoreV3, Constraints: null inputs)
+    p.compute_units = cfg.compute_units;
     REQUIRE(query, PA_ERR_NULLPTR, "query is NULL");
     REQUIRE(key, PA_ERR_NULLPTR, "key is NULL");
     REQUIRE(value, PA_ERR_NULLPTR, "value is NULL");
@@ -560,10 +549,11 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         // MFMA column block: the four waves of a workgroup read neighbouring head slices
         // of the same token rows.  Only with enough work to fill the GPU: on short
         // batches splitting one kv head's range over four waves gives the shorter
-        // critical path.  PA_DECODE_WAVE_HEADS=0 / 1 turns it off / on regardless.
+        // critical path.  The decode_wave_heads option turns it off / on regardless.
         const bool wph_ok = kvh_num % 4 == 0 && p.head_groups == 1;
-        const bool wph_auto = total_tiles >= 64 * int64_t(kComputeUnits);
-        const bool wph = wph_ok && env_flag("PA_DECODE_WAVE_HEADS", wph_auto);
+        const int64_t cus = std::max(1, cfg.compute_units);
+        const bool wph_auto = total_tiles >= 64 * cus;
+        const bool wph = wph_ok && pick(cfg.decode_wave_heads, wph_auto);
         p.decode_wave_heads = wph ? 1 : 0;
         // chunk = tiles one item gives each wave's share of work: about `target`
         // workgroups in all, and a multiple of 4 tiles.  Wave-per-head items are 4x
@@ -584,12 +574,14 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                                 p.kmode == PA_ANTIQUANT_PER_CHANNEL &&
                                 p.vmode == PA_ANTIQUANT_PER_CHANNEL && p.koff == nullptr;
         const int rounds = wph ? (even ? (lean_bytes ? 1 : 2) : 4) : 0;
-        const int target = env_int("PA_DECODE_TARGET_ITEMS", wph ? rounds * kComputeUnits : 2048);
+        const int target = cfg.decode_target_items > 0
+                               ? cfg.decode_target_items
+                               : static_cast<int>(wph ? rounds * cus : 8 * cus);
         const int64_t per_item = (total_tiles + target - 1) / target;      // kv-head tiles
         int chunk = static_cast<int>(std::min<int64_t>(wph ? (per_item + 3) / 4 : per_item, 1 << 20));
         chunk = std::max(chunk, 8);          // short sequences: no split, no combine
         chunk = (chunk + 3) / 4 * 4;
-        chunk = env_int("PA_DECODE_CHUNK_TILES", chunk);
+        if (cfg.decode_chunk_tiles > 0) chunk = cfg.decode_chunk_tiles;
         p.decode_chunk_tiles = chunk;
         int32_t slots = 0;
         for (int64_t b = 0; b < B; ++b) {
@@ -638,15 +630,16 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                              return (x.t1 - x.t0) > (y.t1 - y.t0);
                          });
         const int64_t geff = std::min<int32_t>(p.group, kHeadPack);
-        // work lists: in the op's pinned host buffer; partials: in the device workspace
+        // workspace: the work lists, then the split partials
         p.off_items = 0;
         p.off_combine = align256(p.decode_items.size() * sizeof(DecodeItem));
         p.items_bytes = align256(p.off_combine + p.combine_items.size() * sizeof(CombineItem));
-        p.off_part_o = 0;
-        off = align256(uint64_t(slots) * geff * qv.d * sizeof(float));
+        off = p.items_bytes;
+        p.off_part_o = off;
+        off = align256(off + uint64_t(slots) * geff * qv.d * sizeof(float));
         p.off_part_ml = off;
         off = align256(off + uint64_t(slots) * geff * 2 * sizeof(float));
-        p.workspace_bytes = slots > 0 ? off : 0;
+        p.workspace_bytes = slots > 0 ? off : p.items_bytes;
     } else {
         // ---- prefill: (sequence, query-head block, query-row tile) items, heaviest first.
         // A workgroup covers up to 4 query heads of one kv group (so each K/V tile is
@@ -694,10 +687,10 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                              if (x.ktiles != y.ktiles) return x.ktiles > y.ktiles;
                              return head_desc && x.h > y.h;
                          });
-        if (env_flag("PA_PREFILL_XCD_ORDER", true)) p.prefill_items = xcd_order(p.prefill_items);
+        if (pick(cfg.prefill_xcd_order, true)) p.prefill_items = xcd_order(p.prefill_items, cfg);
         p.off_items = 0;
         p.items_bytes = align256(p.prefill_items.size() * sizeof(PrefillItem));
-        p.workspace_bytes = 0;
+        p.workspace_bytes = p.items_bytes;
     }
 }
 
@@ -821,7 +814,7 @@ void plan_append_impl(const pa_tensor* keyNew, const pa_tensor* valueNew, const 
     p.table_stride = blockTables->stride[0];
     p.off_items = 0;
     p.items_bytes = align256(p.append_items.size() * sizeof(AppendItem));
-    p.workspace_bytes = 0;
+    p.workspace_bytes = p.items_bytes;
 }
 
 }  // namespace
@@ -849,12 +842,13 @@ pa_status plan(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                const pa_tensor* keyAntiquantScale, const pa_tensor* valueAntiquantScale,
                const pa_tensor* keyAntiquantOffset, const pa_tensor* valueAntiquantOffset,
                int keyAntiquantMode, int valueAntiquantMode,
-               const pa_tensor* attnOut, const pa_tensor* lse, Plan& p, std::string& err) {
+               const pa_tensor* attnOut, const pa_tensor* lse, const PlanConfig& cfg, Plan& p,
+               std::string& err) {
     try {
         plan_impl(query, key, value, blockTables, mask, seqLen, kvSeqLen, slopes, maskType,
                   headNum, kvHeadNum, qkScale, keyAntiquantScale, valueAntiquantScale,
                   keyAntiquantOffset, valueAntiquantOffset, keyAntiquantMode, valueAntiquantMode,
-                  attnOut, lse, p);
+                  attnOut, lse, cfg, p);
     } catch (const Fail& f) {
         err = f.msg;
         return f.status;

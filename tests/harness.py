@@ -113,10 +113,15 @@ def oracle_run(inp, batches=None):
 
 
 def compare(out_gpu, lse_gpu, out_ref, lse_ref, rows, out_dtype, label=""):
-    """Assert the gates; return a dict of error statistics."""
-    og = out_gpu.float().cpu().numpy().astype(np.float64)[rows]
+    """Assert the gates; return a dict of error statistics.  Every row of the GPU output
+    (not only ``rows``) must be finite, and every lse must be finite or +inf."""
+    full = out_gpu.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(full)), f"{label}: non-finite output"
+    if lse_gpu is not None:
+        lf = lse_gpu.cpu().numpy()
+        assert np.all(np.isfinite(lf) | (lf == np.inf)), f"{label}: lse NaN or -inf"
+    og = full[rows]
     tol = OUT_TOL[out_dtype]
-    assert np.all(np.isfinite(og)), f"{label}: non-finite output"
     err = np.abs(og - out_ref)
     ref_max = float(np.max(np.abs(out_ref))) if out_ref.size else 0.0
     stats = {

@@ -1,9 +1,10 @@
 """CPU tests of the C ABI: symbols, phase-1 validation and planning.
 
-Phase 1 (pa_paged_attention_get_workspace_size) makes no HIP call and never
-dereferences device pointers, so these tests hand it descriptors with fake,
-aligned device addresses and real host length arrays.  Phase 2 is only called
-on paths that return before any HIP call (NULL op, short workspace, no-op op).
+Phase 1 (pa_paged_attention_get_workspace_size) never dereferences device
+pointers (without a GPU its only HIP calls, the device queries, report no
+device), so these tests hand it descriptors with fake, aligned device addresses
+and real host length arrays.  Phase 2 is only called on paths that return before
+any HIP call (NULL op, short workspace, no-op op, wrong op kind).
 """
 
 import ctypes
@@ -158,11 +159,10 @@ def test_alibi_prefill_items_longest_then_highest_head(monkeypatch):
     """Before the XCD placement, ALiBi prefill items run longest first and, among equal
     lengths, highest head first (the usual slopes fall with the head index, and steep
     heads skip most of their negligible tiles); the XCD placement keeps every item."""
-    monkeypatch.setenv("PA_PREFILL_XCD_ORDER", "0")
-    items = _plan_named("prefill_alibi_f16")["prefill_items"]
+    with pa.plan_options({pa.PA_OPT_PREFILL_XCD_ORDER: 0}):
+        items = _plan_named("prefill_alibi_f16")["prefill_items"]
     keys = [(-it[6], -it[1]) for it in items]
     assert keys == sorted(keys)
-    monkeypatch.delenv("PA_PREFILL_XCD_ORDER")
     placed = [it for it in _plan_named("prefill_alibi_f16")["prefill_items"] if it[7] != 0]
     assert sorted(map(tuple, placed)) == sorted(map(tuple, items))
 
@@ -255,7 +255,8 @@ def _check_prefill_plan(info, q_lens, kv_lens, H, mask, group=None):
     """Every (sequence, query head, query row) is covered exactly once; a workgroup's
     heads share one kv head; ktiles counts the key tiles its rows can see."""
     items = info["prefill_items"]
-    _check_xcd_order(items)
+    cus = info["compute_units"]
+    _check_xcd_order(items, min(8, cus // 32) if cus % 32 == 0 else 1)
     items = [it for it in items if it[7] != 0]
     covered = {}
     q0 = np.concatenate([[0], np.cumsum(q_lens)])
@@ -370,15 +371,13 @@ def test_head_checks():
 
 def test_decode_wave_per_head_switch(monkeypatch):
     """Items of four kv heads only where kvHeadNum % 4 == 0 and a group has <= 16 heads;
-    on by default for large batches, forced on / off by PA_DECODE_WAVE_HEADS."""
-    for env, H, Hkv, want in (("1", 16, 4, 1), ("0", 16, 4, 0), ("1", 12, 3, 0),
-                              ("1", 68, 4, 0)):
-        monkeypatch.setenv("PA_DECODE_WAVE_HEADS", env)
-        c = base(H=H, Hkv=Hkv)
-        info = c.plan()
-        assert info["decode_wave_heads"] == want, (env, H, Hkv)
+    on by default for large batches, forced on / off by PA_OPT_DECODE_WAVE_HEADS."""
+    for flag, H, Hkv, want in ((1, 16, 4, 1), (0, 16, 4, 0), (1, 12, 3, 0), (1, 68, 4, 0)):
+        with pa.plan_options({pa.PA_OPT_DECODE_WAVE_HEADS: flag}):
+            c = base(H=H, Hkv=Hkv)
+            info = c.plan()
+        assert info["decode_wave_heads"] == want, (flag, H, Hkv)
         _check_decode_plan(info, [1, 1], [100, 37], Hkv, H // Hkv)
-    monkeypatch.delenv("PA_DECODE_WAVE_HEADS")
     info = _plan_named("decode_int8_long")
     assert info["decode_wave_heads"] == 1
     info = _plan_named("decode_f16_small")
@@ -492,10 +491,12 @@ class AppendCase:
     def call(self):
         lib = pa.load()
         op = ctypes.c_void_p(None)
+        ws = ctypes.c_uint64(123)
         r = lambda d: ctypes.byref(d) if d is not None else None
         st = lib.pa_kv_cache_append_plan(r(self.knew), r(self.vnew), r(self.kc), r(self.vc),
                                          r(self.table), r(self.seq_len), r(self.kv_seq_len),
-                                         ctypes.byref(op))
+                                         ctypes.byref(ws), ctypes.byref(op))
+        self.workspace_size = int(ws.value)
         return st, op.value
 
 
@@ -546,7 +547,7 @@ def test_append_checks_and_op_kinds():
     pa.pa_op_destroy(op)
     st, _, aop = base().call()
     assert st == pa.PA_OK
-    assert lib.pa_kv_cache_append(aop, None) == pa.PA_ERR_PARAM_INVALID
+    assert lib.pa_kv_cache_append(None, 0, aop, None) == pa.PA_ERR_PARAM_INVALID
     pa.pa_op_destroy(aop)
     # no new tokens: a no-op plan
     st, op = AppendCase(q_lens=[0, 0], kv_lens=[3, 0]).call()
@@ -674,3 +675,71 @@ def test_execute_argument_errors():
     assert st == pa.PA_OK and ws == 0
     assert lib.pa_paged_attention(None, 0, op, None) == pa.PA_OK     # no-op, no HIP call
     lib.pa_op_destroy(op)
+
+
+# ----------------------------------------------------------- plan options
+
+def test_plan_options_are_declared_and_validated():
+    """The planner's tuning overrides are an explicit, declared call (not read from the
+    environment); out-of-range values and unknown options are refused."""
+    for opt in range(pa.PA_OPT_DECODE_CHUNK_TILES, pa.PA_OPT_COMPUTE_UNITS + 1):
+        assert pa.pa_get_plan_option(opt) == -1
+    lib = pa.load()
+    assert lib.pa_set_plan_option(0, 1) == pa.PA_ERR_PARAM_INVALID
+    assert lib.pa_set_plan_option(7, 1) == pa.PA_ERR_PARAM_INVALID
+    assert lib.pa_set_plan_option(pa.PA_OPT_DECODE_WAVE_HEADS, 2) == pa.PA_ERR_PARAM_INVALID
+    assert lib.pa_set_plan_option(pa.PA_OPT_DECODE_CHUNK_TILES, 0) == pa.PA_ERR_PARAM_INVALID
+    assert lib.pa_set_plan_option(pa.PA_OPT_COMPUTE_UNITS, -2) == pa.PA_ERR_PARAM_INVALID
+    with pa.plan_options({pa.PA_OPT_DECODE_CHUNK_TILES: 12}):
+        assert pa.pa_get_plan_option(pa.PA_OPT_DECODE_CHUNK_TILES) == 12
+        assert base(kv_lens=[3000, 37]).plan()["chunk_tiles"] == 12
+    assert pa.pa_get_plan_option(pa.PA_OPT_DECODE_CHUNK_TILES) == -1
+
+
+def test_default_plan_ignores_environment(monkeypatch):
+    """Variables named like the planner's options change nothing: the default plan is a
+    function of the call's arguments and the device size only."""
+    cases = [lambda: base(kv_lens=[3000, 37, 9000], q_lens=[1, 1, 1]),
+             lambda: Case(q_lens=[300, 70], kv_lens=[800, 70], H=8, Hkv=2, D=128, bs=64,
+                          mask=pa.PA_MASK_CAUSAL)]
+    before = [c().plan() for c in cases]
+    for name in ("PA_DECODE_CHUNK_TILES", "PA_DECODE_TARGET_ITEMS", "PA_DECODE_WAVE_HEADS",
+                 "PA_PREFILL_PAIR", "PA_PREFILL_XCD_ORDER", "PA_COMPUTE_UNITS"):
+        monkeypatch.setenv(name, "1")
+    after = [c().plan() for c in cases]
+    assert before == after
+
+
+def test_workspace_holds_work_lists_then_partials():
+    """The workspace starts with the work lists (32-byte prefill / combine items, 48-byte
+    decode items, 256-aligned), followed by the split partials when there are any."""
+    info = base(kv_lens=[100, 37]).plan()                     # short: no split
+    n = len(info["decode_items"])
+    assert info["partial_slots"] == 0
+    assert info["items_bytes"] == -(-48 * n // 256) * 256 == info["workspace_bytes"]
+    info = base(kv_lens=[30000, 37]).plan()                   # long: split + combine
+    assert info["partial_slots"] > 0
+    n, m = len(info["decode_items"]), len(info["combine_items"])
+    assert info["items_bytes"] == -(-48 * n // 256) * 256 + -(-32 * m // 256) * 256
+    parts = info["partial_slots"] * 4 * 128 * 4 + info["partial_slots"] * 4 * 2 * 4
+    assert info["workspace_bytes"] >= info["items_bytes"] + parts
+    assert info["workspace_bytes"] % 256 == 0
+    info = Case(q_lens=[300], kv_lens=[300], H=4, Hkv=4, D=64, bs=16,
+                mask=pa.PA_MASK_CAUSAL).plan()
+    assert info["workspace_bytes"] == info["items_bytes"] == len(info["prefill_items"]) * 32
+
+
+@pytest.mark.parametrize("cus", [32, 64, 128, 256, 80])
+def test_plans_for_smaller_devices(cus):
+    """A partitioned GPU (whole XCDs of 32 CUs) or any other size: the prefill list is
+    ordered for that many XCDs and still covers every row once; decode splits aim at
+    that many CUs."""
+    with pa.plan_options({pa.PA_OPT_COMPUTE_UNITS: cus}):
+        c = Case(q_lens=[512, 512, 300], kv_lens=[512, 2560, 300], H=32, Hkv=8, D=128,
+                 bs=128, mask=pa.PA_MASK_CAUSAL)
+        info = c.plan()
+        assert info["compute_units"] == cus
+        _check_prefill_plan(info, [512, 512, 300], [512, 2560, 300], 32, pa.PA_MASK_CAUSAL, 4)
+        d = base(kv_lens=[8000] * 16, q_lens=[1] * 16)
+        dinfo = d.plan()
+        _check_decode_plan(dinfo, [1] * 16, [8000] * 16, 2, 4)

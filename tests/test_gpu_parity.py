@@ -36,20 +36,9 @@ def _gpu():
 
 # ----------------------------------------------------------- named workloads
 
-SAMPLES = {  # sequences whose outputs the oracle checks one by one at full size
-    "decode_f16_small": None,
-    "prefill_causal_bf16": None,
-    "decode_bf16_batched": [0, 7, 21, 42, 63],
-    "prefill_alibi_f16": [0, 5],
-    "decode_int8_long": [0, 13, 31],
-    "decode_int8_pertoken_long": [2, 19, 30],
-    "decode_fp8_long": [1, 16, 31],
-    "append_prefix_f16": None,
-}
-
-
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))
 def test_named_workload_parity(name):
+    """Every sequence, head and row of each full-size workload against the oracle."""
     w = wl.WORKLOADS[name]
     _say(f"[parity] {name}")
     if w.op == "append":
@@ -67,7 +56,8 @@ def test_named_workload_parity(name):
         return
     inp = wl.make_inputs(w, poison=True)
     out, lse = gpu_run(inp, want_lse=True)
-    ro, rl, rows = oracle_run(inp, SAMPLES[name])
+    ro, rl, rows = oracle_run(inp)
+    assert len(rows) == out.shape[0]
     st = compare(out, lse, ro, rl, rows, inp["query"].dtype, name)
     _say(f"[parity] {name} {st}")
 
@@ -75,12 +65,13 @@ def test_named_workload_parity(name):
 @pytest.mark.parametrize("name", ["decode_bf16_batched", "decode_int8_long",
                                   "decode_int8_pertoken_long", "decode_fp8_long"])
 def test_high_contrast_decode(name):
-    """Queries x4 sharpen the softmax so the 2e-2 bf16 gate bites harder."""
+    """Queries x4 sharpen the softmax so the 2e-2 bf16 gate bites harder (every
+    sequence of the workload)."""
     w = wl.WORKLOADS[name]
     _say(f"[parity] {name} high-contrast")
     inp = wl.make_inputs(w, poison=True, q_scale=4.0)
     out, lse = gpu_run(inp)
-    ro, rl, rows = oracle_run(inp, [1, 17])
+    ro, rl, rows = oracle_run(inp)
     st = compare(out, lse, ro, rl, rows, inp["query"].dtype, name + "-x4")
     _say(f"[parity] {name} x4 {st}")
 
@@ -131,13 +122,13 @@ def test_decode_random(case):
 
 
 @pytest.mark.parametrize("chunk", ["8", "12", "64"])
-def test_decode_forced_splits(chunk, monkeypatch):
+def test_decode_forced_splits(chunk):
     """Many split-KV partials merged by the combine kernel equal the oracle."""
-    monkeypatch.setenv("PA_DECODE_CHUNK_TILES", chunk)
     inp = wl.make_random_case(50, batch=3, head_num=8, kv_head_num=2, head_size=128,
                               block_size=16, q_lens=[1, 1, 1], kv_lens=[3000, 257, 40],
                               dtype="bf16", mask_type=pa.PA_MASK_ALIBI)
-    out, lse, op, ws = gpu_run(inp, keep_op=True)
+    with pa.plan_options({pa.PA_OPT_DECODE_CHUNK_TILES: int(chunk)}):
+        out, lse, op, ws = gpu_run(inp, keep_op=True)
     info = pa.pa_op_describe(op)
     op.destroy()
     assert len(info["combine_items"]) > 0
@@ -155,17 +146,18 @@ WAVE_HEAD_CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(WAVE_HEAD_CASES)))
-def test_decode_wave_per_head(case, monkeypatch):
+def test_decode_wave_per_head(case):
     """Items of four kv heads, one per wave (forced on for small shapes)."""
     dt, kvdt, D, H, Hkv, bs, kv_lens, mask, chunk = WAVE_HEAD_CASES[case]
     _say(f"[decode wave-per-head] case {case}: {WAVE_HEAD_CASES[case]}")
-    monkeypatch.setenv("PA_DECODE_WAVE_HEADS", "1")
+    opts = {pa.PA_OPT_DECODE_WAVE_HEADS: 1}
     if chunk is not None:
-        monkeypatch.setenv("PA_DECODE_CHUNK_TILES", chunk)
+        opts[pa.PA_OPT_DECODE_CHUNK_TILES] = int(chunk)
     inp = wl.make_random_case(300 + case, batch=len(kv_lens), head_num=H, kv_head_num=Hkv,
                               head_size=D, block_size=bs, q_lens=[1] * len(kv_lens),
                               kv_lens=kv_lens, dtype=dt, kv_dtype=kvdt, mask_type=mask)
-    out, lse, op, ws = gpu_run(inp, keep_op=True)
+    with pa.plan_options(opts):
+        out, lse, op, ws = gpu_run(inp, keep_op=True)
     info = pa.pa_op_describe(op)
     op.destroy()
     assert info["decode_wave_heads"] == 1
@@ -178,21 +170,23 @@ ANTIQUANT_MODES = [(0, 0, True), (1, 1, False), (1, 1, True), (0, 1, False), (0,
 
 @pytest.mark.parametrize("aq", ANTIQUANT_MODES, ids=lambda m: f"k{m[0]}v{m[1]}o{int(m[2])}")
 @pytest.mark.parametrize("shape", ["plain", "alibi_d64", "splits", "wave_heads"])
-def test_decode_antiquant_modes(aq, shape, monkeypatch):
+def test_decode_antiquant_modes(aq, shape):
     """int8 decode with per-channel / per-token scales and offsets against the oracle."""
     _say(f"[decode antiquant] modes {aq} shape {shape}")
     kw = dict(batch=3, head_num=8, kv_head_num=2, head_size=128, block_size=32,
               q_lens=[1, 1, 1], kv_lens=[300, 45, 1], dtype="bf16", mask_type=pa.PA_MASK_NONE)
+    opts = {}
     if shape == "alibi_d64":
         kw.update(head_size=64, dtype="f16", mask_type=pa.PA_MASK_ALIBI, kv_lens=[97, 160, 33])
     elif shape == "splits":
-        monkeypatch.setenv("PA_DECODE_CHUNK_TILES", "8")
+        opts[pa.PA_OPT_DECODE_CHUNK_TILES] = 8
         kw.update(kv_lens=[1500, 257, 31])
     elif shape == "wave_heads":
-        monkeypatch.setenv("PA_DECODE_WAVE_HEADS", "1")
+        opts[pa.PA_OPT_DECODE_WAVE_HEADS] = 1
         kw.update(head_num=32, kv_head_num=8, kv_lens=[700, 64, 2049], block_size=64)
     inp = wl.make_random_case(400 + len(shape), kv_dtype="i8", antiquant=aq, **kw)
-    out, lse, op, ws = gpu_run(inp, keep_op=True)
+    with pa.plan_options(opts):
+        out, lse, op, ws = gpu_run(inp, keep_op=True)
     info = pa.pa_op_describe(op)
     op.destroy()
     assert info["antiquant"] == [aq[0], aq[1], int(aq[2])]
@@ -222,9 +216,9 @@ FP8_CASES = [
     ("decode", "bf16", 128, 8, 2, 32, [1, 1, 1], [300, 45, 1], pa.PA_MASK_NONE, {}),
     ("decode", "f16", 64, 8, 2, 64, [1, 1, 1], [97, 160, 33], pa.PA_MASK_ALIBI, {}),
     ("decode", "bf16", 128, 8, 2, 32, [1, 1, 1], [1500, 257, 31], pa.PA_MASK_NONE,
-     {"PA_DECODE_CHUNK_TILES": "8"}),
+     {pa.PA_OPT_DECODE_CHUNK_TILES: 8}),
     ("decode", "bf16", 128, 32, 8, 64, [1, 1, 1], [700, 64, 2049], pa.PA_MASK_NONE,
-     {"PA_DECODE_WAVE_HEADS": "1"}),
+     {pa.PA_OPT_DECODE_WAVE_HEADS: 1}),
     ("prefill", "f16", 128, 8, 2, 32, [70, 1, 130], [200, 33, 130], pa.PA_MASK_CAUSAL, {}),
     ("prefill", "bf16", 128, 8, 8, 32, [64, 100], [600, 100], pa.PA_MASK_ALIBI, {}),
     ("prefill", "f16", 64, 4, 2, 64, [33, 90], [33, 200], pa.PA_MASK_NONE, {}),
@@ -232,16 +226,15 @@ FP8_CASES = [
 
 
 @pytest.mark.parametrize("case", range(len(FP8_CASES)))
-def test_fp8_cache(case, monkeypatch):
+def test_fp8_cache(case):
     """FLOAT8_E4M3FN K/V with per-channel scales (unused slots hold NaN codes)."""
-    kind, dt, D, H, Hkv, bs, ql, kl, mask, env = FP8_CASES[case]
+    kind, dt, D, H, Hkv, bs, ql, kl, mask, opts = FP8_CASES[case]
     _say(f"[fp8] case {case}: {FP8_CASES[case]}")
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
     inp = wl.make_random_case(600 + case, batch=len(kl), head_num=H, kv_head_num=Hkv,
                               head_size=D, block_size=bs, q_lens=ql, kv_lens=kl, dtype=dt,
                               kv_dtype="f8", mask_type=mask)
-    out, lse, op, ws = gpu_run(inp, keep_op=True)
+    with pa.plan_options(opts):
+        out, lse, op, ws = gpu_run(inp, keep_op=True)
     info = pa.pa_op_describe(op)
     op.destroy()
     assert info["mode"] == kind
@@ -488,9 +481,10 @@ def test_two_dimensional_query_form():
     compare(out2.reshape(2, 4, 64), lse, ro, rl, rows, torch.float16, "2-D query")
 
 
-def test_work_lists_copied_once_and_reused_on_other_streams():
-    """The first run copies the op's work lists to the device; later runs of the same op
-    on other streams of the device read that copy and give bit-identical results."""
+def test_work_lists_copied_by_every_execute():
+    """Each execute copies the op's work lists into the workspace it is given: runs on
+    other streams, with a fresh workspace or one filled with garbage, give bit-identical
+    results."""
     inp = wl.make_random_case(73, batch=3, head_num=8, kv_head_num=2, head_size=128,
                               block_size=16, q_lens=[1, 1, 1], kv_lens=[5000, 40, 333],
                               dtype="f16")
@@ -498,27 +492,38 @@ def test_work_lists_copied_once_and_reused_on_other_streams():
     out, lse, op, ws = gpu_run(inp, stream=s, keep_op=True)
     try:
         info = pa.pa_op_describe(op)
-        assert info["work_lists"] == "device"
+        assert info["items_bytes"] > 0
         assert info["partial_slots"] > 0          # the split path and its combine ran
         ro, rl, rows = oracle_run(inp)
         compare(out, lse, ro, rl, rows, torch.float16, "first run, side stream")
         ref_o, ref_l = out.clone(), lse.clone()
-        for stream in (None, torch.cuda.Stream(), s):
+        for stream, fresh in ((None, False), (torch.cuda.Stream(), True), (s, True)):
             out.fill_(float("nan"))
             lse.fill_(float("nan"))
-            pa.pa_paged_attention(ws, op.workspace_size, op, stream)
+            w = ws
+            if fresh:
+                w = torch.full((op.workspace_size,), 0xFF, dtype=torch.uint8, device="cuda")
+                torch.cuda.synchronize()
+            pa.pa_paged_attention(w, op.workspace_size, op, stream)
             torch.cuda.synchronize()
             assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
     finally:
         op.destroy()
 
 
-def test_first_run_under_graph_capture_reads_host_lists():
-    """An op whose first run is captured into a graph keeps its work lists in pinned host
-    memory (no copy or wait under capture); every replay matches the eager result."""
-    inp = wl.make_random_case(74, batch=2, head_num=8, kv_head_num=2, head_size=128,
-                              block_size=16, q_lens=[1, 1], kv_lens=[4100, 77], dtype="bf16")
-    ref_o, ref_l = gpu_run(inp)                  # another op, eager, device lists
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_execute_under_graph_capture(kind):
+    """An execute captured into a graph (its first run, with no eager run before) holds
+    the copy of the work lists as a graph node: every replay matches an eager run, with
+    the program's own eager work between the replays."""
+    if kind == "decode":
+        inp = wl.make_random_case(74, batch=2, head_num=8, kv_head_num=2, head_size=128,
+                                  block_size=16, q_lens=[1, 1], kv_lens=[4100, 77], dtype="bf16")
+    else:
+        inp = wl.make_random_case(75, batch=2, head_num=8, kv_head_num=2, head_size=128,
+                                  block_size=64, q_lens=[200, 70], kv_lens=[600, 70],
+                                  dtype="f16", mask_type=pa.PA_MASK_CAUSAL)
+    ref_o, ref_l = gpu_run(inp)                  # another op, eager
     from tests.harness import to_device
     g = to_device(inp)
     q = g["query"]
@@ -530,16 +535,15 @@ def test_first_run_under_graph_capture_reads_host_lists():
         g["slopes"], g["mask_type"], g["head_num"], g["kv_head_num"], g["qk_scale"],
         g["key_scale"], g["value_scale"], None, None, 0, 0, out, lse)
     ws = pa.alloc_workspace(op.workspace_size, q.device)
-    assert pa.pa_op_describe(op)["work_lists"] == "none"
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     try:
-        with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+        with torch.cuda.graph(graph):
             pa.pa_paged_attention(ws, op.workspace_size, op, None)
-        assert pa.pa_op_describe(op)["work_lists"] == "host"
         for r in range(3):
             out.fill_(float("nan"))
             lse.fill_(float("nan"))
+            ws.fill_(0xFF)                      # the replay must copy the lists in again
             torch.cuda.synchronize()
             graph.replay()
             torch.cuda.synchronize()
@@ -547,7 +551,6 @@ def test_first_run_under_graph_capture_reads_host_lists():
             # the program's own eager work between replays
             x = torch.randn(4096, device=q.device)
             assert torch.isfinite(x.sum()).item()
-        # an eager run of the same op after the replays reads the same host lists
         out.fill_(float("nan"))
         pa.pa_paged_attention(ws, op.workspace_size, op, None)
         torch.cuda.synchronize()
@@ -564,3 +567,65 @@ def test_runs_on_a_side_stream():
     out, lse = gpu_run(inp, stream=s)
     ro, rl, rows = oracle_run(inp)
     compare(out, lse, ro, rl, rows, torch.bfloat16, "side stream")
+
+
+# ------------------------------------------- BnNBsD cache layout (head-major blocks)
+
+def _head_major(inp):
+    """The same pool stored as (numBlocks, kvHeadNum, blockSize, headSize) and passed
+    as its permuted (numBlocks, blockSize, kvHeadNum, headSize) view: each (block, kv
+    head) is one contiguous blockSize x headSize run (aclnnFusedInferAttentionScoreV3,
+    Constraints, paged attention scenario: the BnNBsD layout)."""
+    g = dict(inp)
+    for k in ("key", "value"):
+        g[k] = inp[k].permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    assert g["key"].stride(1) == inp["key"].shape[3]           # slot stride = headSize
+    return g
+
+
+@pytest.mark.parametrize("name", ["prefill_causal_bf16", "prefill_alibi_f16",
+                                  "decode_int8_long", "decode_fp8_long",
+                                  "decode_bf16_batched"])
+def test_named_workload_head_major_cache(name):
+    """Full-size workloads over the BnNBsD view: every row against the oracle."""
+    _say(f"[bnnbsd] {name}")
+    inp = wl.make_inputs(wl.WORKLOADS[name], poison=True)
+    out, lse = gpu_run(_head_major(inp))
+    ro, rl, rows = oracle_run(inp)
+    st = compare(out, lse, ro, rl, rows, inp["query"].dtype, name + " bnnbsd")
+    _say(f"[bnnbsd] {name} {st}")
+
+
+HEAD_MAJOR_CASES = [
+    # (kind, dtype, kv_dtype, D, H, Hkv, bs, q_lens, kv_lens, mask, opts)
+    ("prefill", "f16", None, 128, 8, 2, 64, [200, 1, 130], [700, 33, 130], pa.PA_MASK_CAUSAL, {}),
+    ("prefill", "bf16", None, 64, 4, 4, 32, [100, 65], [1000, 65], pa.PA_MASK_ALIBI, {}),
+    ("prefill", "bf16", "i8", 128, 8, 2, 64, [150, 33], [700, 33], pa.PA_MASK_CAUSAL, {}),
+    ("prefill", "f16", "i8", 128, 4, 4, 128, [130, 64], [2000, 64], pa.PA_MASK_ALIBI, {}),
+    ("prefill", "f16", "f8", 128, 8, 2, 32, [70, 1, 130], [200, 33, 130], pa.PA_MASK_CAUSAL, {}),
+    ("prefill", "bf16", "f8", 64, 8, 8, 64, [64, 100], [600, 100], pa.PA_MASK_ALIBI, {}),
+    ("decode", "bf16", "i8", 128, 64, 8, 128, [1, 1, 1], [5000, 31, 2049], pa.PA_MASK_NONE, {}),
+    ("decode", "bf16", "i8", 128, 32, 8, 64, [1, 1, 1], [700, 64, 2049], pa.PA_MASK_NONE,
+     {pa.PA_OPT_DECODE_WAVE_HEADS: 1}),
+    ("decode", "f16", "f8", 64, 8, 2, 32, [1, 1, 1], [1500, 257, 31], pa.PA_MASK_ALIBI,
+     {pa.PA_OPT_DECODE_CHUNK_TILES: 8}),
+    ("decode", "bf16", "f8", 128, 64, 8, 128, [1, 1], [9000, 130], pa.PA_MASK_NONE, {}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(HEAD_MAJOR_CASES)))
+def test_head_major_cache_cases(case):
+    """16-bit, INT8 and FP8 caches in the BnNBsD layout: prefill (causal, ALiBi) and
+    decode (plain, wave-per-head items, forced splits) against the oracle."""
+    kind, dt, kvdt, D, H, Hkv, bs, ql, kl, mask, opts = HEAD_MAJOR_CASES[case]
+    _say(f"[bnnbsd] case {case}: {HEAD_MAJOR_CASES[case]}")
+    inp = wl.make_random_case(1100 + case, batch=len(kl), head_num=H, kv_head_num=Hkv,
+                              head_size=D, block_size=bs, q_lens=ql, kv_lens=kl, dtype=dt,
+                              kv_dtype=kvdt, mask_type=mask)
+    with pa.plan_options(opts):
+        out, lse, op, ws = gpu_run(_head_major(inp), keep_op=True)
+    info = pa.pa_op_describe(op)
+    op.destroy()
+    assert info["mode"] == kind
+    ro, rl, rows = oracle_run(inp)
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"bnnbsd case {case}")
