@@ -3,9 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--kv-layout bnbsh|bnnbsd] [--no-cpu-baseline] [--copy-probe MiB]
 
-A step is one execute of the planned operator (pa_paged_attention): the copy of its
-work lists into the workspace and every kernel of the path, over one batch of seeded
-synthetic inputs already resident in HBM.  The K timed steps are captured into one HIP
+A step is one execute of the planned operator (pa_paged_attention): every kernel of
+the path, over one batch of seeded synthetic inputs already resident in HBM.  The K timed steps are captured into one HIP
 graph and replayed as a single launch (the replay is checked bit for bit against the
 eager result); the same K steps launched one by one from the host are reported as
 ``ms_per_step_eager``.  Without --warmup, the untimed warmup runs for WARMUP_SECONDS
@@ -236,6 +235,35 @@ def warmup(args, step):
             return n
 
 
+# ------------------------------------------------------------ kernel timing
+
+def time_kernels(op, run, stream, n, combine, before=None):
+    """Durations (ms) of the op's kernels over ``n`` executes, from HIP events attached to
+    each kernel's own dispatch: (main kernel list, split-KV combine list or None).
+    ``before`` (optional) runs ahead of every execute, outside the timed kernels."""
+    import torch
+
+    import paged_kv_cache_314_amd as pa
+    kinds = [pa.PA_TIMED_MAIN] + ([pa.PA_TIMED_COMBINE] if combine else [])
+    ev = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(n)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(n)]) for k in kinds}
+    for starts, stops in ev.values():
+        for e in starts + stops:
+            e.record(stream)       # torch creates its events on first use
+    torch.cuda.synchronize()
+    for i in range(n):
+        if before is not None:
+            before()
+        for k in kinds:
+            pa.pa_op_set_timing_events(op, ev[k][0][i], ev[k][1][i], kernel=k)
+        run(stream)
+    for k in kinds:
+        pa.pa_op_set_timing_events(op, None, None, kernel=k)
+    torch.cuda.synchronize()
+    out = [[s.elapsed_time(e) for s, e in zip(*ev[k])] for k in kinds]
+    return out[0], (out[1] if combine else None)
+
+
 # ------------------------------------------------------------ KV-cache append
 
 def bench_append(args, w, dev):
@@ -263,22 +291,12 @@ def bench_append(args, w, dev):
     plan_us = (time.perf_counter() - t_plan) * 1e6
     info = pa.pa_op_describe(op)
     stream = torch.cuda.current_stream()
-    ws = pa.alloc_workspace(op.workspace_size, dev)
-    run = lambda st: pa.pa_kv_cache_append(ws, op.workspace_size, op, st)
+    run = lambda st: pa.pa_kv_cache_append(op, st)
     args.warmup = warmup(args, lambda: run(stream))
     # kernel events first after the warmup, then the graph-timed steps, then eager (as
     # for the attention workloads)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for e in starts + stops:
-        e.record(stream)
-    torch.cuda.synchronize()
-    for s_ev, e_ev in zip(starts, stops):
-        pa.pa_op_set_timing_events(op, s_ev, e_ev)
-        run(stream)
-    pa.pa_op_set_timing_events(op, None, None)
-    torch.cuda.synchronize()
-    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, stops)) / args.steps
+    kms, _ = time_kernels(op, run, stream, args.steps, False)
+    kernel_ms = sum(kms) / len(kms)
     ref_k, ref_v = kc.clone(), vc.clone()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -476,22 +494,15 @@ def measure(args, name, layout, dev, cpu_seconds):
     ref_out = out.clone()
     ref_lse = lse.clone() if lse is not None else None
 
-    # kernel duration: HIP events attached to the dispatch of the op's first kernel and
-    # its last one, taken first after the warmup (the GPU's clock drifts under long runs
-    # of back-to-back launches; rocprofv3's kernel averages of the same command are taken
-    # in this state)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for e in starts + stops:
-        e.record(stream)
-    torch.cuda.synchronize()
-    for s_ev, e_ev in zip(starts, stops):
-        pa.pa_op_set_timing_events(op, s_ev, e_ev)
-        run(stream)
-    pa.pa_op_set_timing_events(op, None, None)
-    torch.cuda.synchronize()
-    kms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
-    kernel_ms = sum(kms) / len(kms)
+    # kernel durations: HIP events attached to the dispatch of each of the op's kernels,
+    # taken first after the warmup (the GPU's clock drifts under long runs of
+    # back-to-back launches; rocprofv3's kernel averages of the same command are taken in
+    # this state).  The op's kernel time is the sum of its kernels' mean durations.
+    has_combine = len(info["combine_items"]) > 0
+    kms, cms = time_kernels(op, run, stream, args.steps, has_combine)
+    main_ms = sum(kms) / len(kms)
+    combine_ms = sum(cms) / len(cms) if cms else 0.0
+    kernel_ms = main_ms + combine_ms
 
     # timed region: K whole steps, captured once into a HIP graph and replayed as one
     # launch (no host work between steps)
@@ -522,21 +533,10 @@ def measure(args, name, layout, dev, cpu_seconds):
     # 256 MB Infinity Cache and the L2s together) runs on the stream before each execute
     nc = min(args.steps, 20)
     flush = torch.ones(FLUSH_MIB << 18, dtype=torch.float32, device=dev)
-    cstarts = [torch.cuda.Event(enable_timing=True) for _ in range(nc)]
-    cstops = [torch.cuda.Event(enable_timing=True) for _ in range(nc)]
-    for e in cstarts + cstops:
-        e.record(stream)
-    torch.cuda.synchronize()
-    for s_ev, e_ev in zip(cstarts, cstops):
-        flush.sum()
-        pa.pa_op_set_timing_events(op, s_ev, e_ev)
-        run(stream)
-    pa.pa_op_set_timing_events(op, None, None)
-    torch.cuda.synchronize()
-    cold_ms = sum(s.elapsed_time(e) for s, e in zip(cstarts, cstops)) / nc
+    ck, cc = time_kernels(op, run, stream, nc, has_combine, before=lambda: flush.sum())
+    cold_ms = sum(ck) / nc + (sum(cc) / nc if cc else 0.0)
     del flush
 
-    has_combine = len(info["combine_items"]) > 0
     kernels = [f"{kind}_kernel"] + (["combine_kernel"] if has_combine else [])
     if decode:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -557,8 +557,10 @@ def measure(args, name, layout, dev, cpu_seconds):
                                             kernels)
     roof["kernel"] = "+".join(kernels)
     roof["kernel_us"] = kernel_ms * 1e3
-    qs = sorted(kms)
-    pick = lambda f: qs[int(round(f * (len(qs) - 1)))] * 1e3
+    if has_combine:
+        roof["kernel_us_each"] = {f"{kind}_kernel": main_ms * 1e3, "combine_kernel": combine_ms * 1e3}
+    tot = sorted(a + b for a, b in zip(kms, cms)) if cms else sorted(kms)
+    pick = lambda f: tot[int(round(f * (len(tot) - 1)))] * 1e3
     roof["kernel_us_p10_median_p90"] = [pick(0.1), pick(0.5), pick(0.9)]
     work = nbytes / 1e9 if decode else flops / 1e12
     roof["cold"] = {"kernel_us": cold_ms * 1e3, "achieved": work / (cold_ms * 1e-3),

@@ -21,9 +21,8 @@
  *      (the current device's compute-unit count) and, on a host with a device, a pinned
  *      host buffer for the op's work lists (taken from a pool that pa_op_destroy
  *      refills, so steady-state planning allocates nothing).
- *   2. pa_paged_attention(workspace, size, op, stream) enqueues the copy of the work
- *      lists into the workspace and the kernels on `stream`; it allocates nothing and
- *      never waits.
+ *   2. pa_paged_attention(workspace, size, op, stream) enqueues the kernels on `stream`;
+ *      it allocates nothing and never waits.
  *
  * Conventions shared by every entry point
  *   - Tensors are described by pa_tensor (data pointer, dtype, shape, strides in
@@ -31,9 +30,9 @@
  *   - "device" = HIP device memory (e.g. a torch CUDA tensor on ROCm);
  *     "host" = ordinary CPU memory.
  *   - The caller owns every tensor and the workspace; the library never allocates device
- *     memory.  The library owns the pa_op: its plan and a pinned host copy of its work
- *     lists (32 or 48 bytes per workgroup), which each execute copies into the head of
- *     the workspace before its kernels run.
+ *     memory.  The library owns the pa_op: its plan and its work lists (32 or 48 bytes
+ *     per workgroup) in pinned, device-mapped host memory, which the kernels read in
+ *     place (each workgroup loads its own item once).
  *   - Tensors and the workspace must stay alive, and must not be written by others,
  *     until the work enqueued by pa_paged_attention has completed on the stream.
  *   - Block ids in blockTables are not validated (aclnnFusedInferAttentionScoreV3,
@@ -216,12 +215,11 @@ pa_status pa_paged_attention_get_workspace_size_ex(
  * stream).  (PrefixEncoder, Definition: AtbSelfAttentionPrefixEncoder; the pages'
  * context argument becomes a HIP stream.)  workspace: device memory of at least the
  * phase-1 size, 256-byte aligned, or NULL if that size is 0; its contents on entry do
- * not matter and are scratch afterwards.  It holds the op's work lists (copied in by an
- * asynchronous host-to-device copy from the op's pinned buffer, enqueued on `stream`
- * ahead of the kernels) and, when sequences are split, the split-KV partial results.
- * The call only enqueues: no allocation, no wait, so it may be captured into a graph
- * (the copy becomes a graph node that reads the op's pinned buffer on every replay;
- * such a graph must not be replayed after pa_op_destroy).
+ * not matter and are scratch afterwards.  It holds the split-KV partial results; the
+ * size is 0 when no sequence is split.  The call only enqueues kernels: no allocation,
+ * no copy, no wait, so it may be captured into a graph (whose kernels read the op's
+ * pinned work lists on every replay: such a graph must not be replayed after
+ * pa_op_destroy).
  * An op may be executed any number of times, on any stream of any device; two
  * executions must not share a workspace while both are in flight.
  * Returns PA_ERR_NULLPTR (op, or a needed workspace, is NULL), PA_ERR_WORKSPACE_TOO_SMALL,
@@ -255,27 +253,24 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
  *                    call); the slots written must not be shared by two sequences.
  * seqLen, kvSeqLen   HOST, [batch] int32, 0 <= seqLen[b] <= kvSeqLen[b],
  *                    sum(seqLen) = nTokens.
- * workspaceSize      out: device workspace bytes pa_kv_cache_append needs (its work list,
- *                    16 new tokens per 32-byte item; 0 for a no-op).
  * op                 out: handle (pa_op_destroy releases it); nTokens == 0 gives a no-op.
- * Planning is done as for pa_paged_attention_get_workspace_size (same HIP calls).
- * pa_kv_cache_append enqueues the copy of the work list into `workspace` (256-byte
- * aligned device memory of at least workspaceSize bytes, scratch afterwards) and the
- * copy kernel on `stream` (NULL = the null stream); it allocates nothing and never waits,
- * and may be run again, e.g. after the new rows were refilled in place.
+ * Planning is done as for pa_paged_attention_get_workspace_size (same HIP calls; the
+ * work list, 16 new tokens per 32-byte item, is pinned host memory the kernel reads).
+ * pa_kv_cache_append enqueues the copy kernel on `stream` (NULL = the null stream); it
+ * allocates nothing and never waits, and may be run again, e.g. after the new rows were
+ * refilled in place.
  * pa_paged_attention rejects an append op and pa_kv_cache_append an attention op
  * (PA_ERR_PARAM_INVALID).  pa_op_set_timing_events applies to the copy kernel.
  */
 pa_status pa_kv_cache_append_plan(const pa_tensor* keyNew, const pa_tensor* valueNew,
                                   const pa_tensor* keyCache, const pa_tensor* valueCache,
                                   const pa_tensor* blockTables, const pa_tensor* seqLen,
-                                  const pa_tensor* kvSeqLen, uint64_t* workspaceSize,
-                                  pa_op** op);
-pa_status pa_kv_cache_append(void* workspace, uint64_t workspaceSize, pa_op* op, void* stream);
+                                  const pa_tensor* kvSeqLen, pa_op** op);
+pa_status pa_kv_cache_append(pa_op* op, void* stream);
 
 /* Release an operator handle (NULL is ignored).  Work already enqueued is unaffected and
  * the call does not wait for it: the op's pinned work-list buffer goes back to the
- * library's pool and is handed to a new op only after the copies enqueued from it have
+ * library's pool and is handed to a new op only after the kernels that read it have
  * run. */
 void pa_op_destroy(pa_op* op);
 
@@ -307,18 +302,19 @@ pa_status pa_set_plan_option(int option, int32_t value);
 int32_t pa_get_plan_option(int option);
 
 /* Instrumentation: start and stop are hipEvent_t handles (or NULL to clear), created with
- * timing enabled.  While set, each execute of this op attaches start to the dispatch of
- * its main kernel (the decode, prefill or append kernel) and stop to its last kernel
- * (the split-KV combine when there is one), so that hipEventElapsedTime(start, stop) is
- * the duration of the op's kernels, without the copy of the work lists.  The events
- * stay owned by the caller.  Host only; returns PA_ERR_NULLPTR if op is NULL. */
-pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop);
+ * timing enabled.  While set, each execute of this op attaches them to the dispatch of
+ * one of its kernels -- kernel PA_TIMED_MAIN: the decode, prefill or append kernel;
+ * PA_TIMED_COMBINE: the split-KV combine, run by decode ops that split a sequence -- so
+ * that hipEventElapsedTime(start, stop) is that kernel's own duration.  The events stay
+ * owned by the caller.  Host only; returns PA_ERR_NULLPTR if op is NULL and
+ * PA_ERR_PARAM_INVALID for another kernel index. */
+enum { PA_TIMED_MAIN = 0, PA_TIMED_COMBINE = 1 };
+pa_status pa_op_set_timing_events(pa_op* op, int kernel, void* start, void* stop);
 
 /* Write a JSON description of the operator's plan into buf (NUL-terminated, cut at
  * cap - 1 bytes; buf may be NULL when cap is 0) and return the full length without the
  * NUL.  Keys: "mode" ("noop", "fill", "decode", "prefill", "append"), "workspace_bytes",
- * "items_bytes" (the work lists at the head of the workspace), "compute_units" (planned
- * for), "chunk_tiles", "partial_slots", and the work lists "decode_items"
+ * "items_bytes" (the pinned work lists), "compute_units" (planned for), "chunk_tiles", "partial_slots", and the work lists "decode_items"
  * [b, kvh, hg, t0, t1, slot, qrow, kvlen], "combine_items" [kvh, hg, slot0, nsplit, qrow],
  * "prefill_items" [b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads] (heads query heads from
  * h, 128/heads query rows from qbeg), "append_items" [b, row0, pos0, count], "antiquant"

@@ -103,11 +103,9 @@ def load():
     lib.pa_paged_attention.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                        ctypes.c_void_p]
     lib.pa_kv_cache_append_plan.restype = ctypes.c_int
-    lib.pa_kv_cache_append_plan.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_uint64),
-                                            ctypes.POINTER(ctypes.c_void_p)]
+    lib.pa_kv_cache_append_plan.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_void_p)]
     lib.pa_kv_cache_append.restype = ctypes.c_int
-    lib.pa_kv_cache_append.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
-                                       ctypes.c_void_p]
+    lib.pa_kv_cache_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.pa_set_plan_option.restype = ctypes.c_int
     lib.pa_set_plan_option.argtypes = [ctypes.c_int, ctypes.c_int32]
     lib.pa_get_plan_option.restype = ctypes.c_int32
@@ -115,7 +113,8 @@ def load():
     lib.pa_op_destroy.restype = None
     lib.pa_op_destroy.argtypes = [ctypes.c_void_p]
     lib.pa_op_set_timing_events.restype = ctypes.c_int
-    lib.pa_op_set_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_op_set_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p]
     lib.pa_op_describe.restype = ctypes.c_uint64
     lib.pa_op_describe.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_uint64]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -264,24 +263,20 @@ def pa_kv_cache_append_plan(key_new, value_new, key_cache, value_cache, block_ta
              describe(key_cache, device="cuda"), describe(value_cache, device="cuda"),
              describe(block_tables, device="cuda"), describe(seq_len, device="cpu"),
              describe(kv_seq_len, device="cpu")]
-    ws = ctypes.c_uint64(0)
     handle = ctypes.c_void_p(None)
-    _check(lib.pa_kv_cache_append_plan(*[_ref(d) for d in descs], ctypes.byref(ws),
-                                       ctypes.byref(handle)))
+    _check(lib.pa_kv_cache_append_plan(*[_ref(d) for d in descs], ctypes.byref(handle)))
     keep = (key_new, value_new, key_cache, value_cache, block_tables, seq_len, kv_seq_len)
-    return Op(handle.value, int(ws.value), keep)
+    return Op(handle.value, 0, keep)
 
 
-def pa_kv_cache_append(workspace, workspace_size, op, stream=None):
-    """Enqueue a planned KV-cache append on ``stream`` (None = torch's current stream).
-    ``workspace`` is a uint8 CUDA tensor of at least ``workspace_size`` bytes, or None."""
+def pa_kv_cache_append(op, stream=None):
+    """Enqueue a planned KV-cache append on ``stream`` (None = torch's current stream)."""
     lib = load()
     handle = op.handle if isinstance(op, Op) else op
     if stream is None:
         stream = torch.cuda.current_stream()
     raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
-    ptr = workspace.data_ptr() if workspace is not None and workspace.numel() > 0 else None
-    _check(lib.pa_kv_cache_append(ptr, int(workspace_size), handle, raw))
+    _check(lib.pa_kv_cache_append(handle, raw))
 
 
 def kv_cache_append(key_new, value_new, key_cache, value_cache, block_tables, seq_len,
@@ -290,8 +285,7 @@ def kv_cache_append(key_new, value_new, key_cache, value_cache, block_tables, se
     op = pa_kv_cache_append_plan(key_new, value_new, key_cache, value_cache, block_tables,
                                  seq_len, kv_seq_len)
     try:
-        ws = alloc_workspace(op.workspace_size, key_cache.device)
-        pa_kv_cache_append(ws, op.workspace_size, op, stream)
+        pa_kv_cache_append(op, stream)
     finally:
         torch.cuda.synchronize(key_cache.device)
         op.destroy()
@@ -333,13 +327,17 @@ class plan_options:
         return False
 
 
-def pa_op_set_timing_events(op, start, stop):
-    """Record torch.cuda.Event ``start``/``stop`` around the op's kernels (None clears).
-    Events must have been recorded once (torch creates them lazily)."""
+PA_TIMED_MAIN, PA_TIMED_COMBINE = 0, 1
+
+
+def pa_op_set_timing_events(op, start, stop, kernel=PA_TIMED_MAIN):
+    """Record torch.cuda.Event ``start``/``stop`` around one of the op's kernels
+    (PA_TIMED_MAIN or PA_TIMED_COMBINE; None clears).  Events must have been recorded
+    once (torch creates them lazily)."""
     handle = op.handle if isinstance(op, Op) else op
     s = start.cuda_event if start is not None else None
     e = stop.cuda_event if stop is not None else None
-    _check(load().pa_op_set_timing_events(handle, s, e))
+    _check(load().pa_op_set_timing_events(handle, int(kernel), s, e))
 
 
 def pa_op_describe(op):

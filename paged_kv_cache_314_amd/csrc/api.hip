@@ -15,21 +15,24 @@
 #include "pa_kernels.h"
 #include "pagedattn.h"
 
-// A pinned host buffer holding an op's work lists, with the event recorded after the last
-// kernel that read a copy of them.  Buffers are drawn from a pool in phase 1 and given
+// A pinned, device-mapped host buffer holding an op's work lists, which the kernels read
+// in place (each workgroup loads its own item once, at start-up), with the event recorded
+// after the last kernel that read it.  Buffers are drawn from a pool in phase 1 and given
 // back by pa_op_destroy, so steady-state planning allocates nothing.
 struct HostLists {
-    void* ptr = nullptr;
+    void* ptr = nullptr;                // host address
+    const unsigned char* dev = nullptr; // the same memory as the GPU addresses it
     uint64_t bytes = 0;
     hipEvent_t done = nullptr;
 };
 
 struct pa_op {
     pa::Plan plan;
-    HostLists lists;                // pinned copy of the plan's work lists (made in phase 1)
+    HostLists lists;                // the plan's work lists, pinned (made in phase 1)
     bool planned_without_device = false;
-    hipEvent_t t_start = nullptr;   // caller's timing events around the op's kernels
-    hipEvent_t t_stop = nullptr;
+    // caller's timing events: [0] around the main kernel, [1] around the split-KV combine
+    hipEvent_t t_start[2] = {nullptr, nullptr};
+    hipEvent_t t_stop[2] = {nullptr, nullptr};
 };
 
 namespace {
@@ -112,13 +115,17 @@ pa_status acquire_lists(uint64_t bytes, HostLists& out) {
     }
     HostLists c;
     c.bytes = std::max<uint64_t>(4096, bytes);
-    hipError_t e = hipHostMalloc(&c.ptr, c.bytes, hipHostMallocDefault);
+    // coherent: a buffer handed to a new op is never seen stale through a GPU cache
+    hipError_t e = hipHostMalloc(&c.ptr, c.bytes, hipHostMallocMapped | hipHostMallocCoherent);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work lists)");
-    e = hipEventCreateWithFlags(&c.done, hipEventDisableTiming);
+    void* dev = nullptr;
+    e = hipHostGetDevicePointer(&dev, c.ptr, 0);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c.done, hipEventDisableTiming);
     if (e != hipSuccess) {
         (void)hipHostFree(c.ptr);
-        return hip_fail(e, "hipEventCreateWithFlags");
+        return hip_fail(e, "device mapping of the work lists");
     }
+    c.dev = static_cast<const unsigned char*>(dev);
     out = c;
     return PA_OK;
 }
@@ -178,9 +185,8 @@ pa_status make_host_lists(pa_op* op) {
     return PA_OK;
 }
 
-// Checks shared by the execute calls; on success the work lists are enqueued for copy
-// into the head of the workspace.
-pa_status stage_lists(pa_op* op, unsigned char* ws, uint64_t ws_size, hipStream_t s) {
+// Checks shared by the execute calls (workspace size and alignment, work lists present).
+pa_status check_execute(const pa_op* op, const unsigned char* ws, uint64_t ws_size) {
     const pa::Plan& p = op->plan;
     if (ws_size < p.workspace_bytes)
         return fail(PA_ERR_WORKSPACE_TOO_SMALL,
@@ -189,15 +195,13 @@ pa_status stage_lists(pa_op* op, unsigned char* ws, uint64_t ws_size, hipStream_
     if (p.workspace_bytes > 0 && ws == nullptr) return fail(PA_ERR_NULLPTR, "workspace is NULL");
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
         return fail(PA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
-    if (p.items_bytes == 0) return PA_OK;
-    if (op->lists.ptr == nullptr)
-        return fail(PA_ERR_HIP, op->planned_without_device
-                                    ? "the op was planned without a HIP device: plan it again"
-                                    : "the op has no work lists");
-    const hipError_t e = hipMemcpyAsync(ws + p.off_items, op->lists.ptr, p.items_bytes,
-                                        hipMemcpyHostToDevice, s);
-    return e == hipSuccess ? PA_OK : hip_fail(e, "copy of the work lists into the workspace");
+    if (p.items_bytes == 0 || op->lists.dev != nullptr) return PA_OK;
+    return fail(PA_ERR_HIP, op->planned_without_device
+                                ? "the op was planned without a HIP device: plan it again"
+                                : "the op has no work lists");
 }
+
+pa_status execute_attention(pa_op* op, unsigned char* ws, uint64_t workspaceSize, hipStream_t s);
 
 pa::AntiquantArgs antiquant_args(const pa::Plan& p) {
     pa::AntiquantArgs q{};
@@ -267,13 +271,21 @@ pa_status pa_paged_attention_get_workspace_size_ex(
 
 pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op, void* stream) {
     if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
-    const pa::Plan& p = op->plan;
-    if (p.mode == pa::Mode::kAppend)
+    if (op->plan.mode == pa::Mode::kAppend)
         return fail(PA_ERR_PARAM_INVALID, "op is a KV-cache append plan: run it with pa_kv_cache_append");
+    return execute_attention(op, static_cast<unsigned char*>(workspace), workspaceSize,
+                             static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Phase 2 of an attention op with the workspace `ws` (device memory of ws_size bytes).
+pa_status execute_attention(pa_op* op, unsigned char* ws, uint64_t workspaceSize, hipStream_t s) {
+    const pa::Plan& p = op->plan;
     if (p.mode == pa::Mode::kNoop) return PA_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    auto* ws = static_cast<unsigned char*>(workspace);
-    pa_status st = stage_lists(op, ws, workspaceSize, s);
+    pa_status st = check_execute(op, ws, workspaceSize);
     if (st != PA_OK) return st;
     const bool bf16 = p.qtype == PA_BF16;
     const bool f8 = p.kvtype == PA_F8E4M3;
@@ -294,7 +306,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         return e == hipSuccess ? PA_OK : hip_fail(e, "fill kernel launch");
     }
 
-    const unsigned char* lists = ws;
+    const unsigned char* lists = op->lists.dev;
     const float scale_log2 = p.qk_scale * 1.4426950408889634f;
 
     if (p.mode == pa::Mode::kDecode) {
@@ -330,10 +342,9 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.scale_log2 = scale_log2;
         a.wave_heads = p.decode_wave_heads;
         a.aq = antiquant_args(p);
-        // timing events: start with the decode kernel, stop after the last kernel
         const bool combine = !p.combine_items.empty();
         e = pa::launch_decode(a, static_cast<int>(p.decode_items.size()), p.head_size, bf16, i8, f8,
-                              s, op->t_start, combine ? nullptr : op->t_stop);
+                              s, op->t_start[0], op->t_stop[0]);
         if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
         if (combine) {
             pa::CombineArgs c{};
@@ -347,7 +358,7 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
             c.lse_tok_stride = p.lse_tok_stride;
             c.group = p.group;
             e = pa::launch_combine(c, static_cast<int>(p.combine_items.size()), p.head_size, bf16, s,
-                                   op->t_stop);
+                                   op->t_start[1], op->t_stop[1]);
             if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
         }
     } else {
@@ -384,24 +395,25 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         a.scale_log2 = scale_log2;
         a.aq = antiquant_args(p);
         e = pa::launch_prefill(a, static_cast<int>(p.prefill_items.size()), p.head_size, bf16, i8, f8,
-                               s, op->t_start, op->t_stop);
+                               s, op->t_start[0], op->t_stop[0]);
         if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
     }
-    // the copy of the work lists above reads the op's pinned buffer: mark its last use
+    // the kernels read the op's pinned work lists: mark their last use
     if (op->lists.done == nullptr) return PA_OK;
     e = hipEventRecord(op->lists.done, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "hipEventRecord(done)");
 }
 
+}  // namespace
+
+extern "C" {
+
 pa_status pa_kv_cache_append_plan(const pa_tensor* keyNew, const pa_tensor* valueNew,
                                   const pa_tensor* keyCache, const pa_tensor* valueCache,
                                   const pa_tensor* blockTables, const pa_tensor* seqLen,
-                                  const pa_tensor* kvSeqLen, uint64_t* workspaceSize,
-                                  pa_op** op) {
-    if (op != nullptr) *op = nullptr;
-    if (workspaceSize == nullptr || op == nullptr)
-        return fail(PA_ERR_NULLPTR, "workspaceSize and op must not be NULL");
-    *workspaceSize = 0;
+                                  const pa_tensor* kvSeqLen, pa_op** op) {
+    if (op == nullptr) return fail(PA_ERR_NULLPTR, "op must not be NULL");
+    *op = nullptr;
     pa_op* h = new (std::nothrow) pa_op();
     if (h == nullptr) return fail(PA_ERR_HOST_ALLOC, "cannot allocate the operator");
     std::string err;
@@ -416,25 +428,23 @@ pa_status pa_kv_cache_append_plan(const pa_tensor* keyNew, const pa_tensor* valu
         delete h;
         return st;
     }
-    *workspaceSize = h->plan.workspace_bytes;
     *op = h;
     g_last_error.clear();
     return PA_OK;
 }
 
-pa_status pa_kv_cache_append(void* workspace, uint64_t workspaceSize, pa_op* op, void* stream) {
+pa_status pa_kv_cache_append(pa_op* op, void* stream) {
     if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
     const pa::Plan& p = op->plan;
     if (p.mode == pa::Mode::kNoop) return PA_OK;
     if (p.mode != pa::Mode::kAppend)
         return fail(PA_ERR_PARAM_INVALID, "op is not a KV-cache append plan");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    auto* ws = static_cast<unsigned char*>(workspace);
-    pa_status st = stage_lists(op, ws, workspaceSize, s);
+    pa_status st = check_execute(op, nullptr, 0);
     if (st != PA_OK) return st;
     hipError_t e;
     pa::AppendArgs a{};
-    a.items = reinterpret_cast<const pa::AppendItem*>(ws + p.off_items);
+    a.items = reinterpret_cast<const pa::AppendItem*>(op->lists.dev + p.off_items);
     a.knew = p.knew;
     a.vnew = p.vnew;
     a.kcache = const_cast<void*>(p.k);
@@ -455,7 +465,8 @@ pa_status pa_kv_cache_append(void* workspace, uint64_t workspaceSize, pa_op* op,
     a.row_chunks = p.head_size * p.elem_bytes / 16;
     a.block_size = p.block_size;
     a.elem_bytes = p.elem_bytes;
-    e = pa::launch_append(a, static_cast<int>(p.append_items.size()), s, op->t_start, op->t_stop);
+    e = pa::launch_append(a, static_cast<int>(p.append_items.size()), s, op->t_start[0],
+                          op->t_stop[0]);
     if (e != hipSuccess) return hip_fail(e, "append kernel launch");
     if (op->lists.done == nullptr) return PA_OK;
     e = hipEventRecord(op->lists.done, s);
@@ -465,7 +476,7 @@ pa_status pa_kv_cache_append(void* workspace, uint64_t workspaceSize, pa_op* op,
 void pa_op_destroy(pa_op* op) {
     if (op == nullptr) return;
     // the pinned work lists go back to the pool; they are handed out again only once the
-    // copies enqueued by this op's executes have run (their event has completed)
+    // kernels enqueued by this op's executes have run (their event has completed)
     release_lists(op->lists);
     delete op;
 }
@@ -487,10 +498,12 @@ int32_t pa_get_plan_option(int option) {
     return ::option(option);
 }
 
-pa_status pa_op_set_timing_events(pa_op* op, void* start, void* stop) {
+pa_status pa_op_set_timing_events(pa_op* op, int kernel, void* start, void* stop) {
     if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
-    op->t_start = static_cast<hipEvent_t>(start);
-    op->t_stop = static_cast<hipEvent_t>(stop);
+    if (kernel != PA_TIMED_MAIN && kernel != PA_TIMED_COMBINE)
+        return fail(PA_ERR_PARAM_INVALID, "kernel must be PA_TIMED_MAIN or PA_TIMED_COMBINE");
+    op->t_start[kernel] = static_cast<hipEvent_t>(start);
+    op->t_stop[kernel] = static_cast<hipEvent_t>(stop);
     return PA_OK;
 }
 

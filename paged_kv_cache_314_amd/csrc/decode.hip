@@ -764,11 +764,12 @@ hipError_t launch_decode_d(const DecodeArgs& a, int n_items, bool bf16, bool i8,
 }
 
 template <int D, bool BF16>
-hipError_t launch_combine_t(const CombineArgs& a, int n_items, hipStream_t stream, hipEvent_t t1) {
+hipError_t launch_combine_t(const CombineArgs& a, int n_items, hipStream_t stream, hipEvent_t t0,
+                            hipEvent_t t1) {
     CombineArgs c = a;
     const int geff = a.group < kHeadPack ? a.group : kHeadPack;
     c.blocks_per_item = (geff * D + 255) / 256;
-    launch_256(combine_kernel<D, BF16>, n_items * c.blocks_per_item, stream, nullptr, t1, c);
+    launch_256(combine_kernel<D, BF16>, n_items * c.blocks_per_item, stream, t0, t1, c);
     return hipGetLastError();
 }
 
@@ -782,13 +783,13 @@ hipError_t launch_decode(const DecodeArgs& a, int n_items, int head_size, bool b
 }
 
 hipError_t launch_combine(const CombineArgs& a, int n_items, int head_size, bool bf16,
-                          hipStream_t stream, hipEvent_t t1) {
+                          hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     if (n_items <= 0) return hipSuccess;
     if (head_size == 128)
-        return bf16 ? launch_combine_t<128, true>(a, n_items, stream, t1)
-                    : launch_combine_t<128, false>(a, n_items, stream, t1);
-    return bf16 ? launch_combine_t<64, true>(a, n_items, stream, t1)
-                : launch_combine_t<64, false>(a, n_items, stream, t1);
+        return bf16 ? launch_combine_t<128, true>(a, n_items, stream, t0, t1)
+                    : launch_combine_t<128, false>(a, n_items, stream, t0, t1);
+    return bf16 ? launch_combine_t<64, true>(a, n_items, stream, t0, t1)
+                : launch_combine_t<64, false>(a, n_items, stream, t0, t1);
 }
 
 }  // namespace pa

@@ -127,7 +127,7 @@ struct Plan {
     int64_t v_blk_stride = 0, v_slot_stride = 0, v_head_stride = 0;
     int64_t table_stride = 0;
 
-    // work lists (phase 2 copies them into the head of the workspace)
+    // work lists (the kernels read them from the op's pinned host buffer)
     std::vector<DecodeItem> decode_items;
     std::vector<CombineItem> combine_items;
     std::vector<PrefillItem> prefill_items;
@@ -144,8 +144,9 @@ struct Plan {
     int32_t partial_slots = 0;
     int32_t compute_units = 0;       // the device size the lists were made for
 
-    // device workspace: the work lists in its first items_bytes (offsets off_items,
-    // off_combine), then the split-KV partials (off_part_o, off_part_ml); all 256-aligned
+    // work lists: in the op's pinned, device-mapped host buffer (offsets off_items,
+    // off_combine, items_bytes); the device workspace holds only the split-KV partials
+    // (off_part_o, off_part_ml); all 256-aligned
     uint64_t off_items = 0, off_combine = 0, items_bytes = 0;
     uint64_t off_part_o = 0, off_part_ml = 0, workspace_bytes = 0;
 };

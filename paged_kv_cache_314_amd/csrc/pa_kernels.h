@@ -110,7 +110,7 @@ hipError_t launch_decode(const DecodeArgs& a, int n_items, int head_size, bool b
                          bool f8, hipStream_t stream, hipEvent_t t0 = nullptr,
                          hipEvent_t t1 = nullptr);
 hipError_t launch_combine(const CombineArgs& a, int n_items, int head_size, bool bf16,
-                          hipStream_t stream, hipEvent_t t1 = nullptr);
+                          hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_prefill(const PrefillArgs& a, int n_items, int head_size, bool bf16, bool i8,
                           bool f8, hipStream_t stream, hipEvent_t t0 = nullptr,
                           hipEvent_t t1 = nullptr);

@@ -630,16 +630,15 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                              return (x.t1 - x.t0) > (y.t1 - y.t0);
                          });
         const int64_t geff = std::min<int32_t>(p.group, kHeadPack);
-        // workspace: the work lists, then the split partials
+        // work lists: in the op's pinned host buffer; partials: in the device workspace
         p.off_items = 0;
         p.off_combine = align256(p.decode_items.size() * sizeof(DecodeItem));
         p.items_bytes = align256(p.off_combine + p.combine_items.size() * sizeof(CombineItem));
-        off = p.items_bytes;
         p.off_part_o = off;
         off = align256(off + uint64_t(slots) * geff * qv.d * sizeof(float));
         p.off_part_ml = off;
         off = align256(off + uint64_t(slots) * geff * 2 * sizeof(float));
-        p.workspace_bytes = slots > 0 ? off : p.items_bytes;
+        p.workspace_bytes = slots > 0 ? off : 0;
     } else {
         // ---- prefill: (sequence, query-head block, query-row tile) items, heaviest first.
         // A workgroup covers up to 4 query heads of one kv group (so each K/V tile is
@@ -690,7 +689,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         if (pick(cfg.prefill_xcd_order, true)) p.prefill_items = xcd_order(p.prefill_items, cfg);
         p.off_items = 0;
         p.items_bytes = align256(p.prefill_items.size() * sizeof(PrefillItem));
-        p.workspace_bytes = p.items_bytes;
+        p.workspace_bytes = 0;
     }
 }
 
@@ -814,7 +813,7 @@ void plan_append_impl(const pa_tensor* keyNew, const pa_tensor* valueNew, const 
     p.table_stride = blockTables->stride[0];
     p.off_items = 0;
     p.items_bytes = align256(p.append_items.size() * sizeof(AppendItem));
-    p.workspace_bytes = p.items_bytes;
+    p.workspace_bytes = 0;
 }
 
 }  // namespace

@@ -491,12 +491,10 @@ class AppendCase:
     def call(self):
         lib = pa.load()
         op = ctypes.c_void_p(None)
-        ws = ctypes.c_uint64(123)
         r = lambda d: ctypes.byref(d) if d is not None else None
         st = lib.pa_kv_cache_append_plan(r(self.knew), r(self.vnew), r(self.kc), r(self.vc),
                                          r(self.table), r(self.seq_len), r(self.kv_seq_len),
-                                         ctypes.byref(ws), ctypes.byref(op))
-        self.workspace_size = int(ws.value)
+                                         ctypes.byref(op))
         return st, op.value
 
 
@@ -547,7 +545,7 @@ def test_append_checks_and_op_kinds():
     pa.pa_op_destroy(op)
     st, _, aop = base().call()
     assert st == pa.PA_OK
-    assert lib.pa_kv_cache_append(None, 0, aop, None) == pa.PA_ERR_PARAM_INVALID
+    assert lib.pa_kv_cache_append(aop, None) == pa.PA_ERR_PARAM_INVALID
     pa.pa_op_destroy(aop)
     # no new tokens: a no-op plan
     st, op = AppendCase(q_lens=[0, 0], kv_lens=[3, 0]).call()
@@ -710,23 +708,25 @@ def test_default_plan_ignores_environment(monkeypatch):
     assert before == after
 
 
-def test_workspace_holds_work_lists_then_partials():
-    """The workspace starts with the work lists (32-byte prefill / combine items, 48-byte
-    decode items, 256-aligned), followed by the split partials when there are any."""
+def test_workspace_holds_only_split_partials():
+    """The device workspace holds the split partials (fp32 O [slots, heads, D] and
+    (m, l) [slots, heads, 2], 256-aligned) and nothing else: the work lists (32-byte
+    prefill / combine items, 48-byte decode items) live in the op's pinned buffer."""
     info = base(kv_lens=[100, 37]).plan()                     # short: no split
     n = len(info["decode_items"])
-    assert info["partial_slots"] == 0
-    assert info["items_bytes"] == -(-48 * n // 256) * 256 == info["workspace_bytes"]
+    assert info["partial_slots"] == 0 and info["workspace_bytes"] == 0
+    assert info["items_bytes"] == -(-48 * n // 256) * 256
     info = base(kv_lens=[30000, 37]).plan()                   # long: split + combine
     assert info["partial_slots"] > 0
     n, m = len(info["decode_items"]), len(info["combine_items"])
     assert info["items_bytes"] == -(-48 * n // 256) * 256 + -(-32 * m // 256) * 256
-    parts = info["partial_slots"] * 4 * 128 * 4 + info["partial_slots"] * 4 * 2 * 4
-    assert info["workspace_bytes"] >= info["items_bytes"] + parts
-    assert info["workspace_bytes"] % 256 == 0
+    o = -(-info["partial_slots"] * 4 * 128 * 4 // 256) * 256
+    ml = -(-info["partial_slots"] * 4 * 2 * 4 // 256) * 256
+    assert info["workspace_bytes"] == o + ml
     info = Case(q_lens=[300], kv_lens=[300], H=4, Hkv=4, D=64, bs=16,
                 mask=pa.PA_MASK_CAUSAL).plan()
-    assert info["workspace_bytes"] == info["items_bytes"] == len(info["prefill_items"]) * 32
+    assert info["workspace_bytes"] == 0
+    assert info["items_bytes"] == -(-len(info["prefill_items"]) * 32 // 256) * 256
 
 
 @pytest.mark.parametrize("cus", [32, 64, 128, 256, 80])
@@ -743,3 +743,17 @@ def test_plans_for_smaller_devices(cus):
         d = base(kv_lens=[8000] * 16, q_lens=[1] * 16)
         dinfo = d.plan()
         _check_decode_plan(dinfo, [1] * 16, [8000] * 16, 2, 4)
+
+
+
+def test_timing_events_name_a_kernel_of_the_op():
+    """Timing events attach to the main kernel or the split-KV combine; other indices and
+    a NULL op are refused (host only, no HIP call)."""
+    st, _, op = base().call()
+    assert st == pa.PA_OK
+    lib = pa.load()
+    for k in (pa.PA_TIMED_MAIN, pa.PA_TIMED_COMBINE):
+        assert lib.pa_op_set_timing_events(op, k, None, None) == pa.PA_OK
+    assert lib.pa_op_set_timing_events(op, 2, None, None) == pa.PA_ERR_PARAM_INVALID
+    assert lib.pa_op_set_timing_events(None, 0, None, None) == pa.PA_ERR_NULLPTR
+    pa.pa_op_destroy(op)
