@@ -230,6 +230,19 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
                              void* stream);
 
 /*
+ * Phase 2 without a caller workspace, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels as pa_paged_attention, with the workspace taken from a static scratch
+ * array of the library (64 MiB, one per device, held until the process ends).  Allocates
+ * nothing; enqueues the kernels on `stream` and never waits.  Every call on one device uses that device's one scratch array: calls whose
+ * work overlaps on a device (other streams, or other threads) race and must be ordered
+ * by the caller.  An op whose phase-1 workspaceSize exceeds 64 MiB is refused with
+ * PA_ERR_WORKSPACE_TOO_SMALL (run it with pa_paged_attention).  Other errors as for
+ * pa_paged_attention.
+ */
+pa_status pa_paged_attention_static(pa_op* op, void* stream);
+
+/*
  * KV-cache append: write the new tokens' key/value rows into their cache blocks, the
  * step before a prefill / prefix-encoder call.  The pages print no API for it; this one
  * follows their cache layout and length conventions (aclnnFusedInferAttentionScoreV3,

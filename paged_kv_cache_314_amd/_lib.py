@@ -41,6 +41,7 @@ EXPORTED = (
     "pa_paged_attention_get_workspace_size",
     "pa_paged_attention_get_workspace_size_ex",
     "pa_paged_attention",
+    "pa_paged_attention_static",
     "pa_kv_cache_append_plan",
     "pa_kv_cache_append",
     "pa_op_destroy",
@@ -102,6 +103,8 @@ def load():
     lib.pa_paged_attention.restype = ctypes.c_int
     lib.pa_paged_attention.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                        ctypes.c_void_p]
+    lib.pa_paged_attention_static.restype = ctypes.c_int
+    lib.pa_paged_attention_static.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.pa_kv_cache_append_plan.restype = ctypes.c_int
     lib.pa_kv_cache_append_plan.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(ctypes.c_void_p)]
     lib.pa_kv_cache_append.restype = ctypes.c_int
@@ -253,6 +256,17 @@ def pa_paged_attention(workspace, workspace_size, op, stream=None):
     raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
     ptr = workspace.data_ptr() if workspace is not None and workspace.numel() > 0 else None
     _check(lib.pa_paged_attention(ptr, int(workspace_size), handle, raw))
+
+
+def pa_paged_attention_static(op, stream=None):
+    """Phase 2 with the library's static scratch as workspace (no allocation); on
+    ``stream`` (torch.cuda.Stream, raw handle int, or None = torch's current stream)."""
+    lib = load()
+    handle = op.handle if isinstance(op, Op) else op
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    raw = stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+    _check(lib.pa_paged_attention_static(handle, raw))
 
 
 def pa_kv_cache_append_plan(key_new, value_new, key_cache, value_cache, block_tables, seq_len,

@@ -201,6 +201,40 @@ pa_status check_execute(const pa_op* op, const unsigned char* ws, uint64_t ws_si
                                 : "the op has no work lists");
 }
 
+// ------------------------------------------------------- static scratch
+// Workspace of pa_paged_attention_static, for callers that cannot allocate: a file-scope
+// device array of kScratchBytes, one copy per device (each GPU the library runs on holds
+// its own until the process ends).  Host code never uses the array's name as an address
+// (on the host it is only a stand-in for the symbol): the device address of each copy is
+// taken once per device with hipGetSymbolAddress, with that device current, and kept.
+constexpr uint64_t kScratchBytes = uint64_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxScratchDevices] = {};
+
+pa_status scratch_on_device(int dev, unsigned char** out) {
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(PA_ERR_PARAM_INVALID, "device " + std::to_string(dev) + " out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || ptr == nullptr)
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                            "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = static_cast<unsigned char*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
 pa_status execute_attention(pa_op* op, unsigned char* ws, uint64_t workspaceSize, hipStream_t s);
 
 pa::AntiquantArgs antiquant_args(const pa::Plan& p) {
@@ -275,6 +309,27 @@ pa_status pa_paged_attention(void* workspace, uint64_t workspaceSize, pa_op* op,
         return fail(PA_ERR_PARAM_INVALID, "op is a KV-cache append plan: run it with pa_kv_cache_append");
     return execute_attention(op, static_cast<unsigned char*>(workspace), workspaceSize,
                              static_cast<hipStream_t>(stream));
+}
+
+pa_status pa_paged_attention_static(pa_op* op, void* stream) {
+    if (op == nullptr) return fail(PA_ERR_NULLPTR, "op is NULL");
+    const pa::Plan& p = op->plan;
+    if (p.mode == pa::Mode::kAppend)
+        return fail(PA_ERR_PARAM_INVALID, "op is a KV-cache append plan: run it with pa_kv_cache_append");
+    if (p.mode == pa::Mode::kNoop) return PA_OK;
+    if (p.workspace_bytes > kScratchBytes)
+        return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                    "the op needs " + std::to_string(p.workspace_bytes) +
+                        " bytes of workspace; the static scratch holds " + std::to_string(kScratchBytes) +
+                        ": call pa_paged_attention with a workspace");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    hipError_t e = hipStreamGetDevice(s, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    unsigned char* ws = nullptr;
+    pa_status st = scratch_on_device(dev, &ws);
+    if (st != PA_OK) return st;
+    return execute_attention(op, ws, kScratchBytes, s);
 }
 
 }  // extern "C"

@@ -757,3 +757,21 @@ def test_timing_events_name_a_kernel_of_the_op():
     assert lib.pa_op_set_timing_events(op, 2, None, None) == pa.PA_ERR_PARAM_INVALID
     assert lib.pa_op_set_timing_events(None, 0, None, None) == pa.PA_ERR_NULLPTR
     pa.pa_op_destroy(op)
+
+
+def test_static_execute_refuses_ops_beyond_its_scratch():
+    """pa_paged_attention_static holds 64 MiB of scratch: an op planned with a larger
+    workspace is refused before any HIP call (split partials of 8 sequences of 200k
+    tokens cut into single tiles need about 200 MB)."""
+    with pa.plan_options({pa.PA_OPT_DECODE_CHUNK_TILES: 1}):
+        c = base(q_lens=[1] * 8, kv_lens=[200000] * 8, H=8, Hkv=2)
+        st, ws, op = c.call()
+    assert st == pa.PA_OK and ws > 64 << 20
+    lib = pa.load()
+    assert lib.pa_paged_attention_static(op, None) == pa.PA_ERR_WORKSPACE_TOO_SMALL
+    assert "static scratch" in pa.pa_last_error()
+    assert lib.pa_paged_attention_static(None, None) == pa.PA_ERR_NULLPTR
+    pa.pa_op_destroy(op)
+    st, aop = AppendCase(q_lens=[2], kv_lens=[9]).call()
+    assert lib.pa_paged_attention_static(aop, None) == pa.PA_ERR_PARAM_INVALID
+    pa.pa_op_destroy(aop)
