@@ -327,8 +327,9 @@ pa_status pa_op_set_timing_events(pa_op* op, int kernel, void* start, void* stop
 /* Write a JSON description of the operator's plan into buf (NUL-terminated, cut at
  * cap - 1 bytes; buf may be NULL when cap is 0) and return the full length without the
  * NUL.  Keys: "mode" ("noop", "fill", "decode", "prefill", "append"), "workspace_bytes",
- * "items_bytes" (the pinned work lists), "compute_units" (planned for), "chunk_tiles", "partial_slots", and the work lists "decode_items"
- * [b, kvh, hg, t0, t1, slot, qrow, kvlen], "combine_items" [kvh, hg, slot0, nsplit, qrow],
+ * "items_bytes" (the pinned work lists), "compute_units" (planned for), "chunk_tiles",
+ * "partial_slots", and the work lists "decode_items" [b, kvh, hg, t0, t1, slot, qrow,
+ * kvlen, heads, slot_stride, comb, nsplit], "combine_items" [kvh, hg, slot0, nsplit, qrow],
  * "prefill_items" [b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads] (heads query heads from
  * h, 128/heads query rows from qbeg), "append_items" [b, row0, pos0, count], "antiquant"
  * [key mode, value mode, offsets given].  Host only, no HIP call.

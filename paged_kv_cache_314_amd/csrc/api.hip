@@ -173,8 +173,6 @@ pa_status make_host_lists(pa_op* op) {
     if (p.mode == pa::Mode::kDecode) {
         std::memcpy(base + p.off_items, p.decode_items.data(),
                     p.decode_items.size() * sizeof(pa::DecodeItem));
-        std::memcpy(base + p.off_combine, p.combine_items.data(),
-                    p.combine_items.size() * sizeof(pa::CombineItem));
     } else if (p.mode == pa::Mode::kPrefill) {
         std::memcpy(base + p.off_items, p.prefill_items.data(),
                     p.prefill_items.size() * sizeof(pa::PrefillItem));
@@ -378,6 +376,7 @@ pa_status execute_attention(pa_op* op, unsigned char* ws, uint64_t workspaceSize
         a.vscale = p.vscale;
         a.part_o = p.partial_slots ? reinterpret_cast<float*>(ws + p.off_part_o) : nullptr;
         a.part_ml = p.partial_slots ? reinterpret_cast<float*>(ws + p.off_part_ml) : nullptr;
+        a.comb = p.partial_slots ? reinterpret_cast<pa::CombineItem*>(ws + p.off_combine) : nullptr;
         a.q_tok_stride = p.q_tok_stride;
         a.q_head_stride = p.q_head_stride;
         a.out_tok_stride = p.out_tok_stride;
@@ -403,7 +402,7 @@ pa_status execute_attention(pa_op* op, unsigned char* ws, uint64_t workspaceSize
         if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
         if (combine) {
             pa::CombineArgs c{};
-            c.items = reinterpret_cast<const pa::CombineItem*>(lists + p.off_combine);
+            c.items = a.comb;
             c.part_o = a.part_o;
             c.part_ml = a.part_ml;
             c.out = p.out;
@@ -584,7 +583,8 @@ uint64_t pa_op_describe(const pa_op* op, char* buf, uint64_t cap) {
              ", " + std::to_string(d.t0) + ", " + std::to_string(d.t1) + ", " +
              std::to_string(d.slot) + ", " + std::to_string(d.qrow) + ", " +
              std::to_string(d.kvlen) + ", " + std::to_string(d.heads) + ", " +
-             std::to_string(d.slot_stride) + "]";
+             std::to_string(d.slot_stride) + ", " + std::to_string(d.comb) + ", " +
+             std::to_string(d.nsplit) + "]";
     }
     s += "], \"combine_items\": [";
     for (size_t i = 0; i < p.combine_items.size(); ++i) {

@@ -101,6 +101,18 @@ __global__ void __launch_bounds__(256, 2) decode_kernel(DecodeArgs a) {
     const DecodeItem it = a.items[blockIdx.x];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the first split of a split sequence hands the combine kernel its item (from device
+    // memory, so that the combine's workgroups need no read of the host work list)
+    if (it.comb >= 0 && it.t0 == 0 && lane == 0 && (WPH || wave == 0)) {
+        const int w = WPH ? wave : 0;
+        CombineItem c{};
+        c.kvh = it.kvh + w;
+        c.hg = it.hg;
+        c.slot0 = it.slot + w * it.slot_stride;
+        c.nsplit = it.nsplit;
+        c.qrow = it.qrow;
+        a.comb[it.comb + w] = c;
+    }
     const int kvh = it.kvh + (WPH ? wave : 0);  // this wave's kv head
     const int col = lane & 15;                 // packed head (QK/PV column)
     const int qg = lane >> 4;                  // lane group: k-slots 8*qg .. 8*qg+7

@@ -65,7 +65,9 @@ struct DecodeItem {
     int32_t kvlen;    // kvSeqLen[b]
     int32_t heads;    // 1 or 4 (see above)
     int32_t slot_stride;  // heads == 4: slot of kv head kvh + w is slot + w * slot_stride
-    int32_t pad[2];
+    int32_t comb;         // split sequences: index of the combine item of (kvh, hg) (of kv
+                          // head kvh + w: comb + w); -1 when the sequence is not split
+    int32_t nsplit;       // splits of the sequence (1: not split)
 };
 static_assert(sizeof(DecodeItem) == 48, "DecodeItem layout");
 
@@ -92,6 +94,45 @@ struct PrefillItem {
     int32_t heads;    // query heads sharing the workgroup's K/V tiles
 };
 static_assert(sizeof(PrefillItem) == 32, "PrefillItem layout");
+
+// Visiting order of a prefill wave's key tiles (plain constexpr arithmetic, used by the
+// kernel and checked on the host).  The wave owns local query rows wave_q0 ..
+// wave_q0 + 31 of a sequence with qlen queries and kvlen keys; its item visits key
+// tiles 0 .. T = ktiles - 1 (tiles of kPrefillBN keys), one per step k = 0 .. T:
+//   step 0: tile T, the one nearest the queries;
+//   steps 1 .. P: the P tiles holding only keys before the new tokens (visible to every
+//           query row under a causal mask), P - 1 down to 0;
+//   steps P + 1 .. T: the rest of the diagonal, T - 1 down to P.
+// Without a causal mask P = 0 and the order is T down to 0.  The wave computes only
+// tiles t <= t_act (its rows see no key of a higher tile; -1: none), and k_first is its
+// first computed step (its output accumulators are still zero there).
+struct PrefillVisit {
+    int T, t_act, P, k_first;
+};
+
+constexpr PrefillVisit prefill_visit(int ktiles, bool causal, int qlen, int kvlen, int wave_q0) {
+    const int T = ktiles - 1;
+    const int shift = kvlen - qlen;                 // position of local query 0
+    const int wave_q1 = (wave_q0 + 31 < qlen - 1) ? wave_q0 + 31 : qlen - 1;
+    const int wave_pmax = shift + wave_q1;          // highest position among the rows
+    const bool live = wave_q0 < qlen;
+    int t_act = -1;
+    if (live) {
+        if (!causal) t_act = T;
+        else if (wave_pmax >= 0) t_act = (T < wave_pmax / kPrefillBN) ? T : wave_pmax / kPrefillBN;
+    }
+    int P = 0;
+    if (causal && shift > 0) P = (shift / kPrefillBN < T) ? shift / kPrefillBN : T;
+    if (P < 0) P = 0;
+    // a live wave sees every prefix tile (t_act >= P), so after tile T the first tile it
+    // computes is P - 1 if there is a prefix, else the first diagonal tile <= t_act
+    const int k_first = (t_act == T) ? 0 : (P > 0 ? 1 : T - t_act);
+    return PrefillVisit{T, t_act, P, k_first};
+}
+
+constexpr int prefill_tile_of(const PrefillVisit& v, int k) {
+    return k == 0 ? v.T : (k <= v.P ? v.P - k : v.T - (k - v.P));
+}
 
 // Everything phase 2 needs; produced by plan().
 struct Plan {
@@ -144,11 +185,12 @@ struct Plan {
     int32_t partial_slots = 0;
     int32_t compute_units = 0;       // the device size the lists were made for
 
-    // work lists: in the op's pinned, device-mapped host buffer (offsets off_items,
-    // off_combine, items_bytes); the device workspace holds only the split-KV partials
-    // (off_part_o, off_part_ml); all 256-aligned
-    uint64_t off_items = 0, off_combine = 0, items_bytes = 0;
-    uint64_t off_part_o = 0, off_part_ml = 0, workspace_bytes = 0;
+    // work lists: in the op's pinned, device-mapped host buffer (offset off_items,
+    // items_bytes); the device workspace holds the split-KV partials (off_part_o,
+    // off_part_ml) and the combine items, written there by the decode kernel's first
+    // split of each (sequence, kv head, head group) (off_combine); all 256-aligned
+    uint64_t off_items = 0, items_bytes = 0;
+    uint64_t off_part_o = 0, off_part_ml = 0, off_combine = 0, workspace_bytes = 0;
 };
 
 // KV-cache append planning (validation + work list).  On failure returns a status and

@@ -34,6 +34,7 @@ struct DecodeArgs {
     const void* vscale;
     float* part_o;          // [slots][min(group,16)][D] un-normalised partial outputs
     float* part_ml;         // [slots][min(group,16)][2] partial (max, sum), log2 units
+    CombineItem* comb;      // the combine items, written by the first split of each group
     int64_t q_tok_stride, q_head_stride, out_tok_stride, out_head_stride, lse_tok_stride;
     int64_t k_blk_stride, k_slot_stride, k_head_stride;
     int64_t v_blk_stride, v_slot_stride, v_head_stride, table_stride;

@@ -593,6 +593,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
             // (kv head, head group) g owns partial slots slots + g*nsplit + s.  Items are
             // emitted head-major: the splits of one kv head (or head quad) launch together.
             const int32_t gstep = wph ? 4 : 1;
+            const int32_t comb0 = static_cast<int32_t>(p.combine_items.size());
             for (int32_t g = 0; g < groups; g += gstep) {
                 for (int32_t s = 0; s < nsplit; ++s) {
                     DecodeItem it{};
@@ -606,6 +607,8 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                     it.kvlen = klen;
                     it.heads = gstep;
                     it.slot_stride = nsplit;
+                    it.comb = nsplit > 1 ? comb0 + g : -1;
+                    it.nsplit = nsplit;
                     p.decode_items.push_back(it);
                 }
             }
@@ -630,14 +633,16 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                              return (x.t1 - x.t0) > (y.t1 - y.t0);
                          });
         const int64_t geff = std::min<int32_t>(p.group, kHeadPack);
-        // work lists: in the op's pinned host buffer; partials: in the device workspace
+        // work list: in the op's pinned host buffer; partials and combine items: in the
+        // device workspace
         p.off_items = 0;
-        p.off_combine = align256(p.decode_items.size() * sizeof(DecodeItem));
-        p.items_bytes = align256(p.off_combine + p.combine_items.size() * sizeof(CombineItem));
+        p.items_bytes = align256(p.decode_items.size() * sizeof(DecodeItem));
         p.off_part_o = off;
         off = align256(off + uint64_t(slots) * geff * qv.d * sizeof(float));
         p.off_part_ml = off;
         off = align256(off + uint64_t(slots) * geff * 2 * sizeof(float));
+        p.off_combine = off;
+        off = align256(off + p.combine_items.size() * sizeof(CombineItem));
         p.workspace_bytes = slots > 0 ? off : 0;
     } else {
         // ---- prefill: (sequence, query-head block, query-row tile) items, heaviest first.

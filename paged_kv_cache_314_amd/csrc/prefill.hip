@@ -104,10 +104,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     const int qi = wave_q0 + qcol;                          // local query row of this lane
     const bool qvalid = qi < qlen;
     const int pos = shift + qi;                             // its absolute position
-    const int wave_q1 = min(wave_q0 + 31, qlen - 1);        // last valid row of the wave
-    const bool wave_live = wave_q0 < qlen;
-    const int wave_pmin = shift + wave_q0;
-    const int wave_pmax = shift + wave_q1;
+    const int wave_pmin = shift + wave_q0;                  // lowest position of its rows
 
     // ---------------------------------------------------------------- Q^T
     u32x4 qhi[KS], qlo[KS];
@@ -604,34 +601,24 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // A wave works on tiles 0 .. t_act (the rows it owns see no key of a higher tile);
-    // tiles on the diagonal or past kvlen are masked.
-    const int T = it.ktiles - 1;
-    const int t_act = !wave_live ? -1
-                    : (!causal ? T : (wave_pmax < 0 ? -1 : min(T, wave_pmax / BN)));
+    // Visiting order (prefill_visit): the item's last tile T, the one nearest its
+    // queries, first -- under a causal mask (and even more with ALiBi, whose bias grows
+    // towards the diagonal) it holds the row maxima, so later tiles rarely re-base the
+    // running sums, and under ALiBi the tiles far from the queries are then recognised as
+    // negligible at once; then the P tiles holding only keys before the new tokens,
+    // P - 1 down to 0, which the workgroups of all query tiles of a head need and read
+    // side by side on one XCD, sharing them through its L2; then the rest of the
+    // diagonal.  A wave works on tiles 0 .. t_act (its rows see no key of a higher
+    // tile); tiles on the diagonal or past kvlen are masked.  Step k's buffer is k % 2.
+    const PrefillVisit vis = prefill_visit(it.ktiles, causal, qlen, kvlen, wave_q0);
+    const int T = vis.T;
+    const int t_act = vis.t_act;
     auto need_mask = [&](int t) {
         return (t * BN + BN > kvlen) || (causal && t * BN + BN - 1 > wave_pmin);
     };
 
-    // Visiting order.  Step k visits tile tile_of(k); its buffer is k % 2.
-    //  - First the item's last tile T, the one nearest its queries: under a causal mask
-    //    (and even more with ALiBi, whose bias grows towards the diagonal) it holds the
-    //    row maxima, so later tiles rarely re-base the running sums, and under ALiBi the
-    //    tiles far from the queries are then recognised as negligible at once.
-    //  - Then the P tiles that hold only keys before the new tokens (key j < kvlen -
-    //    seqLen is visible to every query row), from P - 1 down to 0: the workgroups of
-    //    all query tiles of a head need them and run side by side on one XCD, so they
-    //    stream these tiles at nearly the same time and share them through the L2.
-    //  - Then the rest of the item's diagonal tiles, from T - 1 down to P.
-    // Without a mask every tile is visible to every row: T down to 0.
-    const int shift_keys = kvlen - qlen;
-    const int P = (!causal) ? 0 : (shift_keys > 0 ? min(shift_keys / BN, T) : 0);
-    auto tile_of = [&](int k) {
-        return k == 0 ? T : (k <= P ? P - k : T - (k - P));
-    };
-    // the wave's first computed step (O and l are zero before it); a live wave sees
-    // every prefix tile (t_act >= P)
-    const int k_first = (t_act == T) ? 0 : (P > 0 ? 1 : T - t_act);
+    auto tile_of = [&](int k) { return prefill_tile_of(vis, k); };
+    const int k_first = vis.k_first;
     auto compute = [&](int t, int buf, bool first) {
         if (t <= t_act) {
             f32x16 sacc[2];

@@ -195,7 +195,16 @@ def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
     wph = info["decode_wave_heads"] == 1
     assert not wph or (Hkv % 4 == 0 and group <= 16)
     by_key = {}
-    for b, kvh, hg, t0, t1, slot, qrow, kvlen, heads, stride in items:
+    combs = info["combine_items"]
+    written = set()
+    for b, kvh, hg, t0, t1, slot, qrow, kvlen, heads, stride, comb, nsplit in items:
+        # the first split of each split group hands the combine kernel its item
+        if comb >= 0 and t0 == 0:
+            for w in range(heads):
+                assert combs[comb + w] == [kvh + w, hg, slot + w * stride, nsplit, qrow]
+                assert comb + w not in written
+                written.add(comb + w)
+        assert (comb >= 0) == (slot >= 0) and (nsplit > 1) == (slot >= 0)
         # an item of 4 kv heads stands for one range of each of kvh .. kvh+3
         assert heads == (4 if wph else 1)
         if heads == 4:
@@ -232,6 +241,7 @@ def _check_decode_plan(info, q_lens, kv_lens, Hkv, group):
                     assert c[2] == slots[0] and c[3] == len(parts)
     assert not by_key and not combines
     assert info["partial_slots"] == len(slots_seen)
+    assert written == set(range(len(combs)))
 
 
 def _check_xcd_order(items, xcds=8):
@@ -710,8 +720,9 @@ def test_default_plan_ignores_environment(monkeypatch):
 
 def test_workspace_holds_only_split_partials():
     """The device workspace holds the split partials (fp32 O [slots, heads, D] and
-    (m, l) [slots, heads, 2], 256-aligned) and nothing else: the work lists (32-byte
-    prefill / combine items, 48-byte decode items) live in the op's pinned buffer."""
+    (m, l) [slots, heads, 2]) and the 32-byte combine items, each region 256-aligned;
+    the work lists (32-byte prefill items, 48-byte decode items) live in the op's
+    pinned buffer."""
     info = base(kv_lens=[100, 37]).plan()                     # short: no split
     n = len(info["decode_items"])
     assert info["partial_slots"] == 0 and info["workspace_bytes"] == 0
@@ -719,10 +730,10 @@ def test_workspace_holds_only_split_partials():
     info = base(kv_lens=[30000, 37]).plan()                   # long: split + combine
     assert info["partial_slots"] > 0
     n, m = len(info["decode_items"]), len(info["combine_items"])
-    assert info["items_bytes"] == -(-48 * n // 256) * 256 + -(-32 * m // 256) * 256
+    assert info["items_bytes"] == -(-48 * n // 256) * 256
     o = -(-info["partial_slots"] * 4 * 128 * 4 // 256) * 256
     ml = -(-info["partial_slots"] * 4 * 2 * 4 // 256) * 256
-    assert info["workspace_bytes"] == o + ml
+    assert info["workspace_bytes"] == o + ml + -(-32 * m // 256) * 256
     info = Case(q_lens=[300], kv_lens=[300], H=4, Hkv=4, D=64, bs=16,
                 mask=pa.PA_MASK_CAUSAL).plan()
     assert info["workspace_bytes"] == 0
