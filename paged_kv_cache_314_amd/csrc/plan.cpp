@@ -7,7 +7,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
-#include <map>
+#include <memory>
 #include <sstream>
 #include <tuple>
 
@@ -170,40 +170,81 @@ uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 // tile through that L2 instead of each fetching it from HBM.  Clusters go to the least
 // loaded XCD, heaviest first; the per-XCD lists are padded to equal length with no-op
 // items (heads == 0) so that list x, entry k lands at position 8 * k + x.
+// Stable counting sort of `v` by key(x) descending (keys in [0, max_key]); the plans' sort
+// keys (tile counts, head indices) are small integers, so this replaces a comparison sort
+// of the work list in the per-step planning cost.  Falls back to std::stable_sort for a
+// key range above 2^16.
+template <typename T, typename Key>
+void counting_sort_desc(std::vector<T>& v, Key key) {
+    int64_t max_key = 0;
+    for (const T& x : v) max_key = std::max<int64_t>(max_key, key(x));
+    if (max_key > (int64_t(1) << 16)) {
+        std::stable_sort(v.begin(), v.end(), [&](const T& a, const T& b) { return key(a) > key(b); });
+        return;
+    }
+    std::vector<uint32_t> start(static_cast<size_t>(max_key) + 2, 0);
+    for (const T& x : v) ++start[static_cast<size_t>(max_key - key(x)) + 1];
+    for (size_t k = 1; k < start.size(); ++k) start[k] += start[k - 1];
+    // plain structs: an uninitialised buffer, filled once, copied back
+    std::unique_ptr<T[]> out(new T[v.size()]);
+    for (const T& x : v) out[start[static_cast<size_t>(max_key - key(x))]++] = x;
+    std::copy(out.get(), out.get() + v.size(), v.begin());
+}
+
 std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const PlanConfig& cfg) {
     const int kXcds = cfg.compute_units % kCusPerXcd == 0
                           ? std::max(1, std::min(8, cfg.compute_units / kCusPerXcd)) : 1;
     const size_t cus_per_xcd = static_cast<size_t>(cfg.compute_units / kXcds);
-    struct Cluster { int64_t work = 0; std::vector<PrefillItem> members; };
-    std::vector<Cluster> clusters;
-    {
-        // a cluster holds at most 1/8 of the items, so that a few large clusters (one
-        // long sequence, few heads) still spread over every XCD
-        const size_t cap = std::max<size_t>(1, (items.size() + kXcds - 1) / kXcds);
-        std::map<std::pair<int32_t, int32_t>, size_t> index;   // (b, h) -> open cluster
-        for (const PrefillItem& it : items) {   // items arrive heaviest first
-            auto ins = index.emplace(std::make_pair(it.b, it.h), clusters.size());
-            if (ins.second) {
-                clusters.emplace_back();
-            } else if (clusters[ins.first->second].members.size() == cap) {
-                ins.first->second = clusters.size();
-                clusters.emplace_back();
-            }
-            Cluster& c = clusters[ins.first->second];
-            c.work += int64_t(it.ktiles) + 1;
-            c.members.push_back(it);
-        }
+    const size_t n = items.size();
+    // clusters: the items of one (sequence, head block), in arrival order (heaviest
+    // first), at most 1/8 of the items each, so that a few large clusters (one long
+    // sequence, few heads) still spread over every XCD
+    const size_t cap = std::max<size_t>(1, (n + kXcds - 1) / kXcds);
+    int32_t maxb = 0, maxh = 0;
+    for (const PrefillItem& it : items) {
+        maxb = std::max(maxb, it.b);
+        maxh = std::max(maxh, it.h);
     }
-    std::stable_sort(clusters.begin(), clusters.end(),
-                     [](const Cluster& x, const Cluster& y) { return x.work > y.work; });
+    const size_t nh = static_cast<size_t>(maxh) + 1;
+    std::vector<int32_t> open((static_cast<size_t>(maxb) + 1) * nh, -1);   // key -> open cluster
+    std::vector<int32_t> cid(n);
+    std::vector<int64_t> work;
+    std::vector<uint32_t> size;
+    work.reserve(n);
+    size.reserve(n);
+    for (size_t i = 0; i < n; ++i) {
+        const PrefillItem& it = items[i];
+        int32_t& c = open[static_cast<size_t>(it.b) * nh + static_cast<size_t>(it.h)];
+        if (c < 0 || size[c] == cap) {
+            c = static_cast<int32_t>(work.size());
+            work.push_back(0);
+            size.push_back(0);
+        }
+        cid[i] = c;
+        work[c] += int64_t(it.ktiles) + 1;
+        ++size[c];
+    }
+    const size_t nc = work.size();
+    // cluster members in arrival order (counting by cluster)
+    std::vector<uint32_t> first(nc + 1, 0);
+    for (size_t c = 0; c < nc; ++c) first[c + 1] = first[c] + size[c];
+    std::vector<uint32_t> fill(first.begin(), first.end() - 1);
+    std::vector<uint32_t> members(n);
+    for (size_t i = 0; i < n; ++i) members[fill[cid[i]]++] = static_cast<uint32_t>(i);
+    // clusters heaviest first (creation order breaks ties), each to the least loaded XCD
+    std::vector<int32_t> order(nc);
+    for (size_t c = 0; c < nc; ++c) order[c] = static_cast<int32_t>(c);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return work[x] > work[y]; });
     std::vector<std::vector<PrefillItem>> lists(kXcds);
+    for (auto& l : lists) l.reserve(cap + cap / 2);
     std::vector<int64_t> load(kXcds, 0);
-    for (const Cluster& c : clusters) {
+    for (const int32_t c : order) {
         int x = 0;
         for (int i = 1; i < kXcds; ++i)
             if (load[i] < load[x]) x = i;
-        load[x] += c.work;
-        lists[x].insert(lists[x].end(), c.members.begin(), c.members.end());
+        load[x] += work[c];
+        for (uint32_t k = first[c]; k < first[c + 1]; ++k) lists[x].push_back(items[members[k]]);
     }
     // An XCD's list that fits one round (at most two workgroups per CU) is placed so that
     // each CU's pair of workgroups is one heavy and one light item: the hardware gives
@@ -216,9 +257,7 @@ std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const 
     if (pick(cfg.prefill_pair, true)) {
         for (auto& l : lists) {
             if (l.size() <= cus_per_xcd || l.size() > 2 * cus_per_xcd) continue;
-            std::stable_sort(l.begin(), l.end(), [](const PrefillItem& x, const PrefillItem& y) {
-                return x.ktiles > y.ktiles;
-            });
+            counting_sort_desc(l, [](const PrefillItem& x) { return int64_t(x.ktiles); });
             std::reverse(l.begin() + cus_per_xcd, l.end());
         }
     }
@@ -584,6 +623,20 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         if (cfg.decode_chunk_tiles > 0) chunk = cfg.decode_chunk_tiles;
         p.decode_chunk_tiles = chunk;
         int32_t slots = 0;
+        {
+            size_t n_items = 0, n_comb = 0;
+            for (int64_t b = 0; b < B; ++b) {
+                if (ql[b * qls] != 1) continue;
+                const int64_t tiles = (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
+                const int64_t nsplit = std::max<int64_t>(1, (tiles + chunk - 1) / chunk);
+                const int64_t groups = int64_t(kvh_num) * p.head_groups;
+                n_items += static_cast<size_t>((groups + (wph ? 3 : 0)) / (wph ? 4 : 1) * nsplit);
+                if (nsplit > 1) n_comb += static_cast<size_t>(groups);
+            }
+            p.decode_items.reserve(n_items);
+            p.combine_items.reserve(n_comb);
+        }
+        std::vector<int32_t> bounds;
         for (int64_t b = 0; b < B; ++b) {
             if (ql[b * qls] != 1) continue;
             const int32_t klen = kl[b * kls];
@@ -594,14 +647,19 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
             // emitted head-major: the splits of one kv head (or head quad) launch together.
             const int32_t gstep = wph ? 4 : 1;
             const int32_t comb0 = static_cast<int32_t>(p.combine_items.size());
+            // split s covers tiles [tiles * s / nsplit, tiles * (s + 1) / nsplit), the same
+            // for every kv head of the sequence
+            bounds.resize(static_cast<size_t>(nsplit) + 1);
+            for (int32_t s = 0; s <= nsplit; ++s)
+                bounds[s] = static_cast<int32_t>(int64_t(tiles) * s / nsplit);
             for (int32_t g = 0; g < groups; g += gstep) {
                 for (int32_t s = 0; s < nsplit; ++s) {
                     DecodeItem it{};
                     it.b = static_cast<int32_t>(b);
                     it.kvh = g / p.head_groups;
                     it.hg = g % p.head_groups;
-                    it.t0 = static_cast<int32_t>(int64_t(tiles) * s / nsplit);
-                    it.t1 = static_cast<int32_t>(int64_t(tiles) * (s + 1) / nsplit);
+                    it.t0 = bounds[s];
+                    it.t1 = bounds[s + 1];
                     it.slot = nsplit > 1 ? slots + g * nsplit + s : -1;
                     it.qrow = q0[b];
                     it.kvlen = klen;
@@ -628,10 +686,7 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         p.partial_slots = slots;
         // longest ranges first: the hardware hands out workgroups in launch order, so
         // this is a greedy longest-processing-time schedule and shortens the tail
-        std::stable_sort(p.decode_items.begin(), p.decode_items.end(),
-                         [](const DecodeItem& x, const DecodeItem& y) {
-                             return (x.t1 - x.t0) > (y.t1 - y.t0);
-                         });
+        counting_sort_desc(p.decode_items, [](const DecodeItem& x) { return int64_t(x.t1 - x.t0); });
         const int64_t geff = std::min<int32_t>(p.group, kHeadPack);
         // work list: in the op's pinned host buffer; partials and combine items: in the
         // device workspace
@@ -686,11 +741,9 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         // the launch (ALiBi prefix workload: 177 -> 160 us).  For other slope orders
         // this is only a different tie-break.
         const bool head_desc = maskType == PA_MASK_ALIBI;
-        std::stable_sort(p.prefill_items.begin(), p.prefill_items.end(),
-                         [head_desc](const PrefillItem& x, const PrefillItem& y) {
-                             if (x.ktiles != y.ktiles) return x.ktiles > y.ktiles;
-                             return head_desc && x.h > y.h;
-                         });
+        // (two stable counting passes: by head, then by tile count)
+        if (head_desc) counting_sort_desc(p.prefill_items, [](const PrefillItem& x) { return int64_t(x.h); });
+        counting_sort_desc(p.prefill_items, [](const PrefillItem& x) { return int64_t(x.ktiles); });
         if (pick(cfg.prefill_xcd_order, true)) p.prefill_items = xcd_order(p.prefill_items, cfg);
         p.off_items = 0;
         p.items_bytes = align256(p.prefill_items.size() * sizeof(PrefillItem));
