@@ -659,12 +659,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
 
     // ------------------------------------------------------------- epilogue
+    // O = O^T / l, rounded to the output type, goes through LDS so that the global
+    // stores write whole rows: a lane holds 4-element pieces of one query row, and
+    // storing those directly leaves 32 rows half-written per instruction.  Each wave
+    // stages its 32 x D tile in its own quarter of the K/V buffer pair that no wave reads
+    // any more (buffer (T + 1) % 2: its last tile was consumed before the last barrier
+    // and nothing is loaded into it afterwards), 16-byte chunks of row r placed at chunk
+    // c ^ (r % NCH) so that both the 8-byte writes and the 16-byte reads are free of
+    // bank conflicts.
     const float L = sum_halves(l_run);
-    if (!qvalid) return;
     const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-    uint16_t* orow = static_cast<uint16_t*>(a.out) +
-                     static_cast<int64_t>(it.qrow0 + qi) * a.out_tok_stride +
-                     static_cast<int64_t>(h) * a.out_head_stride;
+    constexpr int NCH = D / 8;                  // 16-byte chunks per output row
+    uint16_t* stage = ((wave < 2) ? s_k[(T + 1) & 1] : s_v[(T + 1) & 1]) + (wave & 1) * (32 * D);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -690,9 +696,29 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             u32x2 w;
             w.x = pack2<BF16>(o[0], o[1]);
             w.y = pack2<BF16>(o[2], o[3]);
-            *reinterpret_cast<u32x2*>(orow + d0) = w;
+            const int chunk = (dt * 4 + r4) ^ (qcol % NCH);
+            *reinterpret_cast<u32x2*>(stage + qcol * D + chunk * 8 + 4 * g2) = w;
         }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+        constexpr int RPI = 64 / NCH;           // rows per store instruction
+        const int c = lane % NCH;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int r = i * RPI + lane / NCH;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * D + (c ^ (r % NCH)) * 8);
+            if (wave_q0 + r < qlen) {
+                uint16_t* orow = static_cast<uint16_t*>(a.out) +
+                                 static_cast<int64_t>(it.qrow0 + wave_q0 + r) * a.out_tok_stride +
+                                 static_cast<int64_t>(h) * a.out_head_stride;
+                *reinterpret_cast<u32x4*>(orow + 8 * c) = x;
+            }
+        }
+    }
+    if (!qvalid) return;
     if (g2 == 0 && a.lse != nullptr) {
         a.lse[static_cast<int64_t>(it.qrow0 + qi) * a.lse_tok_stride + h] =
             (L > 0.0f) ? (m_ref + kconst + fast_log2(L)) * kLn2 : INFINITY;
