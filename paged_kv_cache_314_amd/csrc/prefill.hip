@@ -45,9 +45,15 @@ namespace {
 constexpr int BN = kPrefillBN;          // 64 keys per tile
 constexpr float kRescaleSlack = 8.0f;   // log2 units a row max may exceed its reference
 constexpr float kNegligible = 32.0f;    // log2 units below the reference: weight < 2^-32
+// ALiBi: a prefix tile whose bias lies more than this many log2 units below that of the
+// workgroup's nearest key, for every row and key, is expected to be negligible, and its V
+// rows are not loaded unless a row turns out to need them
+constexpr float kFarBias = 48.0f;
 // s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
+// the same for lgkmcnt(0) with vmcnt / expcnt at their maxima
+constexpr int kWaitLgkmcnt0 = 0xC07F;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16;
@@ -82,6 +88,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
     __shared__ uint16_t s_k[2][BN * KLD];
     __shared__ uint16_t s_v[2][BN * VLD];
+    __shared__ int s_vote[4];             // per wave: 1 = its rows need the tile's V
 
     const PrefillItem it = a.items[blockIdx.x];
     if (it.heads == 0) return;            // padding item of the XCD-ordered list
@@ -391,7 +398,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 reinterpret_cast<lvoid*>(reinterpret_cast<uintptr_t>(dst + RPI * i * ld)), 16, 0, 0);
         }
     };
-    auto load_tile_direct = [&](int buf, int t) {
+    auto load_tile_direct = [&](int buf, int t, bool with_k, bool with_v) {
         const int j0 = t * BN;
         const int g0 = j0 + 16 * wave;
         int gb = g0;
@@ -410,8 +417,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         const char *kb, *vb;
         if (j0 + BN <= kvlen) {
             bases(kb, vb);
-            issue_group(kb, s_k[buf] + 16 * wave * KLD, KLD, koff_full);
-            issue_group(vb, s_v[buf] + 16 * wave * VLD, VLD, voff_full);
+            if (with_k) issue_group(kb, s_k[buf] + 16 * wave * KLD, KLD, koff_full);
+            if (with_v) issue_group(vb, s_v[buf] + 16 * wave * VLD, VLD, voff_full);
         } else {
             // tail tile (wave-uniform branch): rows past kvlen re-read row kvlen - 1
             asm volatile("" ::: "memory");
@@ -425,8 +432,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 vo[i] = lane_off(i, src, vslot32, false);
             }
             bases(kb, vb);
-            issue_group(kb, s_k[buf] + 16 * wave * KLD, KLD, ko);
-            issue_group(vb, s_v[buf] + 16 * wave * VLD, VLD, vo);
+            if (with_k) issue_group(kb, s_k[buf] + 16 * wave * KLD, KLD, ko);
+            if (with_v) issue_group(vb, s_v[buf] + 16 * wave * VLD, VLD, vo);
         }
     };
 
@@ -619,25 +626,60 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
     auto tile_of = [&](int k) { return prefill_tile_of(vis, k); };
     const int k_first = vis.k_first;
+    // ALiBi over 16-bit K/V: prefix tiles predicted negligible for the whole workgroup
+    // from the smallest slope of its heads and the distance between its first query row
+    // and the tile's last key (the same decision in every wave).  Their V rows are not
+    // loaded with the tile; if a row of the workgroup does see a weight there after all,
+    // the waves agree on it through LDS and load V before its P V.
+    float wg_slope2 = 0.0f;
+    if constexpr (alibi && DIRECT) {
+        wg_slope2 = INFINITY;
+        for (int i = 0; i < heads; ++i) wg_slope2 = fminf(wg_slope2, a.slopes[it.h + i] * kLog2e);
+    }
+    const int wg_pmin = shift + it.qbeg;
+    auto far = [&](int t) {
+        if constexpr (alibi && DIRECT) {
+            return t < vis.P && wg_slope2 * static_cast<float>(wg_pmin - (t * BN + BN - 1)) > kFarBias;
+        } else {
+            return false;
+        }
+    };
     auto compute = [&](int t, int buf, bool first) {
-        if (t <= t_act) {
-            f32x16 sacc[2];
-            u32x4 pop[4];
+        const bool act = t <= t_act;
+        f32x16 sacc[2];
+        u32x4 pop[4];
+        bool neg = true;
+        if (act) {
             qk(buf, sacc);
-            if (!scores(sacc, t * BN, need_mask(t), first)) {
-                probs(sacc, pop);
-                pv(pop, buf);
+            neg = scores(sacc, t * BN, need_mask(t), first);
+        }
+        if constexpr (alibi && DIRECT) {
+            if (far(t)) {
+                // V not loaded: every wave votes, and only if one needs V is it loaded
+                if (lane == 0) s_vote[wave] = (act && !neg) ? 1 : 0;
+                __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);   // the vote is in LDS; the tile
+                // loads in flight stay in flight (no fence, so no vmcnt(0) here)
+                asm volatile("s_barrier" ::: "memory");
+                const bool need = (s_vote[0] | s_vote[1] | s_vote[2] | s_vote[3]) != 0;
+                if (!need) return;
+                load_tile_direct(buf, t, false, true);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                __syncthreads();
             }
+        }
+        if (act && !neg) {
+            probs(sacc, pop);
+            pv(pop, buf);
         }
     };
     if constexpr (DIRECT) {
         // the loads into buffer (k+1) % 2 start after the barrier that follows every read
         // of that buffer's previous tile (step k - 1); vmcnt(0) + barrier publish them
-        if (T >= 0) load_tile_direct(0, tile_of(0));
+        if (T >= 0) load_tile_direct(0, tile_of(0), true, !far(tile_of(0)));
         for (int k = 0; k <= T; ++k) {
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
-            if (k < T) load_tile_direct((k + 1) & 1, tile_of(k + 1));
+            if (k < T) load_tile_direct((k + 1) & 1, tile_of(k + 1), true, !far(tile_of(k + 1)));
             compute(tile_of(k), k & 1, k == k_first);
         }
     } else {
