@@ -10,6 +10,8 @@
 #include <memory>
 #include <sstream>
 #include <tuple>
+#include <utility>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -594,13 +596,14 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         const bool wph_auto = total_tiles >= 64 * cus;
         const bool wph = wph_ok && pick(cfg.decode_wave_heads, wph_auto);
         p.decode_wave_heads = wph ? 1 : 0;
-        // chunk = tiles one item gives each wave's share of work: about `target`
-        // workgroups in all, and a multiple of 4 tiles.  Wave-per-head items are 4x
-        // larger; with nearly equal sequence lengths one full round of resident
-        // workgroups is best (uneven lengths need two rounds for balance): one workgroup
-        // per CU for one-byte caches with per-channel scales, whose 128-byte rows read
-        // with fewer concurrent streams keep more DRAM page locality; two per CU
-        // otherwise (the general-antiquant kernel needs them to hide its latency).
+        // About `target` workgroups in all.  Wave-per-head items cover four kv heads.
+        // The path is bound by HBM, which stays saturated while about one workgroup per
+        // CU is still streaming, and every item pays a start-up latency: so few, long
+        // items.  With nearly equal sequence lengths: one item per CU (fewer concurrent
+        // streams also keep more DRAM page locality); uneven lengths: three per CU, the
+        // lone ones at the end absorbing the imbalance.  The general-antiquant kernel
+        // (per-token scales or offsets) needs two workgroups per CU to hide its latency:
+        // two and four per CU.
         int64_t max_tiles = 0, n_dec = 0;
         for (int64_t b = 0; b < B; ++b) {
             if (ql[b * qls] != 1) continue;
@@ -612,36 +615,89 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         const bool lean_bytes = p.kvtype != PA_F16 && p.kvtype != PA_BF16 &&
                                 p.kmode == PA_ANTIQUANT_PER_CHANNEL &&
                                 p.vmode == PA_ANTIQUANT_PER_CHANNEL && p.koff == nullptr;
-        const int rounds = wph ? (even ? (lean_bytes ? 1 : 2) : 4) : 0;
+        const bool general_antiquant = (p.kvtype == PA_I8 || p.kvtype == PA_F8E4M3) && !lean_bytes;
+        const int rounds = wph ? (even ? (general_antiquant ? 2 : 1) : (general_antiquant ? 4 : 3)) : 0;
         const int target = cfg.decode_target_items > 0
                                ? cfg.decode_target_items
                                : static_cast<int>(wph ? rounds * cus : 8 * cus);
-        const int64_t per_item = (total_tiles + target - 1) / target;      // kv-head tiles
-        int chunk = static_cast<int>(std::min<int64_t>(wph ? (per_item + 3) / 4 : per_item, 1 << 20));
-        chunk = std::max(chunk, 8);          // short sequences: no split, no combine
-        chunk = (chunk + 3) / 4 * 4;
-        if (cfg.decode_chunk_tiles > 0) chunk = cfg.decode_chunk_tiles;
-        p.decode_chunk_tiles = chunk;
+        // Splits per sequence.  A forced chunk size (plan option) gives
+        // ceil(tiles / chunk).  Otherwise the target item count is shared out by largest
+        // remainder: every sequence gets at least one split and at most one per 8 tiles,
+        // and each further split goes to the sequence whose splits are longest, so the
+        // items come out nearly equal in length and as many as targeted (a fixed chunk
+        // leaves lengths between half a chunk and a chunk, and rounds the count down).
+        const int64_t groups_all = int64_t(kvh_num) * p.head_groups;
+        const int64_t per_split = wph ? (groups_all + 3) / 4 : groups_all;   // items per split
+        std::vector<int32_t> nsplit_of(static_cast<size_t>(B), 1);
+        int32_t max_chunk = 0;
+        if (cfg.decode_chunk_tiles > 0) {
+            const int32_t chunk = cfg.decode_chunk_tiles;
+            for (int64_t b = 0; b < B; ++b) {
+                if (ql[b * qls] != 1) continue;
+                const int32_t tiles = (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
+                nsplit_of[b] = std::max<int32_t>(1, (tiles + chunk - 1) / chunk);
+            }
+            max_chunk = chunk;
+        } else if (n_dec > 0) {
+            const int64_t want = std::max<int64_t>(n_dec, (target + per_split / 2) / per_split);
+            const int64_t seq_tiles = total_tiles / groups_all;          // tiles over all sequences
+            int64_t have = 0;
+            for (int64_t b = 0; b < B; ++b) {
+                if (ql[b * qls] != 1) continue;
+                const int64_t tiles = (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
+                const int64_t cap = std::max<int64_t>(1, tiles / 8);
+                const int64_t share = seq_tiles > 0 ? tiles * want / seq_tiles : 1;
+                nsplit_of[b] = static_cast<int32_t>(std::min(cap, std::max<int64_t>(1, share)));
+                have += nsplit_of[b];
+            }
+            // the remaining splits, one at a time, to the sequence with the longest splits
+            // that may still take one (ties: lowest index, for a deterministic plan)
+            using Entry = std::pair<int64_t, int64_t>;    // (tiles * 2^20 / nsplit, -b)
+            std::vector<Entry> heap;
+            auto key = [&](int64_t b) {
+                const int64_t tiles = (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
+                return Entry((tiles << 20) / nsplit_of[b], -b);
+            };
+            for (int64_t b = 0; b < B; ++b) {
+                if (ql[b * qls] != 1) continue;
+                const int64_t tiles = (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
+                if (nsplit_of[b] < std::max<int64_t>(1, tiles / 8)) heap.push_back(key(b));
+            }
+            std::make_heap(heap.begin(), heap.end());
+            while (have < want && !heap.empty()) {
+                std::pop_heap(heap.begin(), heap.end());
+                const int64_t b = -heap.back().second;
+                heap.pop_back();
+                ++nsplit_of[b];
+                ++have;
+                const int64_t tiles = (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
+                if (nsplit_of[b] < std::max<int64_t>(1, tiles / 8)) {
+                    heap.push_back(key(b));
+                    std::push_heap(heap.begin(), heap.end());
+                }
+            }
+        }
         int32_t slots = 0;
         {
             size_t n_items = 0, n_comb = 0;
             for (int64_t b = 0; b < B; ++b) {
                 if (ql[b * qls] != 1) continue;
-                const int64_t tiles = (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
-                const int64_t nsplit = std::max<int64_t>(1, (tiles + chunk - 1) / chunk);
-                const int64_t groups = int64_t(kvh_num) * p.head_groups;
-                n_items += static_cast<size_t>((groups + (wph ? 3 : 0)) / (wph ? 4 : 1) * nsplit);
-                if (nsplit > 1) n_comb += static_cast<size_t>(groups);
+                const int32_t tiles = (kl[b * kls] + kDecodeTile - 1) / kDecodeTile;
+                const int64_t nsplit = nsplit_of[b];
+                max_chunk = std::max<int32_t>(max_chunk, static_cast<int32_t>((tiles + nsplit - 1) / nsplit));
+                n_items += static_cast<size_t>(per_split * nsplit);
+                if (nsplit > 1) n_comb += static_cast<size_t>(groups_all);
             }
             p.decode_items.reserve(n_items);
             p.combine_items.reserve(n_comb);
         }
+        p.decode_chunk_tiles = max_chunk;
         std::vector<int32_t> bounds;
         for (int64_t b = 0; b < B; ++b) {
             if (ql[b * qls] != 1) continue;
             const int32_t klen = kl[b * kls];
             const int32_t tiles = (klen + kDecodeTile - 1) / kDecodeTile;
-            const int32_t nsplit = std::max<int32_t>(1, (tiles + chunk - 1) / chunk);
+            const int32_t nsplit = nsplit_of[b];
             const int32_t groups = kvh_num * p.head_groups;
             // (kv head, head group) g owns partial slots slots + g*nsplit + s.  Items are
             // emitted head-major: the splits of one kv head (or head quad) launch together.
