@@ -18,8 +18,8 @@ sq: the MFMA math operations the kernel executed (SQ_INSTS_VALU_MFMA_MOPS_*, eac
 (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD times the SIMD count).
 
 Both merge into profiles/KERNEL_WORKLOAD_counters.json, keyed by the hash of the
-kernel's sources (bench.py reads it for roofline.traffic and roofline.executed and
-ignores it once the sources change), and print a short text summary.
+kernel's sources and the planner's (bench.py reads it for roofline.traffic and
+roofline.executed and ignores it once either changes), and print a short text summary.
 """
 
 import csv
@@ -30,11 +30,13 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "paged_kv_cache_314_amd", "csrc")
+# a kernel's counters depend on its code and on the work lists the planner gives it
+PLAN_SOURCES = ["plan.cpp", "pa_internal.h"]
 KERNEL_SOURCES = {
-    "decode_kernel": ["decode.hip", "pa_device.h"],
-    "combine_kernel": ["decode.hip", "pa_device.h"],
-    "prefill_kernel": ["prefill.hip", "pa_device.h"],
-    "append_kernel": ["append.hip", "pa_device.h"],
+    "decode_kernel": ["decode.hip", "pa_device.h"] + PLAN_SOURCES,
+    "combine_kernel": ["decode.hip", "pa_device.h"] + PLAN_SOURCES,
+    "prefill_kernel": ["prefill.hip", "pa_device.h"] + PLAN_SOURCES,
+    "append_kernel": ["append.hip", "pa_device.h"] + PLAN_SOURCES,
 }
 COPY_KERNEL = "copyBuffer"
 XCDS = 8                     # MI355X: 8 accelerator complex dies
@@ -43,7 +45,7 @@ MOPS_UNIT = 512              # flops per SQ_INSTS_VALU_MFMA_MOPS_* count
 
 
 def kernel_source_hash(kind):
-    """sha256 (first 16 hex digits) of the sources a kernel is built from."""
+    """sha256 (first 16 hex digits) of the sources a kernel and its work lists come from."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind]:
         with open(os.path.join(CSRC, name), "rb") as f:
