@@ -757,6 +757,45 @@ def test_plans_for_smaller_devices(cus):
 
 
 
+@pytest.mark.parametrize("cus", [256, 80])
+def test_decode_items_per_cu_and_near_equal(cus):
+    """Wave-per-head decode items: one per CU when the sequence lengths are nearly equal,
+    three per CU when they are not (at least one split per sequence), shared out by
+    largest remainder so that the longest item stays near the mean; a forced chunk
+    length or item target still applies."""
+    with pa.plan_options({pa.PA_OPT_COMPUTE_UNITS: cus}):
+        rng = np.random.default_rng(7)
+        uneven = rng.integers(1024, 8193, size=64).tolist()
+        for kv, per_cu in (([4608] * 64, 1), (uneven, 3)):
+            c = Case(q_lens=[1] * 64, kv_lens=kv, H=32, Hkv=8, D=128, bs=128,
+                     dtype=pa.PA_BF16, kv_dtype=pa.PA_BF16)
+            info = c.plan()
+            _check_decode_plan(info, [1] * 64, kv, 8, 4)
+            items = info["decode_items"]
+            # an item covers four of the 8 kv heads, and every sequence takes a split
+            assert len(items) == 2 * max(64, (per_cu * cus + 1) // 2)
+            lens = [it[4] - it[3] for it in items]
+            # the longest item (which bounds the launch) is as short as the count allows:
+            # taking a split away from any sequence would leave an item at least as long
+            nsplit = {it[0]: it[11] for it in items}
+            tiles = {b: -(-kv[b] // 32) for b in nsplit}
+            longest = max(lens)
+            assert longest == max(-(-tiles[b] // nsplit[b]) for b in nsplit)
+            for b, m in nsplit.items():
+                if m > 1:
+                    assert -(-tiles[b] // (m - 1)) >= longest, (b, m, tiles[b], longest)
+            if per_cu == 1:
+                assert max(lens) == min(lens)
+            assert lens == sorted(lens, reverse=True)            # longest first
+        with pa.plan_options({pa.PA_OPT_DECODE_CHUNK_TILES: 40}):
+            info = c.plan()
+            _check_decode_plan(info, [1] * 64, uneven, 8, 4)
+            assert max(it[4] - it[3] for it in info["decode_items"]) <= 40
+        with pa.plan_options({pa.PA_OPT_DECODE_TARGET_ITEMS: 1000}):
+            info = c.plan()
+            assert len(info["decode_items"]) == 1000
+
+
 def test_timing_events_name_a_kernel_of_the_op():
     """Timing events attach to the main kernel or the split-KV combine; other indices and
     a NULL op are refused (host only, no HIP call)."""
