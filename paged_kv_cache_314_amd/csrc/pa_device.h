@@ -211,12 +211,68 @@ __device__ __forceinline__ float dot2_ones(uint32_t a, float c) {
     }
 }
 
+// c + the sum of squares of the two 16-bit values of dword a, in f32 (the squares are
+// exact, the sums are f32).
+template <bool BF16>
+__device__ __forceinline__ float dot2_self(uint32_t a, float c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, a), c, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
+                                      __builtin_bit_cast(f16x2_t, a), c, false);
+    }
+}
+
 // --------------------------------------------------------------------- misc
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, 64);
+}
+
+// v from the lane that DPP control `ctrl` names (quad_perm / row_ror: every lane has a
+// source inside its row, so no lane keeps its own value)
+template <int ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, ctrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRor4 = 0x124;    // row_ror:4
+constexpr int kDppRor8 = 0x128;    // row_ror:8
+
+// sum over the 4 lanes of each quad (every lane of the quad gets it)
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp_f<kDppXor1>(v);
+    return v + dpp_f<kDppXor2>(v);
+}
+
+// max / min over the 64 lanes of the wave (wave-uniform result): DPP within each row of
+// 16 lanes, then the four rows' values through v_readlane
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppRor4>(v));
+    v = fmaxf(v, dpp_f<kDppRor8>(v));
+    const int x = __builtin_bit_cast(int, v);
+    return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 16))),
+                 fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 48))));
+}
+__device__ __forceinline__ float wave_min(float v) {
+    v = fminf(v, dpp_f<kDppXor1>(v));
+    v = fminf(v, dpp_f<kDppXor2>(v));
+    v = fminf(v, dpp_f<kDppRor4>(v));
+    v = fminf(v, dpp_f<kDppRor8>(v));
+    const int x = __builtin_bit_cast(int, v);
+    return fminf(fminf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 0)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 16))),
+                 fminf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 32)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(x, 48))));
 }
 
 // Select the lo (even element) or hi (odd element) 16-bit halves of two dwords.

@@ -45,13 +45,16 @@ namespace {
 constexpr int BN = kPrefillBN;          // 64 keys per tile
 constexpr float kRescaleSlack = 8.0f;   // log2 units a row max may exceed its reference
 constexpr float kNegligible = 32.0f;    // log2 units below the reference: weight < 2^-32
-// ALiBi: a prefix tile whose bias lies more than this many log2 units below that of the
-// workgroup's nearest key, for every row and key, is expected to be negligible, and its V
-// rows are not loaded unless a row turns out to need them
-constexpr float kFarBias = 48.0f;
+// ALiBi over 16-bit K/V: prefix tiles whose bias lies more than this many log2 units
+// below that of the workgroup's nearest key, for every row and key, form the far run, in
+// which a bound on the scores usually shows a tile negligible from its K rows' norms alone
+// (64: few far tiles then fail the bound and have to be computed)
+constexpr float kFarBias = 64.0f;
 // s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
+// vmcnt(n) with expcnt / lgkmcnt at their maxima (n < 64: bits 3:0 and 15:14)
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // the same for lgkmcnt(0) with vmcnt / expcnt at their maxima
 constexpr int kWaitLgkmcnt0 = 0xC07F;
 
@@ -86,9 +89,16 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     constexpr int NL = 16 * CH / 64;      // 16-byte loads per lane for a 16-key group
     constexpr int EPC = 16 / ESZ;         // elements per 16-byte chunk
 
-    __shared__ uint16_t s_k[2][BN * KLD];
-    __shared__ uint16_t s_v[2][BN * VLD];
+    // K tiles in slots 0 and 1, V tiles in slots 2 and 3 (for 16-bit K/V the four slots
+    // are alike, and the far run of an ALiBi item holds K tiles in all four)
+    __shared__ uint16_t s_kv[2 * BN * KLD + 2 * BN * VLD];
     __shared__ int s_vote[4];             // per wave: 1 = its rows need the tile's V
+    // far run of an ALiBi item: per wave, the largest |k|^2 of its 16 rows of the tile (by
+    // step parity), the smallest reference among its query rows, and the largest
+    // |s_mul q| among them
+    __shared__ float s_kmax[2][4], s_mmin[2][4], s_qmax[4];
+    auto kbuf = [](int b) { return s_kv + b * (BN * KLD); };
+    auto vbuf = [](int b) { return s_kv + 2 * (BN * KLD) + b * (BN * VLD); };
 
     const PrefillItem it = a.items[blockIdx.x];
     if (it.heads == 0) return;            // padding item of the XCD-ordered list
@@ -216,6 +226,20 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     }
 
+    // far run of an ALiBi item: the largest |s_mul q| among the wave's query rows (lane l
+    // and l ^ 32 hold the two halves of row l % 32), published by the first barrier
+    if constexpr (alibi && DIRECT) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss = dot2_self<MBF>(qhi[ks][e], ss);
+        }
+        ss += shfl_xor_f(ss, 32);
+        const float qn = wave_max(qvalid ? sqrtf(ss) : 0.0f);
+        if (lane == 0) s_qmax[wave] = qn * fabsf(s_mul);
+    }
+
     // ---------------------------------------------------------- tile loads
     // Wave w stages keys 16w .. 16w+15 of each tile.  They lie in one cache block, so
     // the block base is uniform and each lane reads at fixed offsets from it.
@@ -317,7 +341,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     };
     auto store_k = [&](int buf) {
-        uint16_t* ks = s_k[buf] + lds_k;
+        uint16_t* ks = kbuf(buf) + lds_k;
         if (ktok) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) put_tok(ks + RPI * i * KLD, kreg[i], ktok_s[i], ktok_o[i]);
@@ -336,7 +360,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < NL; ++i)
                 if (j0 + 16 * wave + RPI * i + lrow >= kvlen) vreg[i] = u32x4{0u, 0u, 0u, 0u};
         }
-        uint16_t* vs = s_v[buf] + lds_v;
+        uint16_t* vs = vbuf(buf) + lds_v;
         if (vtok) {
             // rows past kvlen: zero after the dequant (their P is 0; keep them finite)
 #pragma unroll
@@ -398,6 +422,20 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 reinterpret_cast<lvoid*>(reinterpret_cast<uintptr_t>(dst + RPI * i * ld)), 16, 0, 0);
         }
     };
+    // the same loads issued as asm, for the far run of an ALiBi item: the compiler, which
+    // cannot tell which slot a later LDS read touches, then adds no vmcnt(0) of its own
+    // before those reads, and the far run keeps three tiles in flight with explicit
+    // waits (no output register; the s_nop covers the M0 write before the load)
+    auto issue_group_async = [&](const char* base, uint16_t* dst, int ld, const uint32_t (&off)[NL]) {
+        uint64_t bi = reinterpret_cast<uintptr_t>(base);
+        asm volatile("" : "+s"(bi));
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + RPI * i * ld));
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                         :: "v"(off[i]), "s"(bi), "{m0}"(lds) : "memory");
+        }
+    };
     auto load_tile_direct = [&](int buf, int t, bool with_k, bool with_v) {
         const int j0 = t * BN;
         const int g0 = j0 + 16 * wave;
@@ -417,8 +455,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         const char *kb, *vb;
         if (j0 + BN <= kvlen) {
             bases(kb, vb);
-            if (with_k) issue_group(kb, s_k[buf] + 16 * wave * KLD, KLD, koff_full);
-            if (with_v) issue_group(vb, s_v[buf] + 16 * wave * VLD, VLD, voff_full);
+            if (with_k) issue_group(kb, kbuf(buf) + 16 * wave * KLD, KLD, koff_full);
+            if (with_v) issue_group(vb, vbuf(buf) + 16 * wave * VLD, VLD, voff_full);
         } else {
             // tail tile (wave-uniform branch): rows past kvlen re-read row kvlen - 1
             asm volatile("" ::: "memory");
@@ -432,9 +470,21 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 vo[i] = lane_off(i, src, vslot32, false);
             }
             bases(kb, vb);
-            if (with_k) issue_group(kb, s_k[buf] + 16 * wave * KLD, KLD, ko);
-            if (with_v) issue_group(vb, s_v[buf] + 16 * wave * VLD, VLD, vo);
+            if (with_k) issue_group(kb, kbuf(buf) + 16 * wave * KLD, KLD, ko);
+            if (with_v) issue_group(vb, vbuf(buf) + 16 * wave * VLD, VLD, vo);
         }
+    };
+
+    // far run: the wave's 16 K (or V) rows of full tile t into slot `slot`, as asm loads
+    auto load_far = [&](int slot, int t, bool v) {
+        const int g0 = t * BN + 16 * wave;
+        const int blk = bshift >= 0 ? (g0 >> bshift)
+                                    : static_cast<int>(static_cast<uint32_t>(g0) / static_cast<uint32_t>(bs));
+        const uint32_t slotoff = static_cast<uint32_t>(g0 - blk * bs);
+        const uint64_t e = static_cast<uint32_t>(ctab[blk]);
+        uint16_t* dst = s_kv + slot * (BN * KLD) + 16 * wave * KLD;
+        if (!v) issue_group_async(kpool + e * static_cast<uint64_t>(kblk_bytes) + slotoff * kslot32, dst, KLD, koff_full);
+        else issue_group_async(vpool + e * static_cast<uint64_t>(vblk_bytes) + slotoff * vslot32, dst, VLD, voff_full);
     };
 
     // element offset of 16-byte chunk c of K / V tile row r
@@ -463,10 +513,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     uint32_t kaddr[KS];
 #pragma unroll
     for (int ks_i = 0; ks_i < KS; ++ks_i)
-        kaddr[ks_i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_k[0])) +
+        kaddr[ks_i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kbuf(0))) +
                       2u * kpos(qcol, 2 * ks_i + g2);
 
-    // ---- stage 1: S^T = K Q^T for the K tile in s_k[buf] (plus the ALiBi term)
+    // ---- stage 1: S^T = K Q^T for the K tile in slot buf (plus the ALiBi term)
     auto qk = [&](int buf, f32x16 (&sacc)[2]) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -589,11 +639,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         l_run += (psum[0] + psum[1]) + (psum[2] + psum[3]);
     };
 
-    // ---- O^T += V^T P^T with the V tile in s_v[buf], V^T operands by transposed reads of
+    // ---- O^T += V^T P^T with the V tile at vs, V^T operands by transposed reads of
     //      row-major V: the first read gives keys 16kt + 4*g2 + 0..3, the second
     //      16kt + 8 + 4*g2 + 0..3
-    auto pv = [&](const u32x4 (&pop)[4], int buf) {
-        const uint16_t* vs = s_v[buf];
+    auto pv = [&](const u32x4 (&pop)[4], const uint16_t* vs) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
@@ -626,11 +675,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
     auto tile_of = [&](int k) { return prefill_tile_of(vis, k); };
     const int k_first = vis.k_first;
-    // ALiBi over 16-bit K/V: prefix tiles predicted negligible for the whole workgroup
-    // from the smallest slope of its heads and the distance between its first query row
-    // and the tile's last key (the same decision in every wave).  Their V rows are not
-    // loaded with the tile; if a row of the workgroup does see a weight there after all,
-    // the waves agree on it through LDS and load V before its P V.
+    // ALiBi over 16-bit K/V: the far run.  Prefix tiles whose bias, at the smallest
+    // slope of the workgroup's heads and the distance from its first query row to the
+    // tile's last key, lies more than kFarBias below the nearest key's are expected to be
+    // negligible for every row; they are the tiles 0 .. t_far - 1, which the visit order
+    // takes last among the prefix tiles, in one run of steps.
     float wg_slope2 = 0.0f;
     if constexpr (alibi && DIRECT) {
         wg_slope2 = INFINITY;
@@ -638,50 +687,127 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
     const int wg_pmin = shift + it.qbeg;
     auto far = [&](int t) {
-        if constexpr (alibi && DIRECT) {
-            return t < vis.P && wg_slope2 * static_cast<float>(wg_pmin - (t * BN + BN - 1)) > kFarBias;
-        } else {
-            return false;
-        }
+        return t < vis.P && wg_slope2 * static_cast<float>(wg_pmin - (t * BN + BN - 1)) > kFarBias;
     };
     auto compute = [&](int t, int buf, bool first) {
-        const bool act = t <= t_act;
-        f32x16 sacc[2];
-        u32x4 pop[4];
-        bool neg = true;
-        if (act) {
+        if (t <= t_act) {
+            f32x16 sacc[2];
+            u32x4 pop[4];
             qk(buf, sacc);
-            neg = scores(sacc, t * BN, need_mask(t), first);
-        }
-        if constexpr (alibi && DIRECT) {
-            if (far(t)) {
-                // V not loaded: every wave votes, and only if one needs V is it loaded
-                if (lane == 0) s_vote[wave] = (act && !neg) ? 1 : 0;
-                __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);   // the vote is in LDS; the tile
-                // loads in flight stay in flight (no fence, so no vmcnt(0) here)
-                asm volatile("s_barrier" ::: "memory");
-                const bool need = (s_vote[0] | s_vote[1] | s_vote[2] | s_vote[3]) != 0;
-                if (!need) return;
-                load_tile_direct(buf, t, false, true);
-                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-                __syncthreads();
+            if (!scores(sacc, t * BN, need_mask(t), first)) {
+                probs(sacc, pop);
+                pv(pop, vbuf(buf));
             }
         }
-        if (act && !neg) {
-            probs(sacc, pop);
-            pv(pop, buf);
-        }
     };
-    if constexpr (DIRECT) {
-        // the loads into buffer (k+1) % 2 start after the barrier that follows every read
-        // of that buffer's previous tile (step k - 1); vmcnt(0) + barrier publish them
-        if (T >= 0) load_tile_direct(0, tile_of(0), true, !far(tile_of(0)));
-        for (int k = 0; k <= T; ++k) {
+    // plain double-buffered steps k0 .. k1 - 1: tile k in K slot k % 2 and V slot 2 + k % 2;
+    // the loads into slot (k+1) % 2 start after the barrier that follows every read of its
+    // previous tile (step k - 1); vmcnt(0) + barrier publish them
+    auto plain_steps = [&](int k0, int k1) {
+        if (k0 < k1) load_tile_direct(k0 & 1, tile_of(k0), true, true);
+        for (int k = k0; k < k1; ++k) {
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
-            if (k < T) load_tile_direct((k + 1) & 1, tile_of(k + 1), true, !far(tile_of(k + 1)));
+            if (k + 1 < k1) load_tile_direct((k + 1) & 1, tile_of(k + 1), true, true);
             compute(tile_of(k), k & 1, k == k_first);
         }
+    };
+    if constexpr (DIRECT && alibi) {
+        int t_far = 0;                  // far(t) holds for t < t_far (it falls with t)
+        if (wg_slope2 > 0.0f)
+            while (t_far < vis.P && far(t_far)) ++t_far;
+        if (t_far == 0) {
+            plain_steps(0, T + 1);
+        } else {
+            // steps 0 .. kB - 1 (tile T, prefix tiles P - 1 .. t_far), the far run
+            // (tiles t_far - 1 .. 0), then the diagonal tiles T - 1 .. P
+            const int kB = vis.P - t_far + 1;
+            plain_steps(0, kB);
+            // the smallest reference among the workgroup's query rows, taken here and
+            // again after every computed far tile (references only grow)
+            {
+                const float mm = wave_min(qvalid ? m_ref : INFINITY);
+                if (lane == 0) s_mmin[0][wave] = mm;
+            }
+            __syncthreads();            // every wave is done with the last plain tile
+            float mmin = fminf(fminf(s_mmin[0][0], s_mmin[0][1]), fminf(s_mmin[0][2], s_mmin[0][3]));
+            // far tile f (tile t_far - 1 - f, step kB + f) goes to slot f % 4, three
+            // tiles ahead; each step checks the bound on its tile's scores (Cauchy-Schwarz:
+            // max |s_mul q| * max |k| + the tile's largest bias, below every row's
+            // reference by more than kNegligible + 1 for rounding) and skips the tile when
+            // it holds, else computes it: Q K^T in its slot, a vote on whether a row needs
+            // its V, and if one does V loaded into the same slot for P V
+            const int F = t_far;
+            constexpr int NKN = D / 32;             // 16-byte chunks per quarter row
+            constexpr int kLoadsPerTile = NL;       // one wave's loads of one K (or V) group
+            for (int f = 0; f < 3 && f < F; ++f) load_far(f, t_far - 1 - f, false);
+            for (int f = 0; f < F; ++f) {
+                const int t = t_far - 1 - f, slot = f & 3, par = f & 1;
+                const int later = (F - 1 - f < 2) ? F - 1 - f : 2;   // far tiles after f in flight
+                if (later == 2) __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerTile));
+                else if (later == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoadsPerTile));
+                else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                asm volatile("" ::: "memory");      // no LDS read moves above the wait
+                // the bound's per-wave parts: the largest |k| of the 16 rows this wave
+                // loaded (its own LDS-DMA writes are complete after its wait; lane l
+                // reads a quarter of row l / 4, the quarters' chunks in any order), the
+                // smallest reference among its query rows
+                const uint16_t* kr = s_kv + slot * (BN * KLD) + (16 * wave + (lane >> 2)) * KLD + 8 * NKN * (lane & 3);
+                float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int i = 0; i < NKN; ++i) {
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(kr + 8 * i);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ss[e] = dot2_self<MBF>(x[e], ss[e]);
+                }
+                // squared norms: the square root is taken once, after the exchange
+                const float kx2 = wave_max(quad_sum((ss[0] + ss[1]) + (ss[2] + ss[3])));
+                if (lane == 0) s_kmax[par][wave] = kx2;
+                // the parts are in LDS; the far tiles in flight stay in flight
+                __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+                asm volatile("s_barrier" ::: "memory");
+                if (f + 3 < F) load_far((f + 3) & 3, t - 3, false);   // the slot of tile f - 1
+                const float qmax = fmaxf(fmaxf(s_qmax[0], s_qmax[1]), fmaxf(s_qmax[2], s_qmax[3]));
+                const float kmax = sqrtf(fmaxf(fmaxf(s_kmax[par][0], s_kmax[par][1]),
+                                               fmaxf(s_kmax[par][2], s_kmax[par][3])));
+                const float bound = qmax * kmax + wg_slope2 * static_cast<float>(t * BN + BN - 1 - wg_pmin);
+                if (bound < mmin - kNegligible - 1.0f) continue;
+                // the bound does not hold: compute the tile
+                const int k = kB + f;
+                const bool act = t <= t_act;
+                f32x16 sacc[2];
+                u32x4 pop[4];
+                bool neg = true;
+                if (act) {
+                    qk(slot, sacc);
+                    neg = scores(sacc, t * BN, need_mask(t), k == k_first);
+                }
+                // the vote, and the references as this tile may have raised them
+                const float mm = wave_min(qvalid ? m_ref : INFINITY);
+                if (lane == 0) {
+                    s_vote[wave] = (act && !neg) ? 1 : 0;
+                    s_mmin[1][wave] = mm;
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+                asm volatile("s_barrier" ::: "memory");
+                const bool need = (s_vote[0] | s_vote[1] | s_vote[2] | s_vote[3]) != 0;
+                mmin = fminf(fminf(s_mmin[1][0], s_mmin[1][1]), fminf(s_mmin[1][2], s_mmin[1][3]));
+                if (!need) continue;
+                // every wave is past its Q K^T: the tile's V rows go into its slot
+                load_far(slot, t, true);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                __syncthreads();
+                if (act && !neg) {
+                    probs(sacc, pop);
+                    pv(pop, s_kv + slot * (BN * KLD));
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();            // every wave is done with the far slots
+            plain_steps(vis.P + 1, T + 1);
+        }
+    } else if constexpr (DIRECT) {
+        plain_steps(0, T + 1);
     } else {
         if (T >= 0) {
             load_k(tile_of(0));
@@ -712,7 +838,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     const float L = sum_halves(l_run);
     const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
     constexpr int NCH = D / 8;                  // 16-byte chunks per output row
-    uint16_t* stage = ((wave < 2) ? s_k[(T + 1) & 1] : s_v[(T + 1) & 1]) + (wave & 1) * (32 * D);
+    uint16_t* stage = ((wave < 2) ? kbuf((T + 1) & 1) : vbuf((T + 1) & 1)) + (wave & 1) * (32 * D);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
