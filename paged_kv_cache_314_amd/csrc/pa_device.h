@@ -250,6 +250,20 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v + dpp_f<kDppXor2>(v);
 }
 
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane i <- lane 7 - i of its 8
+constexpr int kDppMirror = 0x140;       // row_mirror: lane i <- lane 15 - i of its 16
+
+// sum over each aligned group of N lanes (N = 4, 8 or 16; every lane of the group gets
+// it): the quad sums, then the mirrored half, then the mirrored row
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+    v = quad_sum(v);
+    if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_f<kDppMirror>(v);
+    return v;
+}
+
 // max / min over the 64 lanes of the wave (wave-uniform result): DPP within each row of
 // 16 lanes, then the four rows' values through v_readlane
 __device__ __forceinline__ float wave_max(float v) {

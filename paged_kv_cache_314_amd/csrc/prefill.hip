@@ -53,10 +53,6 @@ constexpr float kFarBias = 64.0f;
 // s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
-// vmcnt(n) with expcnt / lgkmcnt at their maxima (n < 64: bits 3:0 and 15:14)
-constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-// the same for lgkmcnt(0) with vmcnt / expcnt at their maxima
-constexpr int kWaitLgkmcnt0 = 0xC07F;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16;
@@ -92,11 +88,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     // K tiles in slots 0 and 1, V tiles in slots 2 and 3 (for 16-bit K/V the four slots
     // are alike, and the far run of an ALiBi item holds K tiles in all four)
     __shared__ uint16_t s_kv[2 * BN * KLD + 2 * BN * VLD];
-    __shared__ int s_vote[4];             // per wave: 1 = its rows need the tile's V
-    // far run of an ALiBi item: per wave, the largest |k|^2 of its 16 rows of the tile (by
-    // step parity), the smallest reference among its query rows, and the largest
-    // |s_mul q| among them
-    __shared__ float s_kmax[2][4], s_mmin[2][4], s_qmax[4];
+    // far run of an ALiBi item: per wave, the smallest largest-score-so-far among its
+    // query rows, the largest |s_mul q| among them, and the first and last far tile its
+    // rows leave uncovered
+    __shared__ float s_mmin[4], s_qmax[4];
+    __shared__ int s_frange[2][4];
     auto kbuf = [](int b) { return s_kv + b * (BN * KLD); };
     auto vbuf = [](int b) { return s_kv + 2 * (BN * KLD) + b * (BN * VLD); };
 
@@ -422,20 +418,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                 reinterpret_cast<lvoid*>(reinterpret_cast<uintptr_t>(dst + RPI * i * ld)), 16, 0, 0);
         }
     };
-    // the same loads issued as asm, for the far run of an ALiBi item: the compiler, which
-    // cannot tell which slot a later LDS read touches, then adds no vmcnt(0) of its own
-    // before those reads, and the far run keeps three tiles in flight with explicit
-    // waits (no output register; the s_nop covers the M0 write before the load)
-    auto issue_group_async = [&](const char* base, uint16_t* dst, int ld, const uint32_t (&off)[NL]) {
-        uint64_t bi = reinterpret_cast<uintptr_t>(base);
-        asm volatile("" : "+s"(bi));
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst + RPI * i * ld));
-            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                         :: "v"(off[i]), "s"(bi), "{m0}"(lds) : "memory");
-        }
-    };
     auto load_tile_direct = [&](int buf, int t, bool with_k, bool with_v) {
         const int j0 = t * BN;
         const int g0 = j0 + 16 * wave;
@@ -475,18 +457,6 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // far run: the wave's 16 K (or V) rows of full tile t into slot `slot`, as asm loads
-    auto load_far = [&](int slot, int t, bool v) {
-        const int g0 = t * BN + 16 * wave;
-        const int blk = bshift >= 0 ? (g0 >> bshift)
-                                    : static_cast<int>(static_cast<uint32_t>(g0) / static_cast<uint32_t>(bs));
-        const uint32_t slotoff = static_cast<uint32_t>(g0 - blk * bs);
-        const uint64_t e = static_cast<uint32_t>(ctab[blk]);
-        uint16_t* dst = s_kv + slot * (BN * KLD) + 16 * wave * KLD;
-        if (!v) issue_group_async(kpool + e * static_cast<uint64_t>(kblk_bytes) + slotoff * kslot32, dst, KLD, koff_full);
-        else issue_group_async(vpool + e * static_cast<uint64_t>(vblk_bytes) + slotoff * vslot32, dst, VLD, voff_full);
-    };
-
     // element offset of 16-byte chunk c of K / V tile row r
     auto kpos = [&](int r, int c) { return r * KLD + 8 * (DIRECT ? (c ^ kswz(r)) : c); };
     auto vpos = [&](int r, int c) { return r * VLD + 8 * (DIRECT ? (c ^ vswz(r)) : c); };
@@ -498,6 +468,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
     // --------------------------------------------------------------- state
     float m_ref = -INFINITY;              // reference row max (log2 units)
+    float m_top = -INFINITY;              // largest score of the row so far (ALiBi far run)
     float l_run = 0.0f;
     f32x16 oacc[DT];
 #pragma unroll
@@ -596,6 +567,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[mt][r]);
         }
         tmax = max_halves(tmax);
+        if constexpr (alibi && DIRECT) m_top = fmaxf(m_top, mo + tmax);
         const bool grow = (tmax > kRescaleSlack) || (m_ref == -INFINITY && tmax > -INFINITY);
         bool negligible = false;
         if constexpr (alibi && !I8) negligible = !__any(grow || tmax >= -kNegligible);
@@ -666,7 +638,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     // side by side on one XCD, sharing them through its L2; then the rest of the
     // diagonal.  A wave works on tiles 0 .. t_act (its rows see no key of a higher
     // tile); tiles on the diagonal or past kvlen are masked.  Step k's buffer is k % 2.
-    const PrefillVisit vis = prefill_visit(it.ktiles, causal, qlen, kvlen, wave_q0);
+    PrefillVisit vis = prefill_visit(it.ktiles, causal, qlen, kvlen, wave_q0);
     const int T = vis.T;
     const int t_act = vis.t_act;
     auto need_mask = [&](int t) {
@@ -674,7 +646,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     };
 
     auto tile_of = [&](int k) { return prefill_tile_of(vis, k); };
-    const int k_first = vis.k_first;
+    int k_first = vis.k_first;
     // ALiBi over 16-bit K/V: the far run.  Prefix tiles whose bias, at the smallest
     // slope of the workgroup's heads and the distance from its first query row to the
     // tile's last key, lies more than kFarBias below the nearest key's are expected to be
@@ -716,95 +688,114 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         int t_far = 0;                  // far(t) holds for t < t_far (it falls with t)
         if (wg_slope2 > 0.0f)
             while (t_far < vis.P && far(t_far)) ++t_far;
+        t_far = __builtin_amdgcn_readfirstlane(t_far);      // the same in every lane
         if (t_far == 0) {
             plain_steps(0, T + 1);
         } else {
-            // steps 0 .. kB - 1 (tile T, prefix tiles P - 1 .. t_far), the far run
-            // (tiles t_far - 1 .. 0), then the diagonal tiles T - 1 .. P
-            const int kB = vis.P - t_far + 1;
-            plain_steps(0, kB);
-            // the smallest reference among the workgroup's query rows, taken here and
-            // again after every computed far tile (references only grow)
+            // the near tiles first, T down to t_far (the diagonal, then the prefix tiles
+            // near enough to matter), double-buffered as in plain_steps, so that every row
+            // holds its reference from its nearest keys; the far run (tiles t_far - 1 ..
+            // 0) last
+            const int n_near = T - t_far + 1;
+            vis.P = 0;                  // the plain visit order is then T, T - 1, ...
+            k_first = (t_act >= t_far) ? T - t_act : n_near;        // first tile it sees
+            plain_steps(0, n_near);
+            // the smallest row maximum among the workgroup's query rows
             {
-                const float mm = wave_min(qvalid ? m_ref : INFINITY);
-                if (lane == 0) s_mmin[0][wave] = mm;
+                const float mm = wave_min(qvalid ? m_top : INFINITY);
+                if (lane == 0) s_mmin[wave] = mm;
             }
             __syncthreads();            // every wave is done with the last plain tile
-            float mmin = fminf(fminf(s_mmin[0][0], s_mmin[0][1]), fminf(s_mmin[0][2], s_mmin[0][3]));
-            // far tile f (tile t_far - 1 - f, step kB + f) goes to slot f % 4, three
-            // tiles ahead; each step checks the bound on its tile's scores (Cauchy-Schwarz:
-            // max |s_mul q| * max |k| + the tile's largest bias, below every row's
-            // reference by more than kNegligible + 1 for rounding) and skips the tile when
-            // it holds, else computes it: Q K^T in its slot, a vote on whether a row needs
-            // its V, and if one does V loaded into the same slot for P V
+            const float mmin = fminf(fminf(s_mmin[0], s_mmin[1]), fminf(s_mmin[2], s_mmin[3]));
+            // The far run in two passes.  Pass A: every wave streams its own 16 K rows of
+            // each far tile into registers (no LDS, no barrier) and bounds the tile's
+            // scores against those rows (Cauchy-Schwarz: |s_mul q . k| <= max |s_mul q| *
+            // |k|, plus the tile's largest bias).  A tile whose bound lies below every
+            // row's largest score so far by more than kNegligible + 1 (the 1 for rounding)
+            // adds weights under 2^-33 of a row's largest, which l already holds, and
+            // re-bases no row: it is skipped.  The bound holds for the tile when it holds
+            // for each wave's rows, so a wave keeps only the first and the last far tile
+            // its rows leave uncovered.  Pass B: after one barrier, the tiles from the
+            // first to the last uncovered one of any wave are computed as plain tiles.
             const int F = t_far;
-            constexpr int NKN = D / 32;             // 16-byte chunks per quarter row
-            constexpr int kLoadsPerTile = NL;       // one wave's loads of one K (or V) group
-            for (int f = 0; f < 3 && f < F; ++f) load_far(f, t_far - 1 - f, false);
-            for (int f = 0; f < F; ++f) {
-                const int t = t_far - 1 - f, slot = f & 3, par = f & 1;
-                const int later = (F - 1 - f < 2) ? F - 1 - f : 2;   // far tiles after f in flight
-                if (later == 2) __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * kLoadsPerTile));
-                else if (later == 1) __builtin_amdgcn_s_waitcnt(wait_vmcnt(kLoadsPerTile));
-                else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-                asm volatile("" ::: "memory");      // no LDS read moves above the wait
-                // the bound's per-wave parts: the largest |k| of the 16 rows this wave
-                // loaded (its own LDS-DMA writes are complete after its wait; lane l
-                // reads a quarter of row l / 4, the quarters' chunks in any order), the
-                // smallest reference among its query rows
-                const uint16_t* kr = s_kv + slot * (BN * KLD) + (16 * wave + (lane >> 2)) * KLD + 8 * NKN * (lane & 3);
-                float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            const float qmax = fmaxf(fmaxf(s_qmax[0], s_qmax[1]), fmaxf(s_qmax[2], s_qmax[3]));
+            const float thr = mmin - kNegligible - 1.0f;
+            using gu32x4 = const __attribute__((address_space(1))) u32x4;
+            // the wave's rows of far tile f, load i covering row RPI*i + lrow (chunks in
+            // the swizzled order of the LDS loads: a permutation inside each row); the
+            // uniform base and the lane's 32-bit offset give the scalar-base load form
+            auto far_load = [&](u32x4 (&x)[NL], int f) {
+                const int g0 = (t_far - 1 - f) * BN + 16 * wave;
+                const int blk = bshift >= 0 ? (g0 >> bshift)
+                                            : static_cast<int>(static_cast<uint32_t>(g0) / static_cast<uint32_t>(bs));
+                const uint32_t slotoff = static_cast<uint32_t>(g0 - blk * bs);
+                const uint64_t e = static_cast<uint32_t>(ctab[blk]);
+                uint64_t bi = reinterpret_cast<uintptr_t>(kpool + e * static_cast<uint64_t>(kblk_bytes) + slotoff * kslot32);
+                asm volatile("" : "+s"(bi));
 #pragma unroll
-                for (int i = 0; i < NKN; ++i) {
-                    const u32x4 x = *reinterpret_cast<const u32x4*>(kr + 8 * i);
+                for (int i = 0; i < NL; ++i) {
+                    uint32_t o = koff_full[i];
+                    asm volatile("" : "+v"(o));
+                    x[i] = *reinterpret_cast<gu32x4*>(bi + o);
+                }
+            };
+            // tile f's bound against the wave's rows: row RPI*i + lrow has |k|^2 = the sum
+            // of the lane's 8 squares over the CH lanes holding its chunks, and the bound
+            // holds for it iff |k|^2 < lim^2 (NaN fails)
+            int f_lo = F, f_hi = -1;                // the wave's first / last uncovered tile
+            auto check = [&](const u32x4 (&x)[NL], int f) {
+                float rs[NL];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) ss[e] = dot2_self<MBF>(x[e], ss[e]);
+                for (int i = 0; i < NL; ++i) {
+                    float ss = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ss = dot2_self<MBF>(x[i][e], ss);
+                    rs[i] = group_sum<CH>(ss);
                 }
-                // squared norms: the square root is taken once, after the exchange
-                const float kx2 = wave_max(quad_sum((ss[0] + ss[1]) + (ss[2] + ss[3])));
-                if (lane == 0) s_kmax[par][wave] = kx2;
-                // the parts are in LDS; the far tiles in flight stay in flight
-                __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
-                asm volatile("s_barrier" ::: "memory");
-                if (f + 3 < F) load_far((f + 3) & 3, t - 3, false);   // the slot of tile f - 1
-                const float qmax = fmaxf(fmaxf(s_qmax[0], s_qmax[1]), fmaxf(s_qmax[2], s_qmax[3]));
-                const float kmax = sqrtf(fmaxf(fmaxf(s_kmax[par][0], s_kmax[par][1]),
-                                               fmaxf(s_kmax[par][2], s_kmax[par][3])));
-                const float bound = qmax * kmax + wg_slope2 * static_cast<float>(t * BN + BN - 1 - wg_pmin);
-                if (bound < mmin - kNegligible - 1.0f) continue;
-                // the bound does not hold: compute the tile
-                const int k = kB + f;
-                const bool act = t <= t_act;
-                f32x16 sacc[2];
-                u32x4 pop[4];
-                bool neg = true;
-                if (act) {
-                    qk(slot, sacc);
-                    neg = scores(sacc, t * BN, need_mask(t), k == k_first);
+                const int t = t_far - 1 - f;
+                const float lim = (thr - wg_slope2 * static_cast<float>(t * BN + BN - 1 - wg_pmin)) / qmax;
+                const float lim2 = lim > 0.0f ? lim * lim : -1.0f;
+                bool ok = true;
+#pragma unroll
+                for (int i = 0; i < NL; ++i) ok = ok && (rs[i] < lim2);
+                if (__any(!ok)) {
+                    f_lo = f_lo < f ? f_lo : f;
+                    f_hi = f;
                 }
-                // the vote, and the references as this tile may have raised them
-                const float mm = wave_min(qvalid ? m_ref : INFINITY);
-                if (lane == 0) {
-                    s_vote[wave] = (act && !neg) ? 1 : 0;
-                    s_mmin[1][wave] = mm;
-                }
-                __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
-                asm volatile("s_barrier" ::: "memory");
-                const bool need = (s_vote[0] | s_vote[1] | s_vote[2] | s_vote[3]) != 0;
-                mmin = fminf(fminf(s_mmin[1][0], s_mmin[1][1]), fminf(s_mmin[1][2], s_mmin[1][3]));
-                if (!need) continue;
-                // every wave is past its Q K^T: the tile's V rows go into its slot
-                load_far(slot, t, true);
-                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-                __syncthreads();
-                if (act && !neg) {
-                    probs(sacc, pop);
-                    pv(pop, s_kv + slot * (BN * KLD));
+            };
+            // kDepth tiles in flight; the loads are unconditional (an index past the run
+            // re-reads its last tile), which keeps the compiler's waits exact
+            constexpr int kDepth = 4;
+            u32x4 xb[kDepth][NL];
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) far_load(xb[d], d < F ? d : F - 1);
+            int f0 = 0;
+            for (; f0 + kDepth < F; f0 += kDepth) {
+#pragma unroll
+                for (int d = 0; d < kDepth; ++d) {
+                    check(xb[d], f0 + d);
+                    const int fn = f0 + d + kDepth;
+                    far_load(xb[d], fn < F ? fn : F - 1);
                 }
             }
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __syncthreads();            // every wave is done with the far slots
-            plain_steps(vis.P + 1, T + 1);
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d)
+                if (f0 + d < F) check(xb[d], f0 + d);
+            if (lane == 0) {
+                s_frange[0][wave] = f_lo;
+                s_frange[1][wave] = f_hi;
+            }
+            __syncthreads();
+            const int lo = __builtin_amdgcn_readfirstlane(
+                min(min(s_frange[0][0], s_frange[0][1]), min(s_frange[0][2], s_frange[0][3])));
+            const int hi = __builtin_amdgcn_readfirstlane(
+                max(max(s_frange[1][0], s_frange[1][1]), max(s_frange[1][2], s_frange[1][3])));
+            if (lo <= hi) {
+                // Pass B (plain step k visits tile T - k); the barrier frees the buffers
+                // for the epilogue
+                plain_steps(n_near + lo, n_near + hi + 1);
+                __syncthreads();
+            }
         }
     } else if constexpr (DIRECT) {
         plain_steps(0, T + 1);
