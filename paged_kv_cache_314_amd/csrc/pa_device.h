@@ -232,12 +232,13 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
-// v from the lane that DPP control `ctrl` names (quad_perm / row_ror: every lane has a
-// source inside its row, so no lane keeps its own value)
+// v from the lane that DPP control `ctrl` names (quad_perm / row_ror / mirrors: every
+// lane has a source inside its row, so bound_ctrl, which zeroes lanes without one,
+// changes nothing; it lets the compiler fold the move into the instruction that uses it)
 template <int ctrl>
 __device__ __forceinline__ float dpp_f(float v) {
     const int x = __builtin_bit_cast(int, v);
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, ctrl, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, ctrl, 0xF, 0xF, true));
 }
 constexpr int kDppXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]

@@ -739,25 +739,27 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
                     x[i] = *reinterpret_cast<gu32x4*>(bi + o);
                 }
             };
-            // tile f's bound against the wave's rows: row RPI*i + lrow has |k|^2 = the sum
-            // of the lane's 8 squares over the CH lanes holding its chunks, and the bound
-            // holds for it iff |k|^2 < lim^2 (NaN fails)
+            // tile f's bound against the wave's rows.  For load i the lane holds P_i, the
+            // sum of squares of its 8 elements of row RPI*i + lrow; a row's |k|^2 is the
+            // sum of its P over the CH lanes of its group, so the largest |k|^2 among the
+            // group's rows is at most the group's sum of each lane's largest P_i (one
+            // reduction per tile rather than one per row; NaN propagates).  The bound holds
+            // iff qmax^2 * that < c^2 with c = thr - the tile's largest bias > 0.
+            const float qmax2 = qmax * qmax;
             int f_lo = F, f_hi = -1;                // the wave's first / last uncovered tile
             auto check = [&](const u32x4 (&x)[NL], int f) {
-                float rs[NL];
+                float pm = 0.0f;
 #pragma unroll
                 for (int i = 0; i < NL; ++i) {
                     float ss = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) ss = dot2_self<MBF>(x[i][e], ss);
-                    rs[i] = group_sum<CH>(ss);
+                    pm = __builtin_elementwise_maximum(pm, ss);
                 }
+                const float g = group_sum<CH>(pm);
                 const int t = t_far - 1 - f;
-                const float lim = (thr - wg_slope2 * static_cast<float>(t * BN + BN - 1 - wg_pmin)) / qmax;
-                const float lim2 = lim > 0.0f ? lim * lim : -1.0f;
-                bool ok = true;
-#pragma unroll
-                for (int i = 0; i < NL; ++i) ok = ok && (rs[i] < lim2);
+                const float c = thr - wg_slope2 * static_cast<float>(t * BN + BN - 1 - wg_pmin);
+                const bool ok = c > 0.0f && g * qmax2 < c * c;
                 if (__any(!ok)) {
                     f_lo = f_lo < f ? f_lo : f;
                     f_hi = f;

@@ -392,14 +392,25 @@ def test_steep_alibi_long_prefix(dt, D):
     compare(out, lse, ro, rl, rows, inp["query"].dtype, f"steep alibi {dt} D={D}")
 
 
+# far prefix keys given a dominant K row: one per sequence, or two per sequence in far
+# tiles apart (the farthest tile among them), so that the tiles computed run from the
+# first to the last uncovered one across covered tiles
+DOMINANT_KEYS = {
+    "one": ((0, 100), (1, 700)),
+    "two_apart": ((0, 20), (0, 1500), (1, 10), (1, 2000)),
+}
+
+
+@pytest.mark.parametrize("keys", list(DOMINANT_KEYS))
 @pytest.mark.parametrize("D", [64, 128])
-def test_alibi_far_tile_holding_a_dominant_key(D):
-    """ALiBi prefix tiles far enough from a workgroup's rows are predicted negligible and
-    their V rows are not loaded with the tile.  Here one key of such a tile gets an
-    outsized score (its K row is 400 times a direction every query leans towards), so it
-    dominates its rows' softmax despite the bias: the kernel must load that V on demand
-    and match the oracle."""
-    _say(f"[alibi dominant far key] D={D}")
+def test_alibi_far_tile_holding_a_dominant_key(D, keys):
+    """ALiBi prefix tiles far enough from a workgroup's rows are skipped when a bound on
+    their scores (the largest |scaled q| times the largest |k| of the tile, plus the
+    tile's largest bias) shows them negligible.  Here keys of such tiles get outsized
+    scores (their K rows are 400 times a direction every query leans towards), so they
+    dominate their rows' softmax despite the bias: the bound fails for their tiles, which
+    must be computed, and the result must match the oracle."""
+    _say(f"[alibi dominant far key] D={D} keys={keys}")
     inp = wl.make_random_case(970 + D, batch=2, head_num=4, kv_head_num=2, head_size=D,
                               block_size=64, q_lens=[200, 70], kv_lens=[3200, 3070],
                               dtype="f16", mask_type=pa.PA_MASK_ALIBI)
@@ -408,14 +419,14 @@ def test_alibi_far_tile_holding_a_dominant_key(D):
     inp["query"] = (inp["query"].float() + 5.0 * u).to(inp["query"].dtype)
     table = inp["block_tables"]
     bs = inp["key"].shape[1]
-    for b, pos in ((0, 100), (1, 700)):          # far prefix keys of both sequences
+    for b, pos in DOMINANT_KEYS[keys]:
         blk, slot = int(table[b, pos // bs]), pos % bs
         inp["key"][blk, slot] = (400.0 * u).to(inp["key"].dtype)
         inp["value"][blk, slot] = 3.0
     out, lse = gpu_run(inp)
     ro, rl, rows = oracle_run(inp)
-    assert float(np.abs(np.asarray(ro, dtype=np.float64)).max()) > 2.5   # the dominant key's V shows
-    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"alibi dominant far key D={D}")
+    assert float(np.abs(np.asarray(ro, dtype=np.float64)).max()) > 2.5   # a dominant key's V shows
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"alibi dominant far key D={D} {keys}")
 
 
 # ----------------------------------------------------------- unusual qkScale
