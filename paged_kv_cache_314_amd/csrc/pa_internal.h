@@ -22,6 +22,12 @@ constexpr int kCusPerXcd = 32;
 // Prefill: query rows per workgroup and keys per step.
 constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
+// ALiBi over 16-bit K/V: prefix tiles whose bias lies more than this many log2 units
+// below that of the workgroup's nearest key, for every row and key, are far tiles, which
+// a bound on the scores from their K rows' norms usually shows negligible (64: few far
+// tiles then fail the bound and have to be computed).  The planner counts them in an
+// item's cost.
+constexpr float kFarTileBias = 64.0f;
 
 // What the planner sizes work for, and the overrides of its automatic choices (a value
 // < 0 means automatic).  Set by the C ABI from the current device and pa_set_plan_option.

@@ -193,7 +193,9 @@ void counting_sort_desc(std::vector<T>& v, Key key) {
     std::copy(out.get(), out.get() + v.size(), v.begin());
 }
 
-std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const PlanConfig& cfg) {
+template <class Cost>
+std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const PlanConfig& cfg,
+                                   Cost cost, bool lpt_within) {
     const int kXcds = cfg.compute_units % kCusPerXcd == 0
                           ? std::max(1, std::min(8, cfg.compute_units / kCusPerXcd)) : 1;
     const size_t cus_per_xcd = static_cast<size_t>(cfg.compute_units / kXcds);
@@ -223,7 +225,7 @@ std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const 
             size.push_back(0);
         }
         cid[i] = c;
-        work[c] += int64_t(it.ktiles) + 1;
+        work[c] += cost(it);
         ++size[c];
     }
     const size_t nc = work.size();
@@ -262,6 +264,14 @@ std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const 
             counting_sort_desc(l, [](const PrefillItem& x) { return int64_t(x.ktiles); });
             std::reverse(l.begin() + cus_per_xcd, l.end());
         }
+    }
+    // lpt_within: longer lists are re-sorted heaviest first (stable, so items of equal
+    // cost keep the cluster order), for ALiBi, whose items' costs spread widely with the
+    // head's slope; the query tiles of one head still start close together, within the
+    // round of workgroups that holds them (ALiBi prefix workload: 121 -> 119 us)
+    if (lpt_within) {
+        for (auto& l : lists)
+            if (l.size() > 2 * cus_per_xcd) counting_sort_desc(l, cost);
     }
     size_t len = 0;
     for (const auto& l : lists) len = std::max(len, l.size());
@@ -789,18 +799,30 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
                 }
             }
         }
-        // Heaviest first.  Under ALiBi an item's cost also depends on its head's slope:
-        // steep heads skip most of their prefix tiles' P V as negligible.  The slopes
-        // live in device memory, out of the planner's reach, but the usual geometric
-        // slopes 2^(-8(h+1)/headNum) fall with h, so among items of equal length the
-        // higher heads (the costlier ones) go first and the short items fill the end of
-        // the launch (ALiBi prefix workload: 177 -> 160 us).  For other slope orders
-        // this is only a different tie-break.
-        const bool head_desc = maskType == PA_MASK_ALIBI;
-        // (two stable counting passes: by head, then by tile count)
-        if (head_desc) counting_sort_desc(p.prefill_items, [](const PrefillItem& x) { return int64_t(x.h); });
-        counting_sort_desc(p.prefill_items, [](const PrefillItem& x) { return int64_t(x.ktiles); });
-        if (pick(cfg.prefill_xcd_order, true)) p.prefill_items = xcd_order(p.prefill_items, cfg);
+        // Heaviest first (the hardware hands out workgroups in launch order, so this is a
+        // longest-processing-time schedule).  An item costs its key tiles, except that
+        // under ALiBi the prefix tiles far enough from its rows for their bias alone to
+        // make them negligible cost only a bound on their K rows' norms, about a seventh
+        // of a computed tile (measured): 20 units a computed tile, 3 a far one.  Which
+        // tiles are far depends on the slopes, which live in device memory out of the
+        // planner's reach; the usual geometric slopes 2^(-8(h+1)/headNum) are assumed and
+        // the kernel's rule applied (other slopes only change the order).
+        const bool alibi = maskType == PA_MASK_ALIBI;
+        auto cost = [&](const PrefillItem& x) -> int64_t {
+            int64_t far = 0;
+            if (alibi && x.ktiles > 0) {
+                const int64_t shift = int64_t(x.kvlen) - x.qlen, T = x.ktiles - 1;
+                const int64_t P = std::min<int64_t>(shift > 0 ? shift / kPrefillBN : 0, T);
+                // the smallest slope of the item's heads, in log2 units
+                const double s2 = std::exp2(-8.0 * double(x.h + x.heads) / double(headNum)) * 1.4426950408889634;
+                const int64_t pmin = shift + x.qbeg;
+                while (far < P && s2 * double(pmin - (far * kPrefillBN + kPrefillBN - 1)) > double(kFarTileBias)) ++far;
+            }
+            return 20 * (int64_t(x.ktiles) - far) + 3 * far;
+        };
+        counting_sort_desc(p.prefill_items, cost);
+        if (pick(cfg.prefill_xcd_order, true))
+            p.prefill_items = xcd_order(p.prefill_items, cfg, cost, alibi);
         p.off_items = 0;
         p.items_bytes = align256(p.prefill_items.size() * sizeof(PrefillItem));
         p.workspace_bytes = 0;

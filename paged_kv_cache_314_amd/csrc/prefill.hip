@@ -45,11 +45,6 @@ namespace {
 constexpr int BN = kPrefillBN;          // 64 keys per tile
 constexpr float kRescaleSlack = 8.0f;   // log2 units a row max may exceed its reference
 constexpr float kNegligible = 32.0f;    // log2 units below the reference: weight < 2^-32
-// ALiBi over 16-bit K/V: prefix tiles whose bias lies more than this many log2 units
-// below that of the workgroup's nearest key, for every row and key, form the far run, in
-// which a bound on the scores usually shows a tile negligible from its K rows' norms alone
-// (64: few far tiles then fail the bound and have to be computed)
-constexpr float kFarBias = 64.0f;
 // s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their maxima (gfx9
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -86,9 +81,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     constexpr int EPC = 16 / ESZ;         // elements per 16-byte chunk
 
     // K tiles in slots 0 and 1, V tiles in slots 2 and 3 (for 16-bit K/V the four slots
-    // are alike, and the far run of an ALiBi item holds K tiles in all four)
+    // are alike)
     __shared__ uint16_t s_kv[2 * BN * KLD + 2 * BN * VLD];
-    // far run of an ALiBi item: per wave, the smallest largest-score-so-far among its
+    // far tiles of an ALiBi item: per wave, the smallest largest-score-so-far among its
     // query rows, the largest |s_mul q| among them, and the first and last far tile its
     // rows leave uncovered
     __shared__ float s_mmin[4], s_qmax[4];
@@ -222,7 +217,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         }
     }
 
-    // far run of an ALiBi item: the largest |s_mul q| among the wave's query rows (lane l
+    // far tiles of an ALiBi item: the largest |s_mul q| among the wave's query rows (lane l
     // and l ^ 32 hold the two halves of row l % 32), published by the first barrier
     if constexpr (alibi && DIRECT) {
         float ss = 0.0f;
@@ -468,7 +463,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
     // --------------------------------------------------------------- state
     float m_ref = -INFINITY;              // reference row max (log2 units)
-    float m_top = -INFINITY;              // largest score of the row so far (ALiBi far run)
+    float m_top = -INFINITY;              // largest score of the row so far (ALiBi far tiles)
     float l_run = 0.0f;
     f32x16 oacc[DT];
 #pragma unroll
@@ -647,11 +642,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
     auto tile_of = [&](int k) { return prefill_tile_of(vis, k); };
     int k_first = vis.k_first;
-    // ALiBi over 16-bit K/V: the far run.  Prefix tiles whose bias, at the smallest
-    // slope of the workgroup's heads and the distance from its first query row to the
-    // tile's last key, lies more than kFarBias below the nearest key's are expected to be
-    // negligible for every row; they are the tiles 0 .. t_far - 1, which the visit order
-    // takes last among the prefix tiles, in one run of steps.
+    // ALiBi over 16-bit K/V: far tiles.  Prefix tiles whose bias, at the smallest slope
+    // of the workgroup's heads and the distance from its first query row to the tile's
+    // last key, lies more than kFarTileBias below the nearest key's are expected to be
+    // negligible for every row; they are the tiles 0 .. t_far - 1, which are bounded
+    // (and, where the bound holds, skipped) after the other tiles are computed.
     float wg_slope2 = 0.0f;
     if constexpr (alibi && DIRECT) {
         wg_slope2 = INFINITY;
@@ -659,7 +654,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
     const int wg_pmin = shift + it.qbeg;
     auto far = [&](int t) {
-        return t < vis.P && wg_slope2 * static_cast<float>(wg_pmin - (t * BN + BN - 1)) > kFarBias;
+        return t < vis.P && wg_slope2 * static_cast<float>(wg_pmin - (t * BN + BN - 1)) > kFarTileBias;
     };
     auto compute = [&](int t, int buf, bool first) {
         if (t <= t_act) {
@@ -694,7 +689,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         } else {
             // the near tiles first, T down to t_far (the diagonal, then the prefix tiles
             // near enough to matter), double-buffered as in plain_steps, so that every row
-            // holds its reference from its nearest keys; the far run (tiles t_far - 1 ..
+            // holds its reference from its nearest keys; the far tiles (t_far - 1 ..
             // 0) last
             const int n_near = T - t_far + 1;
             vis.P = 0;                  // the plain visit order is then T, T - 1, ...
@@ -707,7 +702,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             }
             __syncthreads();            // every wave is done with the last plain tile
             const float mmin = fminf(fminf(s_mmin[0], s_mmin[1]), fminf(s_mmin[2], s_mmin[3]));
-            // The far run in two passes.  Pass A: every wave streams its own 16 K rows of
+            // The far tiles in two passes.  Pass A: every wave streams its own 16 K rows of
             // each far tile into registers (no LDS, no barrier) and bounds the tile's
             // scores against those rows (Cauchy-Schwarz: |s_mul q . k| <= max |s_mul q| *
             // |k|, plus the tile's largest bias).  A tile whose bound lies below every

@@ -155,16 +155,38 @@ def test_plan_for_named_workloads(name):
         _check_prefill_plan(info, ql, kv, w.head_num, w.mask_type, w.head_num // w.kv_head_num)
 
 
-def test_alibi_prefill_items_longest_then_highest_head(monkeypatch):
-    """Before the XCD placement, ALiBi prefill items run longest first and, among equal
-    lengths, highest head first (the usual slopes fall with the head index, and steep
-    heads skip most of their negligible tiles); the XCD placement keeps every item."""
+def _alibi_item_cost(it, head_num):
+    """Estimated cost of an ALiBi prefill item: 20 per computed key tile, 3 per far
+    prefix tile (bias alone over 64 log2 units below the nearest key's at the item's
+    smallest slope, geometric slopes 2^(-8(h+1)/H) assumed)."""
+    b, h, qbeg, qlen, kvlen, qrow0, ktiles, heads = it[:8]
+    shift, T = kvlen - qlen, ktiles - 1
+    P = min(shift // 64 if shift > 0 else 0, T)
+    s2 = 2.0 ** (-8.0 * (h + heads) / head_num) * 1.4426950408889634
+    far = 0
+    while far < P and s2 * (shift + qbeg - (64 * far + 63)) > 64.0:
+        far += 1
+    return 20 * (ktiles - far) + 3 * far
+
+
+def test_alibi_prefill_items_heaviest_first_by_estimated_cost():
+    """ALiBi prefill items run heaviest first by an estimated cost that counts far prefix
+    tiles (only bounded, not computed) at 3/20 of a computed tile; the XCD placement keeps
+    every item and leaves each XCD's list (longer than two rounds here) heaviest first."""
+    w = wl.WORKLOADS["prefill_alibi_f16"]
     with pa.plan_options({pa.PA_OPT_PREFILL_XCD_ORDER: 0}):
         items = _plan_named("prefill_alibi_f16")["prefill_items"]
-    keys = [(-it[6], -it[1]) for it in items]
-    assert keys == sorted(keys)
-    placed = [it for it in _plan_named("prefill_alibi_f16")["prefill_items"] if it[7] != 0]
-    assert sorted(map(tuple, placed)) == sorted(map(tuple, items))
+    costs = [_alibi_item_cost(it, w.head_num) for it in items]
+    assert costs == sorted(costs, reverse=True)
+    assert costs[0] > costs[-1]                 # the steep heads' items do come out lighter
+    placed = _plan_named("prefill_alibi_f16")["prefill_items"]
+    real = [it for it in placed if it[7] != 0]
+    assert sorted(map(tuple, real)) == sorted(map(tuple, items))
+    for x in range(8):
+        lst = [it for it in placed[x::8] if it[7] != 0]
+        assert len(lst) > 64
+        c = [_alibi_item_cost(it, w.head_num) for it in lst]
+        assert c == sorted(c, reverse=True)
 
 
 def test_single_round_prefill_pairs_heavy_with_light():
