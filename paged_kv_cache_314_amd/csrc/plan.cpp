@@ -180,7 +180,8 @@ template <typename T, typename Key>
 void counting_sort_desc(std::vector<T>& v, Key key) {
     int64_t max_key = 0;
     for (const T& x : v) max_key = std::max<int64_t>(max_key, key(x));
-    if (max_key > (int64_t(1) << 16)) {
+    // a key range far above the element count: the prefix pass would dominate
+    if (max_key > (int64_t(1) << 16) || max_key > 8 * static_cast<int64_t>(v.size()) + 64) {
         std::stable_sort(v.begin(), v.end(), [&](const T& a, const T& b) { return key(a) > key(b); });
         return;
     }
@@ -193,9 +194,9 @@ void counting_sort_desc(std::vector<T>& v, Key key) {
     std::copy(out.get(), out.get() + v.size(), v.begin());
 }
 
-template <class Cost>
-std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const PlanConfig& cfg,
-                                   Cost cost, bool lpt_within) {
+// cost[i]: the estimated cost of items[i]
+std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const std::vector<int64_t>& cost,
+                                   const PlanConfig& cfg, bool lpt_within) {
     const int kXcds = cfg.compute_units % kCusPerXcd == 0
                           ? std::max(1, std::min(8, cfg.compute_units / kCusPerXcd)) : 1;
     const size_t cus_per_xcd = static_cast<size_t>(cfg.compute_units / kXcds);
@@ -225,7 +226,7 @@ std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const 
             size.push_back(0);
         }
         cid[i] = c;
-        work[c] += cost(it);
+        work[c] += cost[i];
         ++size[c];
     }
     const size_t nc = work.size();
@@ -238,46 +239,47 @@ std::vector<PrefillItem> xcd_order(const std::vector<PrefillItem>& items, const 
     // clusters heaviest first (creation order breaks ties), each to the least loaded XCD
     std::vector<int32_t> order(nc);
     for (size_t c = 0; c < nc; ++c) order[c] = static_cast<int32_t>(c);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t x, int32_t y) { return work[x] > work[y]; });
-    std::vector<std::vector<PrefillItem>> lists(kXcds);
+    counting_sort_desc(order, [&](int32_t c) { return work[c]; });
+    std::vector<std::vector<uint32_t>> lists(kXcds);     // positions in items
     for (auto& l : lists) l.reserve(cap + cap / 2);
     std::vector<int64_t> load(kXcds, 0);
+    std::vector<int32_t> xcd_of(nc);
     for (const int32_t c : order) {
         int x = 0;
         for (int i = 1; i < kXcds; ++i)
             if (load[i] < load[x]) x = i;
         load[x] += work[c];
-        for (uint32_t k = first[c]; k < first[c + 1]; ++k) lists[x].push_back(items[members[k]]);
+        xcd_of[c] = x;
+        if (!lpt_within)
+            for (uint32_t k = first[c]; k < first[c + 1]; ++k) lists[x].push_back(members[k]);
     }
+    // lpt_within (ALiBi, whose items' costs spread widely with the head's slope): each
+    // XCD's list in the items' own order, heaviest first, rather than cluster by cluster;
+    // the query tiles of one head still start close together, within the round of
+    // workgroups that holds them (ALiBi prefix workload: 121 -> 119 us)
+    if (lpt_within)
+        for (size_t i = 0; i < n; ++i) lists[xcd_of[cid[i]]].push_back(static_cast<uint32_t>(i));
     // An XCD's list that fits one round (at most two workgroups per CU) is placed so that
     // each CU's pair of workgroups is one heavy and one light item: the hardware gives
     // every CU of the XCD its first workgroup before any CU gets a second, so positions
     // k and k + (CUs per XCD) share a CU.  Heaviest first, then the rest lightest first,
     // lets the long items run most of their tiles without a partner wave on their SIMDs
     // (measured: the causal 512-token, 4-sequence GQA workload runs 16% faster than with
-    // equal-weight pairs).  Longer lists keep the cluster order, which is what lets the
-    // query tiles of one (sequence, head block) share its K/V tiles through the L2.
+    // equal-weight pairs).  Longer lists keep the cluster order (or, under lpt_within, the
+    // cost order), which lets the query tiles of one (sequence, head block) share its K/V
+    // tiles through the L2.
     if (pick(cfg.prefill_pair, true)) {
         for (auto& l : lists) {
             if (l.size() <= cus_per_xcd || l.size() > 2 * cus_per_xcd) continue;
-            counting_sort_desc(l, [](const PrefillItem& x) { return int64_t(x.ktiles); });
+            counting_sort_desc(l, [&](uint32_t i) { return int64_t(items[i].ktiles); });
             std::reverse(l.begin() + cus_per_xcd, l.end());
         }
-    }
-    // lpt_within: longer lists are re-sorted heaviest first (stable, so items of equal
-    // cost keep the cluster order), for ALiBi, whose items' costs spread widely with the
-    // head's slope; the query tiles of one head still start close together, within the
-    // round of workgroups that holds them (ALiBi prefix workload: 121 -> 119 us)
-    if (lpt_within) {
-        for (auto& l : lists)
-            if (l.size() > 2 * cus_per_xcd) counting_sort_desc(l, cost);
     }
     size_t len = 0;
     for (const auto& l : lists) len = std::max(len, l.size());
     std::vector<PrefillItem> out(len * kXcds);   // value-initialised: heads == 0 = no-op
     for (int x = 0; x < kXcds; ++x)
-        for (size_t k = 0; k < lists[x].size(); ++k) out[k * kXcds + x] = lists[x][k];
+        for (size_t k = 0; k < lists[x].size(); ++k) out[k * kXcds + x] = items[lists[x][k]];
     return out;
 }
 
@@ -808,21 +810,44 @@ void plan_impl(const pa_tensor* query, const pa_tensor* key, const pa_tensor* va
         // planner's reach; the usual geometric slopes 2^(-8(h+1)/headNum) are assumed and
         // the kernel's rule applied (other slopes only change the order).
         const bool alibi = maskType == PA_MASK_ALIBI;
-        auto cost = [&](const PrefillItem& x) -> int64_t {
+        // reach[h] = kFarTileBias / (head h's assumed slope in log2 units): a key is far
+        // for head h beyond that distance (the smallest slope of an item's heads is its
+        // last head's)
+        std::vector<double> reach(alibi ? headNum : 0);
+        for (int32_t h = 0; h < static_cast<int32_t>(reach.size()); ++h)
+            reach[h] = double(kFarTileBias) /
+                       (std::exp2(-8.0 * double(h + 1) / double(headNum)) * 1.4426950408889634);
+        auto item_cost = [&](const PrefillItem& x) -> int64_t {
             int64_t far = 0;
             if (alibi && x.ktiles > 0) {
                 const int64_t shift = int64_t(x.kvlen) - x.qlen, T = x.ktiles - 1;
                 const int64_t P = std::min<int64_t>(shift > 0 ? shift / kPrefillBN : 0, T);
-                // the smallest slope of the item's heads, in log2 units
-                const double s2 = std::exp2(-8.0 * double(x.h + x.heads) / double(headNum)) * 1.4426950408889634;
-                const int64_t pmin = shift + x.qbeg;
-                while (far < P && s2 * double(pmin - (far * kPrefillBN + kPrefillBN - 1)) > double(kFarTileBias)) ++far;
+                // tile t (< P) is far iff (pmin - (64 t + 63)) > reach, i.e. 64 t < y: the
+                // ceil(y / 64) tiles t >= 0 below that bound
+                const double y = double(shift + x.qbeg - (kPrefillBN - 1)) - reach[x.h + x.heads - 1];
+                if (y > 0.0) far = std::min<int64_t>(P, static_cast<int64_t>(std::ceil(y * (1.0 / kPrefillBN))));
             }
             return 20 * (int64_t(x.ktiles) - far) + 3 * far;
         };
-        counting_sort_desc(p.prefill_items, cost);
+        const size_t n_items = p.prefill_items.size();
+        std::vector<int64_t> cost(n_items);
+        for (size_t i = 0; i < n_items; ++i) cost[i] = item_cost(p.prefill_items[i]);
+        {
+            // heaviest first (stable): positions sorted by cost, then gathered
+            std::vector<uint32_t> pos(n_items);
+            for (size_t i = 0; i < n_items; ++i) pos[i] = static_cast<uint32_t>(i);
+            counting_sort_desc(pos, [&](uint32_t i) { return cost[i]; });
+            std::vector<PrefillItem> sorted(n_items);
+            std::vector<int64_t> sorted_cost(n_items);
+            for (size_t k = 0; k < n_items; ++k) {
+                sorted[k] = p.prefill_items[pos[k]];
+                sorted_cost[k] = cost[pos[k]];
+            }
+            p.prefill_items.swap(sorted);
+            cost.swap(sorted_cost);
+        }
         if (pick(cfg.prefill_xcd_order, true))
-            p.prefill_items = xcd_order(p.prefill_items, cfg, cost, alibi);
+            p.prefill_items = xcd_order(p.prefill_items, cost, cfg, alibi);
         p.off_items = 0;
         p.items_bytes = align256(p.prefill_items.size() * sizeof(PrefillItem));
         p.workspace_bytes = 0;

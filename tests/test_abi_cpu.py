@@ -163,9 +163,11 @@ def _alibi_item_cost(it, head_num):
     shift, T = kvlen - qlen, ktiles - 1
     P = min(shift // 64 if shift > 0 else 0, T)
     s2 = 2.0 ** (-8.0 * (h + heads) / head_num) * 1.4426950408889634
-    far = 0
-    while far < P and s2 * (shift + qbeg - (64 * far + 63)) > 64.0:
-        far += 1
+    # tile t < P is far iff s2 * (shift + qbeg - (64 t + 63)) > 64, i.e. 64 t < y
+    y = (shift + qbeg - 63) - 64.0 / s2
+    far = min(P, math.ceil(y / 64)) if y > 0 else 0
+    # the same count by enumeration
+    assert far == sum(1 for t in range(P) if s2 * (shift + qbeg - (64 * t + 63)) > 64.0)
     return 20 * (ktiles - far) + 3 * far
 
 
