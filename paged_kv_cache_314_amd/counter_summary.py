@@ -18,14 +18,16 @@ sq: the MFMA math operations the kernel executed (SQ_INSTS_VALU_MFMA_MOPS_*, eac
 (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD times the SIMD count).
 
 Both merge into profiles/KERNEL_WORKLOAD_counters.json, keyed by the hash of the
-kernel's sources and the planner's (bench.py reads it for roofline.traffic and
-roofline.executed and ignores it once either changes), and print a short text summary.
+kernel's sources and the planner's with comments and blank space left out (bench.py
+reads it for roofline.traffic and roofline.executed and ignores it once the code of
+either changes), and print a short text summary.
 """
 
 import csv
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -44,12 +46,23 @@ SIMDS = 256 * 4              # 256 CUs of 4 SIMDs
 MOPS_UNIT = 512              # flops per SQ_INSTS_VALU_MFMA_MOPS_* count
 
 
+def code_text(text):
+    """C/C++ source without its comments and with runs of blank space collapsed: what a
+    change must touch to change the compiled code (these sources hold no string literal
+    with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kind):
-    """sha256 (first 16 hex digits) of the sources a kernel and its work lists come from."""
+    """sha256 (first 16 hex digits) of the code of the sources a kernel and its work lists
+    come from (comments and blank space left out)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode("utf-8"))
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -24,6 +24,11 @@
 //                read ds_read_b64_tr_b16
 // Q stays in registers as the B operand; LDS is double-buffered so one barrier per key
 // tile suffices, and the next tile's global loads are in flight during the MFMA work.
+// ALiBi over 16-bit K/V: prefix tiles whose bias alone lies far below the nearest keys'
+// are not computed when a Cauchy-Schwarz bound on their scores (the workgroup's largest
+// |scaled q| times the tile's largest |k|, plus the tile's largest bias), taken from
+// their K rows streamed through registers after the other tiles, shows every weight
+// negligible next to its row's largest; a tile the bound does not cover is computed.
 // int8 K/V are converted exactly to f16 on the way into LDS; the per-channel K scale is
 // folded into Q (kept to ~22 bits as an f16 hi + lo pair), the V scale into the output.
 // FLOAT8_E4M3FN K/V take the int8 path with the codes expanded exactly to f16 instead.

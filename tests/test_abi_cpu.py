@@ -849,3 +849,34 @@ def test_static_execute_refuses_ops_beyond_its_scratch():
     st, aop = AppendCase(q_lens=[2], kv_lens=[9]).call()
     assert lib.pa_paged_attention_static(aop, None) == pa.PA_ERR_PARAM_INVALID
     pa.pa_op_destroy(aop)
+
+
+# ------------------------------------------------------------ counter records
+
+def test_counter_records_key_on_code_not_comments(tmp_path, monkeypatch):
+    """profiles/*_counters.json are keyed by a hash of the kernels' and the planner's code:
+    a comment or blank-space edit keeps the key, a code edit changes it, and every
+    committed record carries the key of the sources as they stand (bench.py would
+    otherwise report its traffic and executed work as null)."""
+    import glob
+    import json
+    import shutil
+
+    from paged_kv_cache_314_amd import counter_summary as cs
+
+    assert cs.code_text("int a; // note\n/* block\n comment */\n\n  int  b;") == "int a; int b;"
+    for f in glob.glob(os.path.join(cs.ROOT, "profiles", "*_counters.json")):
+        with open(f) as fh:
+            rec = json.load(fh)
+        assert rec["source_sha256_16"] == cs.kernel_source_hash(rec["kernel"]), f
+    # edits on a copy of the sources
+    src = tmp_path / "csrc"
+    shutil.copytree(cs.CSRC, src)
+    monkeypatch.setattr(cs, "CSRC", str(src))
+    base = cs.kernel_source_hash("prefill_kernel")
+    p = src / "prefill.hip"
+    text = p.read_text()
+    p.write_text("// a new comment line\n" + text.replace("\n", "\n\n", 3))
+    assert cs.kernel_source_hash("prefill_kernel") == base
+    p.write_text(text.replace("constexpr int BN = kPrefillBN;", "constexpr int BN = kPrefillBN + 0;"))
+    assert cs.kernel_source_hash("prefill_kernel") != base
