@@ -376,20 +376,23 @@ def test_prefill_random(case):
 
 # ----------------------------------------------- steep ALiBi: negligible tiles skipped
 
-@pytest.mark.parametrize("dt,D", [("f16", 128), ("bf16", 64)])
-def test_steep_alibi_long_prefix(dt, D):
+@pytest.mark.parametrize("dt,D,bs", [("f16", 128, 64), ("bf16", 64, 64),
+                                     ("f16", 128, 80), ("bf16", 64, 48)])
+def test_steep_alibi_long_prefix(dt, D, bs):
     """Slopes of 1 over a 3000-token prefix: nearly every prefix tile lies more than 32
-    log2 units below its rows' reference, so the kernel skips its P and P V; out and
-    lse must still match the full computation of the oracle."""
-    _say(f"[steep alibi] {dt} D={D}")
-    inp = wl.make_random_case(950 + D, batch=2, head_num=4, kv_head_num=2, head_size=D,
-                              block_size=64, q_lens=[200, 70], kv_lens=[3200, 3070],
+    log2 units below its rows' reference (most of them far tiles, skipped on a bound from
+    their K rows' norms), so the kernel skips their P and P V; out and lse must still
+    match the full computation of the oracle.  Block sizes of 80 and 48 make the far
+    tiles' loads find their blocks by division."""
+    _say(f"[steep alibi] {dt} D={D} blockSize={bs}")
+    inp = wl.make_random_case(950 + D + bs, batch=2, head_num=4, kv_head_num=2, head_size=D,
+                              block_size=bs, q_lens=[200, 70], kv_lens=[3200, 3070],
                               dtype=dt, mask_type=pa.PA_MASK_ALIBI)
     inp["slopes"] = torch.full((4,), 1.0, dtype=torch.float32)
     inp["slopes"][3] = 0.004          # one shallow head: its tiles are all computed
     out, lse = gpu_run(inp)
     ro, rl, rows = oracle_run(inp)
-    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"steep alibi {dt} D={D}")
+    compare(out, lse, ro, rl, rows, inp["query"].dtype, f"steep alibi {dt} D={D} bs={bs}")
 
 
 # far prefix keys given a dominant K row: one per sequence, or two per sequence in far
