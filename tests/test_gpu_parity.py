@@ -94,6 +94,23 @@ def test_prefill_is_deterministic():
     assert torch.equal(a_lse, b_lse)
 
 
+def test_alibi_far_tiles_are_deterministic():
+    """The far-tile bound takes data-dependent branches (which tiles are computed); two
+    runs on the same inputs, one of them with a dominant key in a far tile, still give
+    bitwise equal results."""
+    inp = wl.make_random_case(977, batch=2, head_num=4, kv_head_num=2, head_size=128,
+                              block_size=64, q_lens=[200, 70], kv_lens=[3200, 3070],
+                              dtype="f16", mask_type=pa.PA_MASK_ALIBI)
+    inp["slopes"] = torch.full((4,), 0.5, dtype=torch.float32)
+    u = torch.full((128,), 1.0 / 128 ** 0.5)
+    blk = int(inp["block_tables"][1, 300 // 64])
+    inp["key"][blk, 300 % 64] = (400.0 * u).to(inp["key"].dtype)
+    a_out, a_lse = gpu_run(inp, want_lse=True)
+    b_out, b_lse = gpu_run(inp, want_lse=True)
+    assert torch.equal(a_out.view(torch.int16), b_out.view(torch.int16))
+    assert torch.equal(a_lse, b_lse)
+
+
 # ----------------------------------------------------------- random decode
 
 DECODE_CASES = [
